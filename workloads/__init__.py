@@ -1,0 +1,10 @@
+"""Seeded synthetic inputs for the speculative-decoding verify step.
+
+This package is shared by the CPU oracle's tests and by the GPU path's tests
+and benchmark. It only draws random numbers and lays them out in memory; it
+holds none of the verify step's arithmetic (no softmax, no acceptance test, no
+attention, no counter-based uniforms).
+"""
+
+from .gen import PRESETS, Preset, make_attention_inputs, make_reject_inputs, make_inputs  # noqa: F401
+from .gen import bf16_bits, verify_seed, draft_from_logits  # noqa: F401
