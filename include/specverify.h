@@ -1,0 +1,164 @@
+/*
+ * specverify.h - C-ABI of libspecverify.so: the target-side verify step of
+ * lossless speculative decoding on one AMD Instinct MI355X (gfx950).
+ *
+ * One verify step of a batch of B sequences is three calls on one stream:
+ *   spec_verify_attn     paged-KV attention of the k+1 verify rows
+ *   spec_reject_sample   vocab-wide softmax + acceptance chain + residual / bonus sample
+ *   spec_commit_lengths  the accepted length rolls each cache length forward
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are device pointers owned by the caller, contiguous and
+ *    row-major as documented per argument. The library allocates nothing,
+ *    keeps no global state and never synchronises: work is enqueued on
+ *    `stream` (a hipStream_t; NULL means the default stream) and the caller
+ *    synchronises. Calls on different streams may run concurrently if they
+ *    use different workspaces and outputs.
+ *  - Host-side arguments are validated before anything is enqueued; on any
+ *    error nothing is enqueued and an error code is returned. Device-resident
+ *    data (token ids, block ids, lengths) is a documented precondition and is
+ *    not checked.
+ *  - Workspaces are caller-allocated device memory of at least the size the
+ *    matching *_workspace_size call reports, ZERO-FILLED ONCE after allocation.
+ *    Every call leaves the synchronisation counters inside a workspace at zero
+ *    again, so a workspace is reused across calls without clearing; two calls
+ *    in flight at the same time must not share one.
+ *  - No C++ exception crosses this interface.
+ *
+ * Sources for what is computed (page titles; the pages print no API):
+ *  [ACC]  "Accelerating RL Post-Training Rollouts via System-Integrated
+ *         Speculative Decoding" (gist.science summary), section 2 "Method",
+ *         core mechanism: the draft proposes k tokens, the target verifies all
+ *         of them in one forward pass, rejection sampling against the target's
+ *         distribution keeps the rollout distribution identical to the policy.
+ *  [ODC]  "Online Draft Co-Training for Speculative Decoding in Large-Scale,
+ *         Long-Context RL Post-Training" (ta-paperlens commentary), metaphor
+ *         section: the verifier rewrites from the first draft token that misses.
+ *  [RESP] "ReSpec: Towards Optimizing Speculative Decoding in Reinforcement
+ *         Learning Systems" (talk notes), "Adaptive Server": speculation
+ *         extends the KV cache; accepted length is the progress measure (GAP 2).
+ *  [EFR]  "EfficientRollout: System-Aware Self-Speculative Decoding for RL
+ *         Rollouts", abstract: long, high-temperature generations; the active
+ *         batch shrinks during a rollout.
+ *  The acceptance rule itself is standard speculative sampling (Leviathan et
+ *  al. 2023; Chen et al. 2023); Philox4x32-10 is from Salmon et al., SC'11.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t spec_status;
+
+#define SPEC_OK                       0
+#define SPEC_ERR_NULL_POINTER         1  /* a required pointer argument is NULL            */
+#define SPEC_ERR_BAD_SHAPE            2  /* a size argument is out of the supported range  */
+#define SPEC_ERR_BAD_VALUE            3  /* a scalar (temperature, scale) is invalid       */
+#define SPEC_ERR_WORKSPACE_TOO_SMALL  4  /* workspace_bytes below the reported size        */
+#define SPEC_ERR_NO_DEVICE            5  /* no HIP device, or the current device is not gfx950 */
+#define SPEC_ERR_HIP                  6  /* a HIP runtime call or kernel launch failed     */
+#define SPEC_ERR_UNIMPLEMENTED        7  /* shape combination not built into this library  */
+
+#define SPEC_ABI_VERSION 1
+
+/* Static string for a status code (never NULL). */
+const char* spec_status_string(spec_status s);
+
+/* SPEC_ABI_VERSION of the loaded library. */
+int32_t spec_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Verify attention  [ACC]: all k drafted tokens are checked in one target pass.
+ *
+ * For every sequence b the cache already holds its L_b committed tokens plus
+ * the k+1 verify tokens [x_last, d_0 .. d_{k-1}] at positions L_b .. L_b+k
+ * (the caller appends their K/V rows before this call). Query row i
+ * (0 <= i <= k) attends to keys 0 .. L_b+i (causal inside the draft);
+ * query head h reads KV head h / (Hq/Hkv). Scores are sm_scale * q.k, softmax
+ * in fp32, output in bf16 (round to nearest even).
+ *
+ *  q            bf16  [B][k+1][Hq][D]
+ *  k_cache      bf16  [num_blocks][Hkv][block_size][D]
+ *  v_cache      bf16  [num_blocks][Hkv][D][block_size]   (key index fastest)
+ *  block_table  int32 [B][max_blocks]   logical page -> physical page
+ *  seq_lens     int32 [B]   committed length L_b (keys read: L_b + k + 1)
+ *  out          bf16  [B][k+1][Hq][D]
+ *
+ * Shapes: B >= 1; 1 <= k <= 15; Hkv >= 1; Hq % Hkv == 0; D in {64, 128};
+ * block_size in {16, 32, 64}; max_blocks >= 1; num_blocks >= 1;
+ * max_seq_len >= k + 1; sm_scale finite and > 0.
+ * Device preconditions: L_b + k + 1 <= min(max_seq_len, max_blocks*block_size);
+ * the first ceil((L_b+k+1)/block_size) block-table entries of b are < num_blocks.
+ * Entries past that are never read. Cache slots past key L_b+k are never read
+ * into the result (their contents may be anything, NaN included).
+ * Workspace: spec_verify_attn_workspace_size(B, k, Hq, Hkv, D, max_seq_len).
+ * ---------------------------------------------------------------------- */
+spec_status spec_verify_attn_workspace_size(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t max_seq_len, size_t* bytes_out);
+
+spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, void* out,
+                             int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t block_size, int32_t max_blocks, int32_t num_blocks,
+                             int32_t max_seq_len, float sm_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rejection sampling  [ACC], [ODC], [EFR].
+ *
+ * p_j = softmax(target_logits[b][j] / T), q_j = softmax(draft_logits[b][j] / T).
+ * For j = 0 .. k-1, at position P = L_b + 1 + j with (u_acc, u_smp) =
+ * Philox4x32-10(counter = (P, seq_id lo, seq_id hi, 0), key = (seed lo, seed hi)),
+ * u = (word >> 8) * 2^-24 from words 0 and 1: accept d_j iff u_acc < p_j(d_j)/q_j(d_j)
+ * (q_j(d_j) = 0 counts as +inf when p_j(d_j) > 0). The first rejection at j emits
+ * a sample of max(0, p_j - q_j) (normalised) and stops; if all k are accepted a
+ * bonus token is drawn from p_k with u_smp at P = L_b + 1 + k. Sampling is
+ * inverse-CDF in ascending token id: the smallest y with C(y) > u_smp * C(V-1).
+ *
+ *  target_logits fp32 [B][k+1][V]      draft_logits fp32 [B][k][V]
+ *  draft_tokens  int32 [B][k]  (each < V)
+ *  seq_ids       int64 [B]  stable per-sequence ids (batch-slot independent)
+ *  seq_lens      int32 [B]  committed lengths L_b (read only)
+ *  out_tokens    int32 [B][k+1]  accepted drafts, then the sampled token at index
+ *                num_accepted[b], then -1
+ *  num_accepted  int32 [B]  a_b in [0, k]
+ *  out_probs     fp32 [B][k+1] or NULL: p_i(out_tokens[b][i]) for i <= a_b, 0 after
+ *  accept_probs  fp32 [B][k]   or NULL: min(1, p_j/q_j) at d_j for tested j, -1 for untested
+ *
+ * Shapes: B >= 1; 1 <= k <= 15; V >= 2; temperature finite and > 0.
+ * Rows after a sequence's first rejection are not read.
+ * Workspace: spec_reject_sample_workspace_size(B, k, V).
+ * ---------------------------------------------------------------------- */
+spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out);
+
+spec_status spec_reject_sample(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, const int64_t* seq_ids,
+                               const int32_t* seq_lens, int32_t B, int32_t k, int32_t V,
+                               float temperature, uint64_t seed,
+                               int32_t* out_tokens, int32_t* num_accepted,
+                               float* out_probs, float* accept_probs,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Commit  [ACC] (accepted length per step), [RESP] (KV cache extended in place).
+ *
+ * seq_lens[b] <- seq_lens[b] + num_accepted[b] + 1, unless that exceeds
+ * capacity_tokens: then seq_lens[b] is left unchanged and overflow_flags[b] = 1
+ * (overflow_flags[b] = 0 otherwise; overflow_flags may be NULL).
+ *
+ *  seq_lens int32 [B] in/out;  num_accepted int32 [B] in [0, k];  overflow_flags int32 [B] or NULL
+ * Shapes: B >= 1; 1 <= k <= 15; capacity_tokens >= 1.
+ * ---------------------------------------------------------------------- */
+spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
+                                int32_t capacity_tokens, int32_t* overflow_flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

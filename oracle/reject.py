@@ -56,9 +56,13 @@ def softmax_t(logits: np.ndarray, temperature: float) -> np.ndarray:
     return e / math.fsum(e)
 
 
-def inverse_cdf(weights: np.ndarray, u: float):
-    """(token, margin): smallest y with C(y) > u * C(V-1); margin relative to the total weight."""
-    C = np.cumsum(weights)
+def inverse_cdf(weights: np.ndarray, u: float, C: np.ndarray | None = None):
+    """(token, margin): smallest y with C(y) > u * C(V-1); margin relative to the total weight.
+
+    ``C`` may pass the running sum of ``weights`` when it is already known.
+    """
+    if C is None:
+        C = np.cumsum(weights)
     R = float(C[-1])
     t = u * R
     y = int(np.searchsorted(C, t, side="right"))
@@ -96,6 +100,7 @@ class SequenceRows:
         self._p = {}
         self._q = {}
         self._res = {}
+        self._cdf = {}
 
     def p(self, j: int) -> np.ndarray:
         if j not in self._p:
@@ -112,6 +117,13 @@ class SequenceRows:
             r = np.maximum(0.0, self.p(j) - self.q(j))
             self._res[j] = r if r.sum() > 0 else self.p(j)
         return self._res[j]
+
+    def cdf(self, kind: str, j: int) -> np.ndarray:
+        """Running sum of the residual ("res") or of p ("p") of row j, computed once."""
+        key = (kind, j)
+        if key not in self._cdf:
+            self._cdf[key] = np.cumsum(self.residual(j) if kind == "res" else self.p(j))
+        return self._cdf[key]
 
 
 def decide(rows: SequenceRows, draft_tokens, k: int, uniforms) -> SequenceResult:
@@ -134,12 +146,12 @@ def decide(rows: SequenceRows, draft_tokens, k: int, uniforms) -> SequenceResult
             tokens.append(x)
             out_probs.append(p_x)
             continue
-        y, margin = inverse_cdf(rows.residual(j), u_smp)
+        y, margin = inverse_cdf(rows.residual(j), u_smp, rows.cdf("res", j))
         decisions.append(Decision("sample", j, y, margin))
         tokens.append(y)
         out_probs.append(float(rows.p(j)[y]))
         return SequenceResult(tokens, j, out_probs, accept_probs, decisions)
-    y, margin = inverse_cdf(rows.p(k), uniforms[k][1])
+    y, margin = inverse_cdf(rows.p(k), uniforms[k][1], rows.cdf("p", k))
     decisions.append(Decision("sample", k, y, margin))
     tokens.append(y)
     out_probs.append(float(rows.p(k)[y]))

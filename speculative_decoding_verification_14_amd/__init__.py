@@ -1,0 +1,194 @@
+"""Python binding of libspecverify.so, the HIP (gfx950) verify step of lossless
+speculative decoding: paged-KV verify attention, vocab-wide rejection sampling
+and the cache-length commit.
+
+Argument marshalling only: every step runs in the library's kernels. torch
+tensors provide device memory and the stream; nothing here computes on them.
+The library must be built (``python -m speculative_decoding_verification_14_amd.build``
+or ``__graft_entry__.build()``); importing works without it, but every call
+raises ``SpecError`` if it is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", "reject_sample",
+           "reject_sample_workspace_size", "commit_lengths", "verify_step", "LIB_PATH", "SYMBOLS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+
+SPEC_OK = 0
+_c_int32, _c_size, _vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/specverify.h
+SYMBOLS = {
+    "spec_status_string": (ctypes.c_char_p, [_c_int32]),
+    "spec_abi_version": (_c_int32, []),
+    "spec_verify_attn_workspace_size": (_c_int32, [_c_int32] * 6 + [ctypes.POINTER(_c_size)]),
+    "spec_verify_attn": (_c_int32, [_vp] * 6 + [_c_int32] * 9 + [ctypes.c_float, _vp, _c_size, _vp]),
+    "spec_reject_sample_workspace_size": (_c_int32, [_c_int32] * 3 + [ctypes.POINTER(_c_size)]),
+    "spec_reject_sample": (_c_int32, [_vp] * 5 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
+                           + [_vp] * 5 + [_c_size, _vp]),
+    "spec_commit_lengths": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _c_int32, _vp, _vp]),
+}
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = library().spec_status_string(code).decode() if _lib is not None else f"status {code}"
+        super().__init__(f"{where}: {msg} (status {code})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library():
+    """The loaded libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                                       "(python -m speculative_decoding_verification_14_amd.build)")
+                lib = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SYMBOLS.items():
+                    fn = getattr(lib, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = lib
+    return _lib
+
+
+def _check(code: int, where: str):
+    if code != SPEC_OK:
+        raise SpecError(code, where)
+
+
+def _need(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t, dtype, name):
+    return None if t is None else _need(t, dtype, name)
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# Per-device workspaces, zero-filled once; the library leaves its counters at zero.
+_workspaces: dict = {}
+
+
+def _workspace(kind: str, device, nbytes: int):
+    import torch
+    key = (kind, str(device))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def verify_attn_workspace_size(B, k, Hq, Hkv, D, max_seq_len) -> int:
+    n = _c_size(0)
+    _check(library().spec_verify_attn_workspace_size(B, k, Hq, Hkv, D, max_seq_len, ctypes.byref(n)),
+           "spec_verify_attn_workspace_size")
+    return n.value
+
+
+def reject_sample_workspace_size(B, k, V) -> int:
+    n = _c_size(0)
+    _check(library().spec_reject_sample_workspace_size(B, k, V, ctypes.byref(n)), "spec_reject_sample_workspace_size")
+    return n.value
+
+
+def verify_attn(q, k_cache, v_cache, block_table, seq_lens, out, max_seq_len: int, sm_scale: float | None = None,
+                workspace=None, stream=None):
+    """spec_verify_attn. q/out bf16 [B][k+1][Hq][D]; k_cache bf16 [NB][Hkv][bs][D];
+    v_cache bf16 [NB][Hkv][D][bs]; block_table int32 [B][max_blocks]; seq_lens int32 [B]."""
+    import torch
+    B, k1, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    lib = library()
+    need = verify_attn_workspace_size(B, k1 - 1, Hq, Hkv, D, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = _workspace("attn", q.device, need)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.spec_verify_attn(_need(q, torch.bfloat16, "q"), _need(k_cache, torch.bfloat16, "k_cache"),
+                                _need(v_cache, torch.bfloat16, "v_cache"), _need(block_table, torch.int32, "block_table"),
+                                _need(seq_lens, torch.int32, "seq_lens"), _need(out, torch.bfloat16, "out"),
+                                B, k1 - 1, Hq, Hkv, D, bs, max_blocks, NB, int(max_seq_len), scale,
+                                wptr, wbytes, _stream_handle(stream)), "spec_verify_attn")
+    return out
+
+
+def reject_sample(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, temperature: float, seed: int,
+                  out_tokens, num_accepted, out_probs=None, accept_probs=None, workspace=None, stream=None):
+    """spec_reject_sample. target fp32 [B][k+1][V]; draft fp32 [B][k][V]; draft_tokens int32 [B][k];
+    seq_ids int64 [B]; seq_lens int32 [B]; outputs as in include/specverify.h."""
+    import torch
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    lib = library()
+    need = reject_sample_workspace_size(B, k, V)
+    if workspace is None:
+        workspace = _workspace("reject", target_logits.device, need)
+    _check(lib.spec_reject_sample(_need(target_logits, torch.float32, "target_logits"),
+                                  _need(draft_logits, torch.float32, "draft_logits"),
+                                  _need(draft_tokens, torch.int32, "draft_tokens"),
+                                  _need(seq_ids, torch.int64, "seq_ids"), _need(seq_lens, torch.int32, "seq_lens"),
+                                  B, k, V, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                  _need(out_tokens, torch.int32, "out_tokens"),
+                                  _need(num_accepted, torch.int32, "num_accepted"),
+                                  _opt(out_probs, torch.float32, "out_probs"),
+                                  _opt(accept_probs, torch.float32, "accept_probs"),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream)), "spec_reject_sample")
+    return out_tokens, num_accepted
+
+
+def commit_lengths(seq_lens, num_accepted, k: int, capacity_tokens: int, overflow_flags=None, stream=None):
+    """spec_commit_lengths: seq_lens[b] += num_accepted[b] + 1 unless past capacity_tokens."""
+    import torch
+    B = seq_lens.shape[0]
+    _check(library().spec_commit_lengths(_need(seq_lens, torch.int32, "seq_lens"),
+                                         _need(num_accepted, torch.int32, "num_accepted"), B, int(k),
+                                         int(capacity_tokens), _opt(overflow_flags, torch.int32, "overflow_flags"),
+                                         _stream_handle(stream)), "spec_commit_lengths")
+    return seq_lens
+
+
+def verify_step(q, k_cache, v_cache, block_table, seq_lens, attn_out, max_seq_len, target_logits, draft_logits,
+                draft_tokens, seq_ids, temperature, seed, out_tokens, num_accepted, capacity_tokens,
+                out_probs=None, accept_probs=None, overflow_flags=None, sm_scale=None, stream=None):
+    """One verify step on one stream: attention, rejection sampling, commit.
+
+    The logits are taken as given (the LM head between attention and sampling is
+    the caller's); seq_lens is read by the first two calls and updated by the third.
+    """
+    verify_attn(q, k_cache, v_cache, block_table, seq_lens, attn_out, max_seq_len, sm_scale, stream=stream)
+    reject_sample(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, temperature, seed, out_tokens,
+                  num_accepted, out_probs, accept_probs, stream=stream)
+    commit_lengths(seq_lens, num_accepted, draft_tokens.shape[1], capacity_tokens, overflow_flags, stream=stream)
+    return out_tokens, num_accepted

@@ -1,0 +1,150 @@
+// C-ABI of libspecverify.so: argument validation, launch geometry, status codes.
+// The entry points and their contracts are declared in include/specverify.h.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "specverify.h"
+
+using namespace specverify;
+
+namespace {
+
+// Per-device memo of the gfx950 check (0 unknown, 1 gfx950, 2 other); immutable once set.
+std::atomic<int> g_arch_ok[64];
+
+spec_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return SPEC_ERR_NO_DEVICE;
+    }
+    if (dev < 64) {
+        const int memo = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (memo == 1) return SPEC_OK;
+        if (memo == 2) return SPEC_ERR_NO_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SPEC_ERR_NO_DEVICE;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? SPEC_OK : SPEC_ERR_NO_DEVICE;
+}
+
+bool is_pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+spec_status attn_shape_check(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len) {
+    if (B < 1 || B > 65535) return SPEC_ERR_BAD_SHAPE;
+    if (k < 1 || k > 15) return SPEC_ERR_BAD_SHAPE;
+    if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return SPEC_ERR_BAD_SHAPE;
+    if (max_seq_len < k + 1) return SPEC_ERR_BAD_SHAPE;
+    const long long rows = static_cast<long long>(k + 1) * (Hq / Hkv);
+    if (static_cast<long long>(Hkv) * ((rows + 31) / 32) > 65535) return SPEC_ERR_BAD_SHAPE;
+    return SPEC_OK;
+}
+
+spec_status from_hip(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(spec_status s) {
+    switch (s) {
+        case SPEC_OK: return "ok";
+        case SPEC_ERR_NULL_POINTER: return "a required pointer argument is NULL";
+        case SPEC_ERR_BAD_SHAPE: return "a size argument is outside the supported range";
+        case SPEC_ERR_BAD_VALUE: return "a scalar argument (temperature or scale) is invalid";
+        case SPEC_ERR_WORKSPACE_TOO_SMALL: return "workspace is smaller than the reported size";
+        case SPEC_ERR_NO_DEVICE: return "no HIP device, or the current device is not gfx950";
+        case SPEC_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        case SPEC_ERR_UNIMPLEMENTED: return "shape combination not built into this library";
+        default: return "unknown status";
+    }
+}
+
+int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+spec_status spec_verify_attn_workspace_size(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t max_seq_len, size_t* bytes_out) {
+    if (!bytes_out) return SPEC_ERR_NULL_POINTER;
+    const spec_status s = attn_shape_check(B, k, Hq, Hkv, D, max_seq_len);
+    if (s != SPEC_OK) return s;
+    *bytes_out = attn_geometry(B, k, Hq, Hkv, D, max_seq_len).workspace;
+    return SPEC_OK;
+}
+
+spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, void* out,
+                             int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t block_size, int32_t max_blocks, int32_t num_blocks,
+                             int32_t max_seq_len, float sm_scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return SPEC_ERR_NULL_POINTER;
+    spec_status s = attn_shape_check(B, k, Hq, Hkv, D, max_seq_len);
+    if (s != SPEC_OK) return s;
+    if (!is_pow2_in(block_size, 16, 64)) return SPEC_ERR_BAD_SHAPE;
+    if (max_blocks < 1 || num_blocks < 1) return SPEC_ERR_BAD_SHAPE;
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return SPEC_ERR_BAD_VALUE;
+    const AttnGeometry geo = attn_geometry(B, k, Hq, Hkv, D, max_seq_len);
+    if (geo.workspace > 0 && !workspace) return SPEC_ERR_NULL_POINTER;
+    if (workspace_bytes < geo.workspace) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    if ((s = check_device()) != SPEC_OK) return s;
+    AttnLaunch p;
+    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
+    p.block_table = block_table; p.seq_lens = seq_lens; p.out = out;
+    p.B = B; p.k = k; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
+    p.block_size = block_size; p.max_blocks = max_blocks; p.num_blocks = num_blocks;
+    p.max_seq_len = max_seq_len; p.sm_scale = sm_scale;
+    p.workspace = workspace;
+    return from_hip(launch_attn(p, geo, static_cast<hipStream_t>(stream)));
+}
+
+spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out) {
+    if (!bytes_out) return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2) return SPEC_ERR_BAD_SHAPE;
+    *bytes_out = reject_workspace_bytes(B, k, V);
+    return SPEC_OK;
+}
+
+spec_status spec_reject_sample(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, const int64_t* seq_ids,
+                               const int32_t* seq_lens, int32_t B, int32_t k, int32_t V,
+                               float temperature, uint64_t seed,
+                               int32_t* out_tokens, int32_t* num_accepted,
+                               float* out_probs, float* accept_probs,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (!target_logits || !draft_logits || !draft_tokens || !seq_ids || !seq_lens || !out_tokens ||
+        !num_accepted || !workspace)
+        return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2) return SPEC_ERR_BAD_SHAPE;
+    if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
+    if (workspace_bytes < reject_workspace_bytes(B, k, V)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    RejectLaunch p;
+    p.target_logits = target_logits; p.draft_logits = draft_logits; p.draft_tokens = draft_tokens;
+    p.seq_ids = seq_ids; p.seq_lens = seq_lens;
+    p.B = B; p.k = k; p.V = V; p.temperature = temperature; p.seed = seed;
+    p.out_tokens = out_tokens; p.num_accepted = num_accepted;
+    p.out_probs = out_probs; p.accept_probs = accept_probs;
+    p.workspace = workspace;
+    return from_hip(launch_reject(p, static_cast<hipStream_t>(stream)));
+}
+
+spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
+                                int32_t capacity_tokens, int32_t* overflow_flags, void* stream) {
+    if (!seq_lens || !num_accepted) return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || k < 1 || k > 15 || capacity_tokens < 1) return SPEC_ERR_BAD_SHAPE;
+    const spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    return from_hip(launch_commit(seq_lens, num_accepted, B, capacity_tokens, overflow_flags,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specverify {
+
+struct AttnLaunch {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* out;
+    int B, k, Hq, Hkv, D, block_size, max_blocks, num_blocks, max_seq_len;
+    float sm_scale;
+    void* workspace;
+};
+
+struct AttnGeometry {
+    int rows;          // (k+1) * G query rows per KV head
+    int tiles;         // 16-row MFMA tiles per row group (1 or 2)
+    int row_groups;    // groups of up to 32 rows
+    int chunk;         // keys per workgroup (multiple of 128)
+    int splits;        // max KV splits per (sequence, KV head)
+    size_t workspace;  // bytes
+};
+
+AttnGeometry attn_geometry(int B, int k, int Hq, int Hkv, int D, int max_seq_len);
+hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& g, hipStream_t stream);
+
+struct RejectLaunch {
+    const float* target_logits;
+    const float* draft_logits;
+    const int32_t* draft_tokens;
+    const int64_t* seq_ids;
+    const int32_t* seq_lens;
+    int B, k, V;
+    float temperature;
+    uint64_t seed;
+    int32_t* out_tokens;
+    int32_t* num_accepted;
+    float* out_probs;
+    float* accept_probs;
+    void* workspace;
+};
+
+size_t reject_workspace_bytes(int B, int k, int V);
+hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream);
+
+hipError_t launch_commit(int32_t* seq_lens, const int32_t* num_accepted, int B, int capacity,
+                         int32_t* overflow_flags, hipStream_t stream);
+
+}  // namespace specverify
