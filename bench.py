@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = spec_verify_attn (one attention layer) + spec_reject_sample +
+spec_commit_lengths over one batch of the 8B-shaped workload (B=64, k=3,
+Hq=32, Hkv=8, D=128, contexts U[1024, 8192] in 16-token pages, vocab 128256,
+T=1). Inputs are seeded synthetic arrays resident in HBM before timing; the
+committed lengths are restored before every step so each step does the same
+work. Prints one JSON line:
+
+  value     verified tokens/s = sum_b (a_b + 1) per step / wall time per step
+  roofline  the dominant call (verify attention): algorithmic bytes / its
+            average duration from HIP events on the launch stream, vs 8 TB/s
+  cpu_baseline  the fp64 oracle on this host's cores, on a bounded sample
+
+Other modes:
+  --cpu-baseline-only          time the oracle (run in a single-threaded child)
+  --copy-calibration           also run a plain device copy of known size (for
+                               scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)
+  --summarize-rocprof DIR      turn rocprofv3 output in DIR into a text summary
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified tokens/s + HBM GB/s (% of peak) for spec verify, 8B shape, k=3"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_counters.txt")
+KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/attention.hip",
+                  "speculative_decoding_verification_14_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(preset, seq_lens, num_accepted):
+    """Bytes the method itself must move (each K/V row, Q/O row, examined logits row once)."""
+    import numpy as np
+    L = np.asarray(seq_lens, dtype=np.int64)
+    a = np.asarray(num_accepted, dtype=np.int64)
+    B, k, Hq, Hkv, D, bs, V = preset.B, preset.k, preset.Hq, preset.Hkv, preset.D, preset.block_size, preset.V
+    n_keys = L + k + 1
+    attn = int(np.sum(n_keys) * Hkv * D * 2 * 2 + 2 * B * (k + 1) * Hq * D * 2
+               + np.sum((n_keys + bs - 1) // bs) * 4 + B * 4)
+    rows = (a + 1) + np.minimum(a + 1, k)
+    reject = int(np.sum(rows) * V * 4 + B * (k * 4 + 8 + 4) + B * (k + 1) * 8 + B * (4 + k * 4))
+    commit = int(B * 4 * 3)
+    return attn, reject, commit
+
+
+def stored_traffic():
+    """HBM bytes per verify-attention call from committed rocprofv3 counter runs, if still valid."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, v = line.partition(":")
+                vals[key.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(workload: str, attn_pairs: int = 48, seed_offset: int = 0) -> dict:
+    """Oracle seconds per step, extrapolated from a bounded sample, on this process's threads."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import commit as ocommit
+    from oracle import reject as orej
+    from workloads import PRESETS, make_inputs
+    p = PRESETS[workload]
+    inp = make_inputs(workload)
+    rng = np.random.default_rng(1234 + seed_offset)
+    all_pairs = [(b, g) for b in range(p.B) for g in range(p.Hkv)]
+    pick = [all_pairs[i] for i in rng.choice(len(all_pairs), size=min(attn_pairs, len(all_pairs)), replace=False)]
+    t0 = time.perf_counter()
+    oatt.verify_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"], p.k,
+                          p.Hq, p.Hkv, p.block_size, inp["sm_scale"], pairs=pick)
+    t_attn_sample = time.perf_counter() - t0
+    # scale by keys covered, since pairs differ in context length
+    keys_all = float(np.sum(inp["seq_lens"].astype(np.int64) + p.k + 1)) * p.Hkv
+    keys_pick = float(sum(int(inp["seq_lens"][b]) + p.k + 1 for b, _ in pick))
+    t_attn = t_attn_sample * keys_all / keys_pick
+    t0 = time.perf_counter()
+    res = orej.verify_batch(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["seq_ids"],
+                            inp["seq_lens"], p.k, p.temperature, inp["seed"])
+    t_rej = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ocommit.commit_lengths(inp["seq_lens"], res["num_accepted"], inp["max_blocks"] * p.block_size)
+    t_commit = time.perf_counter() - t0
+    tokens = int(np.sum(res["num_accepted"] + 1))
+    total = t_attn + t_rej + t_commit
+    return dict(seconds_per_step=total, attn_seconds=t_attn, reject_seconds=t_rej, tokens_per_step=tokens,
+                tokens_per_s=tokens / total, attn_pairs=len(pick), attn_sample_seconds=t_attn_sample,
+                sample=(f"attention of {len(pick)} of {len(all_pairs)} (sequence, KV head) pairs timed and "
+                        f"scaled by key count; rejection sampling of all {p.B} sequences and the commit timed "
+                        f"in full; one step of the {workload} workload"))
+
+
+def run_cpu_baseline_child(workload: str) -> dict | None:
+    env = dict(os.environ)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS",
+                "NUMEXPR_NUM_THREADS"):
+        env[var] = "1"
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", "--workload", workload]
+    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr[-2000:])
+        return None
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+# ----------------------------------------------------------------------------- rocprof summary
+
+def _kernel_label(name: str) -> str:
+    """Readable kernel name: namespaces and the argument list dropped, template arguments kept."""
+    name = name.replace("(anonymous namespace)::", "").replace("specverify::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return name[:cut][:70]
+
+
+def summarize_rocprof(path: str, out: str, command: str) -> None:
+    """Summarise rocprofv3 kernel stats and/or counter CSVs found under ``path``."""
+    lines = [f"# rocprofv3 summary", f"# command: {command}", ""]
+    stats = sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True))
+    for s in stats:
+        lines.append(f"## kernel stats ({os.path.relpath(s, path)})")
+        lines.append(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+        with open(s) as f:
+            for row in csv.DictReader(f):
+                short = _kernel_label(row["Name"])
+                lines.append(f"{short:70s} {int(row['Calls']):6d} {float(row['AverageNs']) / 1e3:10.2f} "
+                             f"{float(row['MinNs']) / 1e3:10.2f} {float(row['MaxNs']) / 1e3:10.2f} "
+                             f"{float(row['Percentage']):6.2f}")
+        lines.append("")
+    ctrs = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    for c in ctrs:
+        lines.append(f"## counters per dispatch, averaged by kernel ({os.path.relpath(c, path)})")
+        agg = {}
+        with open(c) as f:
+            for row in csv.DictReader(f):
+                key = (_kernel_label(row["Kernel_Name"]), row["Counter_Name"])
+                agg.setdefault(key, []).append(float(row["Counter_Value"]))
+        lines.append(f"{'kernel':70s} {'counter':>12s} {'dispatches':>10s} {'mean':>16s}")
+        for (k, cn), v in sorted(agg.items()):
+            lines.append(f"{k:70s} {cn:>12s} {len(v):10d} {sum(v) / len(v):16.1f}")
+        lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ----------------------------------------------------------------------------- GPU benchmark
+
+def gpu_bench(args) -> dict:
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_14_amd as sv
+    from workloads import PRESETS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU (one MI355X)")
+    sv.library()
+    dev = torch.device("cuda:0")
+    p = PRESETS[args.workload]
+    print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
+    inp = make_inputs(args.workload)
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q, kc, vc = bf16(inp["q"]), bf16(inp["k_cache"]), bf16(inp["v_cache"])
+    bt = t(inp["block_table"])
+    seq_lens0 = t(inp["seq_lens"])
+    seq_lens = seq_lens0.clone()
+    tl, dl, dt, sid = t(inp["target_logits"]), t(inp["draft_logits"]), t(inp["draft_tokens"]), t(inp["seq_ids"])
+    B, k = p.B, p.k
+    attn_out = torch.empty_like(q)
+    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    num_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out_probs = torch.empty((B, k + 1), dtype=torch.float32, device=dev)
+    acc_probs = torch.empty((B, k), dtype=torch.float32, device=dev)
+    overflow = torch.empty(B, dtype=torch.int32, device=dev)
+    cap = inp["max_blocks"] * p.block_size
+    msl = inp["max_seq_len"]
+    attn_ws = torch.zeros(max(256, sv.verify_attn_workspace_size(B, k, p.Hq, p.Hkv, p.D, msl)),
+                          dtype=torch.uint8, device=dev)
+    rej_ws = torch.zeros(sv.reject_sample_workspace_size(B, k, p.V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    del inp["k_cache"], inp["v_cache"]
+
+    def step(events=None):
+        seq_lens.copy_(seq_lens0)
+        if events is not None:
+            events[0].record(stream)
+        sv.verify_attn(q, kc, vc, bt, seq_lens, attn_out, msl, None, attn_ws, stream)
+        if events is not None:
+            events[1].record(stream)
+        sv.reject_sample(tl, dl, dt, sid, seq_lens, p.temperature, inp["seed"], out_tokens, num_acc, out_probs,
+                         acc_probs, rej_ws, stream)
+        if events is not None:
+            events[2].record(stream)
+        sv.commit_lengths(seq_lens, num_acc, k, cap, overflow, stream)
+        if events is not None:
+            events[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    acc_ref = num_acc.cpu().numpy().copy()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rej_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    com_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    acc = num_acc.cpu().numpy()
+    if not np.array_equal(acc, acc_ref):
+        raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
+
+    copy_info = None
+    if args.copy_calibration:
+        n = 1 << 29   # 512 MiB copied = 512 MiB read + 512 MiB written
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        copy_info = dict(bytes_read=n, bytes_written=n, calls=3)
+
+    tokens = int(np.sum(acc + 1))
+    a_bytes, r_bytes, c_bytes = algorithmic_bytes(p, np.asarray(seq_lens0.cpu()), acc)
+    mean = lambda v: sum(v) / len(v)
+    med = lambda v: sorted(v)[len(v) // 2]
+    attn_avg_s = mean(attn_ms) / 1e3
+    rej_avg_s = mean(rej_ms) / 1e3
+    com_avg_s = mean(com_ms) / 1e3
+    step_s = wall / args.steps
+    attn_gbs = a_bytes / attn_avg_s / 1e9
+    rej_gbs = r_bytes / rej_avg_s / 1e9
+    traffic = stored_traffic()
+    result = dict(
+        metric=METRIC, value=tokens / step_s, unit="verified tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=step_s * 1e3, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=(f"{args.workload}: B={B}, k={k}, Hq={p.Hq}, Hkv={p.Hkv}, D={p.D}, "
+                              f"contexts {p.ctx}, block_size={p.block_size}, V={p.V}, T={p.temperature}, "
+                              "one attention layer + rejection sampling + commit"),
+                    global_batch=B, k=k, parallelism="none (1 GPU)"),
+        roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=attn_gbs / HBM_PEAK_GBS, traffic=traffic,
+                      kernel="spec_verify_attn (attn_partial_kernel + attn_merge_kernel)",
+                      algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_avg_s * 1e6),
+        verified_tokens_per_step=tokens,
+        mean_emitted_per_sequence=tokens / B,
+        step_gbs=(a_bytes + r_bytes + c_bytes) / step_s / 1e9,
+        kernels=dict(
+            verify_attn=dict(avg_us=attn_avg_s * 1e6, median_us=med(attn_ms) * 1e3, bytes=a_bytes, gbs=attn_gbs,
+                             frac_of_peak=attn_gbs / HBM_PEAK_GBS),
+            reject_sample=dict(avg_us=rej_avg_s * 1e6, median_us=med(rej_ms) * 1e3, bytes=r_bytes, gbs=rej_gbs,
+                               frac_of_peak=rej_gbs / HBM_PEAK_GBS),
+            commit_lengths=dict(avg_us=com_avg_s * 1e6, bytes=c_bytes)),
+        event_sum_ms_per_step=(attn_avg_s + rej_avg_s + com_avg_s) * 1e3,
+    )
+    if copy_info:
+        result["copy_calibration"] = copy_info
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--out", metavar="FILE")
+    ap.add_argument("--command", default="", help="command line recorded in a rocprof summary")
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.out or "/dev/stdout", args.command)
+        return
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline(args.workload)))
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the verify step is data parallel over sequences; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    result = gpu_bench(args)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cb = run_cpu_baseline_child(args.workload)
+        if cb is not None:
+            result["cpu_baseline"] = dict(value=cb["tokens_per_s"], unit="verified tokens/s", cores=1,
+                                          kind="oracle", sample=cb["sample"],
+                                          seconds_per_step=cb["seconds_per_step"],
+                                          cpu=_cpu_model())
+    print(json.dumps(result))
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -134,41 +134,35 @@ __global__ __launch_bounds__(kAT) void attn_partial_kernel(AttnArgs a) {
     }
 
     const size_t head_stride = size_t(D) << a.bs_log2;   // elements per (block, KV head)
-    for (int t0 = c0 + wave * kBlockKeys; t0 < c1; t0 += kAWaves * kBlockKeys) {
-        // ---- K fragments: tile t, lane row l16 holds key t0 + 8*(l16/4) + 4t + l16%4.
-        uint4 kraw[2][DS];
+
+    // Fragments of one 32-key block. K: tile t, lane row l16 holds key
+    // t0 + 8*(l16/4) + 4t + l16%4, dims 32*ds + 8*lg .. +7. V: lane holds keys
+    // t0 + 8*lg .. +7 of dims 16j + l16. Addresses are clamped into the chunk so
+    // the loads are unconditional and can all be in flight; keys >= c1 are masked
+    // (scores) or zeroed (values) when the block is consumed.
+    auto load_block = [&](int t0, uint4 (&kr)[2][DS], uint4 (&vr)[DJ]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int key = t0 + 8 * (l16 >> 2) + 4 * t + (l16 & 3);
-            if (key < c1) {
-                const int pg = s_bt[(key >> a.bs_log2) - p0];
-                const uint16_t* kp = a.kc + (size_t(pg) * a.Hkv + g) * head_stride +
-                                     size_t(key & (bs - 1)) * D + 8 * lg;
+            const int key = min(t0 + 8 * (l16 >> 2) + 4 * t + (l16 & 3), c1 - 1);
+            const int pg = s_bt[(key >> a.bs_log2) - p0];
+            const uint16_t* kp = a.kc + (size_t(pg) * a.Hkv + g) * head_stride + size_t(key & (bs - 1)) * D + 8 * lg;
 #pragma unroll
-                for (int ds = 0; ds < DS; ++ds) kraw[t][ds] = load16(kp + 32 * ds);
-            } else {
-#pragma unroll
-                for (int ds = 0; ds < DS; ++ds) kraw[t][ds] = make_uint4(0, 0, 0, 0);
-            }
+            for (int ds = 0; ds < DS; ++ds) kr[t][ds] = load16(kp + 32 * ds);
         }
-        // ---- V fragments: lane holds keys t0 + 8*lg .. +7 of dims 16j + l16.
-        uint4 vraw[DJ];
-        const int vkey0 = t0 + 8 * lg;
-        if (vkey0 < c1) {
-            const int pg = s_bt[(vkey0 >> a.bs_log2) - p0];
-            const uint16_t* vp = a.vc + (size_t(pg) * a.Hkv + g) * head_stride + (vkey0 & (bs - 1));
+        const int vkey0 = min(t0 + 8 * lg, (c1 - 1) & ~7);
+        const int pg = s_bt[(vkey0 >> a.bs_log2) - p0];
+        const uint16_t* vp = a.vc + (size_t(pg) * a.Hkv + g) * head_stride + (vkey0 & (bs - 1));
 #pragma unroll
-            for (int j = 0; j < DJ; ++j) vraw[j] = load16(vp + size_t(16 * j + l16) * bs);
-            if (vkey0 + 8 > c1) {
-#pragma unroll
-                for (int j = 0; j < DJ; ++j) vraw[j] = zero_keys_from(vraw[j], vkey0, c1);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < DJ; ++j) vraw[j] = make_uint4(0, 0, 0, 0);
-        }
+        for (int j = 0; j < DJ; ++j) vr[j] = load16(vp + size_t(16 * j + l16) * bs);
+    };
 
+    auto compute_block = [&](int t0, uint4 (&kr)[2][DS], uint4 (&vr)[DJ]) {
         const bool full = (t0 + kBlockKeys <= c1) && (t0 + kBlockKeys - 1 <= L);
+        if (t0 + kBlockKeys > c1) {
+            // tail block: values of keys >= c1 (other splits' keys or garbage) become 0
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) vr[j] = zero_keys_from(vr[j], t0 + 8 * lg, c1);
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             f32x4 st[2];
@@ -177,7 +171,7 @@ __global__ __launch_bounds__(kAT) void attn_partial_kernel(AttnArgs a) {
                 f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kraw[t][ds]), qop[n][ds], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t][ds]), qop[n][ds], acc, 0, 0, 0);
                 st[t] = acc;
             }
             // lane's scores: row l16 of tile n, keys t0 + 8*lg + i (i = 4t + e)
@@ -214,9 +208,16 @@ __global__ __launch_bounds__(kAT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < DJ; ++j) {
                 o[n][j] *= alpha;
-                o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vraw[j]), pop, o[n][j], 0, 0, 0);
+                o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[j]), pop, o[n][j], 0, 0, 0);
             }
         }
+    };
+
+    constexpr int kStep = kAWaves * kBlockKeys;
+    for (int t0 = c0 + wave * kBlockKeys; t0 < c1; t0 += kStep) {
+        uint4 kr[2][DS], vr[DJ];
+        load_block(t0, kr, vr);
+        compute_block(t0, kr, vr);
     }
 
     // ---- combine the four waves: per row, M = max over waves, weights 2^(m_w - M).
