@@ -45,6 +45,9 @@ spec_status attn_shape_check(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int3
     if (max_seq_len < k + 1) return SPEC_ERR_BAD_SHAPE;
     const long long rows = static_cast<long long>(k + 1) * (Hq / Hkv);
     if (static_cast<long long>(Hkv) * ((rows + 31) / 32) > 65535) return SPEC_ERR_BAD_SHAPE;
+    // the per-sequence work prefix (128-key iterations) is kept in int32
+    if (static_cast<long long>(B) * ((static_cast<long long>(max_seq_len) + 127) / 128) > 0x7FFFFFFFLL)
+        return SPEC_ERR_BAD_SHAPE;
     return SPEC_OK;
 }
 

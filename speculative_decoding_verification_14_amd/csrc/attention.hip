@@ -7,23 +7,27 @@
 // inside the draft), query head h reads KV head h / G.
 //
 // How (one MI355X):
-//  * One workgroup (4 waves) per (sequence, KV head, row group, KV split). The
-//    (k+1) x G query rows of a KV head are packed into 16-row tiles, so both
-//    products are dense 16-wide contractions and run on v_mfma_f32_16x16x32_bf16:
-//      S^T = K Q^T   (A = 16 keys x 32 dims from the K page, B = Q^T from registers)
-//      O^T += V^T P^T (A = 16 dims x 32 keys from the V page, B = P^T from registers)
+//  * MFMA tiles. The (k+1) x G query rows of a KV head are packed into 16-row
+//    tiles, so both products are dense 16-wide contractions on
+//    v_mfma_f32_16x16x32_bf16:
+//      S^T = K Q^T    (A = 16 keys x 32 dims from the K page, B = Q^T in registers)
+//      O^T += V^T P^T (A = 16 dims x 32 keys from the V page, B = P^T in registers)
 //    Computing the transposes puts the softmax statistics of query row r and the
 //    accumulators of O^T[., r] on the same lanes (lane % 16 == r), so the online
-//    softmax needs no cross-lane traffic beyond a 4-lane max.
-//  * Every operand fetch is a 16-byte global load straight into MFMA registers:
-//    K pages are [block][Hkv][slot][D] (8 consecutive dims of a key), V pages are
-//    [block][Hkv][D][slot] (8 consecutive keys of a dim). Each K/V byte of a
-//    sequence is read exactly once; there is no reuse for LDS to exploit, so LDS
-//    holds only the block-table slice of the chunk and the cross-wave combine.
-//  * Waves take interleaved 32-key blocks of the workgroup's chunk; at the end the
-//    four waves' (max, sum, O) are combined through LDS. A sequence that fits one
-//    chunk writes its bf16 output directly; longer ones write fp32 partials that
-//    the merge kernel combines in split order (deterministic).
+//    softmax needs only a 4-lane max. Operands are 16-byte global loads straight
+//    into MFMA registers: K pages are [block][Hkv][slot][D], V pages are
+//    [block][Hkv][D][slot]. Each K/V byte is read once; LDS holds only the
+//    block-table slice and the cross-wave combine.
+//  * Persistent, balanced grid. Contexts are ragged, so a grid of fixed-size KV
+//    splits leaves half its workgroups empty and a ragged tail. Instead the work
+//    of all (sequence, KV head, 128-key iteration) triples is laid out in one
+//    flat order and P = CUs x occupancy workgroups each take an equal contiguous
+//    share. A share covers whole (sequence, head) segments, whose output is
+//    written directly, plus at most one partial segment at each end, written as
+//    fp32 (max, sum, O) partials; a merge launch combines the pieces of a split
+//    segment in workgroup order (deterministic).
+//  * Inside a piece the four waves take interleaved 32-key blocks; at the end the
+//    waves' (max, sum, O) are combined through LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,8 +37,11 @@ namespace {
 constexpr int kAT = 256;
 constexpr int kAWaves = kAT / kWave;
 constexpr int kBlockKeys = 32;
-constexpr int kMaxChunk = 16384;
-constexpr int kMaxChunkPages = kMaxChunk / 16;
+constexpr int kIterKeys = kAWaves * kBlockKeys;     // keys per workgroup iteration
+constexpr int kBtSpan = 4096;                       // keys whose block-table entries sit in LDS at once
+constexpr int kBtEntries = kBtSpan / 16;
+constexpr int kLdsPrefix = 4096;                    // batch sizes whose work prefix each workgroup builds in LDS
+constexpr int kMaxP = 1024;                         // workgroups of the persistent grid (workspace is sized for this)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -44,9 +51,10 @@ struct AttnArgs {
     const int32_t* bt;
     const int32_t* seq_lens;
     uint16_t* out;
-    float* part_o;     // [B][Hkv][RG][splits][32 rows][D]
-    float* part_ml;    // [B][Hkv][RG][splits][32 rows][2]
-    int k, Hq, Hkv, G, rows, row_groups, max_blocks, bs_log2, chunk, splits;
+    float* part_o;     // [kMaxP][2][32 rows][D]
+    float* part_ml;    // [kMaxP][2][32 rows][2]
+    int32_t* prefix;   // [B+1] exclusive prefix of iterations per sequence
+    int B, k, Hq, Hkv, G, rows, row_groups, U, max_blocks, bs_log2, P;
     float scale_log2;
 };
 
@@ -75,251 +83,339 @@ __device__ __forceinline__ uint4 zero_keys_from(uint4 v, int key0, int limit) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+__device__ __forceinline__ int iters_of(int seq_len, int k) {
+    const int n = seq_len + k + 1;
+    return n <= 0 ? 0 : (n + kIterKeys - 1) / kIterKeys;
+}
+
+// Workgroup w of P owns flat positions [range_start(w), range_start(w+1)).
+__device__ __forceinline__ long long range_start(int w, long long total, int P) {
+    const long long q = total / P, r = total % P;
+    return w * q + (w < r ? w : r);
+}
+
+__device__ __forceinline__ int range_owner(long long x, long long total, int P) {
+    const long long q = total / P, r = total % P;
+    if (x < r * (q + 1)) return static_cast<int>(x / (q + 1));
+    return static_cast<int>(r + (x - r * (q + 1)) / q);
+}
+
+// Exclusive prefix of iterations per sequence, built by one 256-thread workgroup
+// into `dst` (LDS or global); dst[B] is the total.
+__device__ void build_prefix(const int32_t* seq_lens, int B, int k, int32_t* dst, int* s_wave) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    int carry = 0;
+    for (int base = 0; base < B; base += kAT) {
+        const int b = base + tid;
+        int v = (b < B) ? iters_of(seq_lens[b], k) : 0;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(v, o, kWave);
+            if (lane >= o) v += y;
+        }
+        if (lane == kWave - 1) s_wave[wave] = v;
+        __syncthreads();
+        int before = carry;
+        for (int i = 0; i < wave; ++i) before += s_wave[i];
+        if (b < B) dst[b + 1] = before + v;
+        int tot = carry;
+        for (int i = 0; i < kAWaves; ++i) tot += s_wave[i];
+        __syncthreads();
+        carry = tot;
+    }
+    if (tid == 0) dst[0] = 0;
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kAT) void attn_plan_kernel(const int32_t* seq_lens, int B, int k, int32_t* prefix) {
+    __shared__ int s_wave[kAWaves];
+    build_prefix(seq_lens, B, k, prefix, s_wave);
+}
+
 template <int D, int NT>
-__global__ __launch_bounds__(kAT) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
     constexpr int DS = D / 32;   // k-steps of S^T = K Q^T
     constexpr int DJ = D / 16;   // 16-dim blocks of O^T
-    __shared__ int s_bt[kMaxChunkPages];
+    __shared__ int s_bt[kBtEntries];
+    __shared__ int32_t s_prefix[kLdsPrefix + 1];
+    __shared__ int s_wave[kAWaves];
     __shared__ float s_m[kAWaves][NT][16];
     __shared__ float s_l[kAWaves][NT][16];
     __shared__ float s_o[kAWaves][16][D + 4];
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y / a.row_groups, rg = blockIdx.y % a.row_groups;
-    const int b = blockIdx.z;
-    const int L = a.seq_lens[b];
-    const int N = L + a.k + 1;
-    const int c0 = split * a.chunk;
-    if (c0 >= N) return;
-    const int c1 = min(N, c0 + a.chunk);
-    // clamped to the grid: lengths past max_seq_len (a broken precondition) lose keys, never fault
-    const int n_splits_b = min(a.splits, (N + a.chunk - 1) / a.chunk);
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int l16 = lane & 15, lg = lane >> 4;
     const int bs = 1 << a.bs_log2;
+    const int w = blockIdx.x;
 
-    const int p0 = c0 >> a.bs_log2;
-    const int np = ((c1 - 1) >> a.bs_log2) - p0 + 1;
-    for (int i = tid; i < np; i += kAT) s_bt[i] = a.bt[size_t(b) * a.max_blocks + p0 + i];
-
-    // Q^T operands and the last visible key of this lane's query row in each tile.
-    bf16x8 qop[NT][DS];
-    int lim[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int r = rg * 32 + n * 16 + l16;
-        if (r < a.rows) {
-            const int i = r / a.G;
-            const int h = g * a.G + r % a.G;
-            const uint16_t* qp = a.q + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + 8 * lg;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(load16(qp + 32 * ds));
-            lim[n] = L + i;
-        } else {
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
-            lim[n] = N - 1;   // padding rows: harmless finite result, never stored
-        }
+    const int32_t* prefix = a.prefix;
+    if (a.B <= kLdsPrefix) {
+        build_prefix(a.seq_lens, a.B, a.k, s_prefix, s_wave);
+        if (w == 0)
+            for (int i = tid; i <= a.B; i += kAT) a.prefix[i] = s_prefix[i];
+        prefix = s_prefix;
     }
-    __syncthreads();
+    const long long total = static_cast<long long>(a.U) * prefix[a.B];
+    const long long r0 = range_start(w, total, a.P), r1 = range_start(w + 1, total, a.P);
+    if (r0 >= r1) return;
 
-    float m_run[NT], l_run[NT];
-    f32x4 o[NT][DJ];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        m_run[n] = -INFINITY;
-        l_run[n] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < DJ; ++j) o[n][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // segment (b, u) starts at U * prefix[b] + u * iters_b; find the last b whose start is <= r0
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<long long>(a.U) * prefix[mid] <= r0) lo = mid; else hi = mid - 1;
     }
+    int b = lo;
+    int iters_b = prefix[b + 1] - prefix[b];
+    const long long off = r0 - static_cast<long long>(a.U) * prefix[b];
+    int u = static_cast<int>(off / iters_b);
+    int it0 = static_cast<int>(off % iters_b);
 
     const size_t head_stride = size_t(D) << a.bs_log2;   // elements per (block, KV head)
+    long long cur = r0;
+    bool first_piece = true;
+    while (cur < r1) {
+        const int it1 = static_cast<int>(min(static_cast<long long>(iters_b), it0 + (r1 - cur)));
+        const int g = u / a.row_groups, rg = u % a.row_groups;
+        const int L = a.seq_lens[b];
+        const int N = L + a.k + 1;
+        const int c0 = it0 * kIterKeys;
+        const int c1 = min(N, it1 * kIterKeys);
 
-    // Fragments of one 32-key block. K: tile t, lane row l16 holds key
-    // t0 + 8*(l16/4) + 4t + l16%4, dims 32*ds + 8*lg .. +7. V: lane holds keys
-    // t0 + 8*lg .. +7 of dims 16j + l16. Addresses are clamped into the chunk so
-    // the loads are unconditional and can all be in flight; keys >= c1 are masked
-    // (scores) or zeroed (values) when the block is consumed.
-    auto load_block = [&](int t0, uint4 (&kr)[2][DS], uint4 (&vr)[DJ]) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int key = min(t0 + 8 * (l16 >> 2) + 4 * t + (l16 & 3), c1 - 1);
-            const int pg = s_bt[(key >> a.bs_log2) - p0];
-            const uint16_t* kp = a.kc + (size_t(pg) * a.Hkv + g) * head_stride + size_t(key & (bs - 1)) * D + 8 * lg;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) kr[t][ds] = load16(kp + 32 * ds);
-        }
-        const int vkey0 = min(t0 + 8 * lg, (c1 - 1) & ~7);
-        const int pg = s_bt[(vkey0 >> a.bs_log2) - p0];
-        const uint16_t* vp = a.vc + (size_t(pg) * a.Hkv + g) * head_stride + (vkey0 & (bs - 1));
-#pragma unroll
-        for (int j = 0; j < DJ; ++j) vr[j] = load16(vp + size_t(16 * j + l16) * bs);
-    };
-
-    auto compute_block = [&](int t0, uint4 (&kr)[2][DS], uint4 (&vr)[DJ]) {
-        const bool full = (t0 + kBlockKeys <= c1) && (t0 + kBlockKeys - 1 <= L);
-        if (t0 + kBlockKeys > c1) {
-            // tail block: values of keys >= c1 (other splits' keys or garbage) become 0
-#pragma unroll
-            for (int j = 0; j < DJ; ++j) vr[j] = zero_keys_from(vr[j], t0 + 8 * lg, c1);
-        }
+        // Q^T operands and the last visible key of this lane's query row in each tile.
+        bf16x8 qop[NT][DS];
+        int lim[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            f32x4 st[2];
+            const int r = rg * 32 + n * 16 + l16;
+            if (r < a.rows) {
+                const int i = r / a.G;
+                const int h = g * a.G + r % a.G;
+                const uint16_t* qp = a.q + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + 8 * lg;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int ds = 0; ds < DS; ++ds)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t][ds]), qop[n][ds], acc, 0, 0, 0);
-                st[t] = acc;
-            }
-            // lane's scores: row l16 of tile n, keys t0 + 8*lg + i (i = 4t + e)
-            float sv[8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sv[4 * t + e] = st[t][e] * a.scale_log2;
-            if (!full) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int key = t0 + 8 * lg + i;
-                    if (key >= c1 || key > lim[n]) sv[i] = -INFINITY;
-                }
-            }
-            float bmax = sv[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sv[i]);
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
-            const float m_new = fmaxf(m_run[n], bmax);
-            const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_ref);
-            float p[8];
-            float psum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-                psum += p[i];
-            }
-            l_run[n] = l_run[n] * alpha + psum;
-            m_run[n] = m_new;
-            const bf16x8 pop = pack_bf16x8(p);
-#pragma unroll
-            for (int j = 0; j < DJ; ++j) {
-                o[n][j] *= alpha;
-                o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[j]), pop, o[n][j], 0, 0, 0);
-            }
-        }
-    };
-
-    constexpr int kStep = kAWaves * kBlockKeys;
-    for (int t0 = c0 + wave * kBlockKeys; t0 < c1; t0 += kStep) {
-        uint4 kr[2][DS], vr[DJ];
-        load_block(t0, kr, vr);
-        compute_block(t0, kr, vr);
-    }
-
-    // ---- combine the four waves: per row, M = max over waves, weights 2^(m_w - M).
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        float lt = l_run[n] + __shfl_xor(l_run[n], 16, kWave);
-        lt += __shfl_xor(lt, 32, kWave);
-        if (lg == 0) {
-            s_m[wave][n][l16] = m_run[n];
-            s_l[wave][n][l16] = lt;
-        }
-    }
-    __syncthreads();
-
-    const bool single = (n_splits_b == 1);
-    const size_t unit = (size_t(b) * a.Hkv + g) * a.row_groups + rg;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        // this lane's row l16: scale own accumulators by 2^(m_wave - M)
-        float M = s_m[0][n][l16];
-#pragma unroll
-        for (int v = 1; v < kAWaves; ++v) M = fmaxf(M, s_m[v][n][l16]);
-        const float M_ref = (M == -INFINITY) ? 0.0f : M;
-        const float wself = __builtin_amdgcn_exp2f(m_run[n] - M_ref);
-#pragma unroll
-        for (int j = 0; j < DJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s_o[wave][l16][16 * j + 4 * lg + e] = o[n][j][e] * wself;
-        __syncthreads();
-        // 256 threads: row r = tid / 16, dims (tid % 16) * (D/16) .. +D/16
-        {
-            const int r = tid / 16;
-            const int d0 = (tid % 16) * (D / 16);
-            float Mr = s_m[0][n][r];
-#pragma unroll
-            for (int v = 1; v < kAWaves; ++v) Mr = fmaxf(Mr, s_m[v][n][r]);
-            const float Mr_ref = (Mr == -INFINITY) ? 0.0f : Mr;
-            float lsum = 0.0f;
-#pragma unroll
-            for (int v = 0; v < kAWaves; ++v) lsum += s_l[v][n][r] * __builtin_amdgcn_exp2f(s_m[v][n][r] - Mr_ref);
-            float acc[D / 16];
-#pragma unroll
-            for (int dd = 0; dd < D / 16; ++dd) {
-                float x = 0.0f;
-#pragma unroll
-                for (int v = 0; v < kAWaves; ++v) x += s_o[v][r][d0 + dd];
-                acc[dd] = x;
-            }
-            const int row = rg * 32 + n * 16 + r;
-            if (single) {
-                if (row < a.rows) {
-                    const int i = row / a.G;
-                    const int h = g * a.G + row % a.G;
-                    uint16_t* op = a.out + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + d0;
-                    const float inv = 1.0f / lsum;
-#pragma unroll
-                    for (int dd = 0; dd < D / 16; ++dd) op[dd] = f32_to_bf16_bits(acc[dd] * inv);
-                }
+                for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(load16(qp + 32 * ds));
+                lim[n] = L + i;
             } else {
-                const size_t slot = (unit * a.splits + split) * 32 + n * 16 + r;
-                float* po = a.part_o + slot * D + d0;
 #pragma unroll
-                for (int dd = 0; dd < D / 16; ++dd) po[dd] = acc[dd];
-                if ((tid % 16) == 0) {
-                    a.part_ml[slot * 2 + 0] = Mr;
-                    a.part_ml[slot * 2 + 1] = lsum;
+                for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
+                lim[n] = N - 1;   // padding rows: harmless finite result, never stored
+            }
+        }
+
+        float m_run[NT], l_run[NT];
+        f32x4 o[NT][DJ];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            m_run[n] = -INFINITY;
+            l_run[n] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < DJ; ++j) o[n][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+
+        for (int s0 = c0; s0 < c1; s0 += kBtSpan) {
+            // s0 and every sub-range end below c1 are multiples of 128: no 32-key block straddles s1
+            const int s1 = min(c1, s0 + kBtSpan);
+            const int p0 = s0 >> a.bs_log2;
+            const int np = ((s1 - 1) >> a.bs_log2) - p0 + 1;
+            __syncthreads();
+            for (int i = tid; i < np; i += kAT) s_bt[i] = a.bt[size_t(b) * a.max_blocks + p0 + i];
+            __syncthreads();
+
+            // K: tile t, lane row l16 holds key t0 + 8*(l16/4) + 4t + l16%4, dims 32*ds + 8*lg .. +7.
+            // V: lane holds keys t0 + 8*lg .. +7 of dims 16j + l16. Addresses are clamped into
+            // the sub-range so the loads are unconditional; keys >= s1 are masked (scores) or
+            // zeroed (values) when the block is consumed.
+            for (int t0 = s0 + wave * kBlockKeys; t0 < s1; t0 += kIterKeys) {
+                uint4 kr[2][DS], vr[DJ];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int key = min(t0 + 8 * (l16 >> 2) + 4 * t + (l16 & 3), s1 - 1);
+                    const int pg = s_bt[(key >> a.bs_log2) - p0];
+                    const uint16_t* kp = a.kc + (size_t(pg) * a.Hkv + g) * head_stride +
+                                         size_t(key & (bs - 1)) * D + 8 * lg;
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) kr[t][ds] = load16(kp + 32 * ds);
+                }
+                {
+                    const int vkey0 = min(t0 + 8 * lg, (s1 - 1) & ~7);
+                    const int pg = s_bt[(vkey0 >> a.bs_log2) - p0];
+                    const uint16_t* vp = a.vc + (size_t(pg) * a.Hkv + g) * head_stride + (vkey0 & (bs - 1));
+#pragma unroll
+                    for (int j = 0; j < DJ; ++j) vr[j] = load16(vp + size_t(16 * j + l16) * bs);
+                }
+                if (t0 + kBlockKeys > s1) {
+                    // tail block: values of keys >= s1 (past the sequence, or another piece's) become 0
+#pragma unroll
+                    for (int j = 0; j < DJ; ++j) vr[j] = zero_keys_from(vr[j], t0 + 8 * lg, s1);
+                }
+                const bool full = (t0 + kBlockKeys <= s1) && (t0 + kBlockKeys - 1 <= L);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    f32x4 st[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int ds = 0; ds < DS; ++ds)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t][ds]), qop[n][ds], acc,
+                                                                         0, 0, 0);
+                        st[t] = acc;
+                    }
+                    // lane's scores: row l16 of tile n, keys t0 + 8*lg + i (i = 4t + e)
+                    float sv[8];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sv[4 * t + e] = st[t][e] * a.scale_log2;
+                    if (!full) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int key = t0 + 8 * lg + i;
+                            if (key >= s1 || key > lim[n]) sv[i] = -INFINITY;
+                        }
+                    }
+                    float bmax = sv[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sv[i]);
+                    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
+                    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
+                    const float m_new = fmaxf(m_run[n], bmax);
+                    const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_ref);
+                    float p[8];
+                    float psum = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+                        psum += p[i];
+                    }
+                    l_run[n] = l_run[n] * alpha + psum;
+                    m_run[n] = m_new;
+                    const bf16x8 pop = pack_bf16x8(p);
+#pragma unroll
+                    for (int j = 0; j < DJ; ++j) {
+                        o[n][j] *= alpha;
+                        o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[j]), pop, o[n][j], 0, 0, 0);
+                    }
                 }
             }
         }
+
+        // ---- combine the four waves: per row, M = max over waves, weights 2^(m_w - M).
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            float lt = l_run[n] + __shfl_xor(l_run[n], 16, kWave);
+            lt += __shfl_xor(lt, 32, kWave);
+            if (lg == 0) {
+                s_m[wave][n][l16] = m_run[n];
+                s_l[wave][n][l16] = lt;
+            }
+        }
         __syncthreads();
+        const bool whole = (it0 == 0) && (it1 == iters_b);
+        const size_t slot = size_t(w) * 2 + (first_piece ? 0 : 1);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            float M = s_m[0][n][l16];
+#pragma unroll
+            for (int v = 1; v < kAWaves; ++v) M = fmaxf(M, s_m[v][n][l16]);
+            const float M_ref = (M == -INFINITY) ? 0.0f : M;
+            const float wself = __builtin_amdgcn_exp2f(m_run[n] - M_ref);
+#pragma unroll
+            for (int j = 0; j < DJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s_o[wave][l16][16 * j + 4 * lg + e] = o[n][j][e] * wself;
+            __syncthreads();
+            {   // 256 threads: row r = tid / 16, dims (tid % 16) * (D/16) .. +D/16
+                const int r = tid / 16;
+                const int d0 = (tid % 16) * (D / 16);
+                float Mr = s_m[0][n][r];
+#pragma unroll
+                for (int v = 1; v < kAWaves; ++v) Mr = fmaxf(Mr, s_m[v][n][r]);
+                const float Mr_ref = (Mr == -INFINITY) ? 0.0f : Mr;
+                float lsum = 0.0f;
+#pragma unroll
+                for (int v = 0; v < kAWaves; ++v) lsum += s_l[v][n][r] * __builtin_amdgcn_exp2f(s_m[v][n][r] - Mr_ref);
+                float acc[D / 16];
+#pragma unroll
+                for (int dd = 0; dd < D / 16; ++dd) {
+                    float x = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < kAWaves; ++v) x += s_o[v][r][d0 + dd];
+                    acc[dd] = x;
+                }
+                const int row = rg * 32 + n * 16 + r;
+                if (whole) {
+                    if (row < a.rows) {
+                        const int i = row / a.G;
+                        const int h = g * a.G + row % a.G;
+                        uint16_t* op = a.out + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + d0;
+                        const float inv = 1.0f / lsum;
+#pragma unroll
+                        for (int dd = 0; dd < D / 16; ++dd) op[dd] = f32_to_bf16_bits(acc[dd] * inv);
+                    }
+                } else {
+                    const size_t prow = slot * 32 + n * 16 + r;
+                    float* po = a.part_o + prow * D + d0;
+#pragma unroll
+                    for (int dd = 0; dd < D / 16; ++dd) po[dd] = acc[dd];
+                    if ((tid % 16) == 0) {
+                        a.part_ml[prow * 2 + 0] = Mr;
+                        a.part_ml[prow * 2 + 1] = lsum;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        cur += it1 - it0;
+        first_piece = false;
+        it0 = 0;
+        if (++u == a.U) {
+            u = 0;
+            if (++b >= a.B) break;
+            iters_b = prefix[b + 1] - prefix[b];
+        }
     }
 }
 
-// Merge the split partials of one (sequence, KV head, row group) in split order.
+// Combine the pieces of every (sequence, KV head, row group) segment that was
+// split between workgroups, in workgroup order.
 template <int D>
 __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) {
-    const int g = blockIdx.x / a.row_groups, rg = blockIdx.x % a.row_groups;
-    const int b = blockIdx.y;
-    const int N = a.seq_lens[b] + a.k + 1;
-    const int ns = min(a.splits, (N + a.chunk - 1) / a.chunk);
-    if (ns <= 1) return;
+    const int u = blockIdx.x, b = blockIdx.y;
+    const long long total = static_cast<long long>(a.U) * a.prefix[a.B];
+    const int iters_b = a.prefix[b + 1] - a.prefix[b];
+    if (iters_b <= 0) return;
+    const long long S = static_cast<long long>(a.U) * a.prefix[b] + static_cast<long long>(u) * iters_b;
+    const long long E = S + iters_b;
+    const int w0 = range_owner(S, total, a.P), w1 = range_owner(E - 1, total, a.P);
+    if (w0 == w1) return;                      // one workgroup wrote the output directly
+    const int first_slot = (S == range_start(w0, total, a.P)) ? 0 : 1;
+    const int g = u / a.row_groups, rg = u % a.row_groups;
     const int tid = threadIdx.x;
-    const size_t unit = (size_t(b) * a.Hkv + g) * a.row_groups + rg;
     for (int n = 0; n < tiles; ++n) {
         const int r = tid / 16;
         const int d0 = (tid % 16) * (D / 16);
         const int row = rg * 32 + n * 16 + r;
         if (row >= a.rows) continue;
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((unit * a.splits + s) * 32 + n * 16 + r) * 2]);
+        for (int ww = w0; ww <= w1; ++ww) {
+            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * 32 + n * 16 + r;
+            M = fmaxf(M, a.part_ml[prow * 2]);
+        }
         float lsum = 0.0f;
         float acc[D / 16];
 #pragma unroll
         for (int dd = 0; dd < D / 16; ++dd) acc[dd] = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-            const size_t slot = (unit * a.splits + s) * 32 + n * 16 + r;
-            const float ms = a.part_ml[slot * 2];
-            const float w = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-            lsum += w * a.part_ml[slot * 2 + 1];
-            const float* po = a.part_o + slot * D + d0;
+        for (int ww = w0; ww <= w1; ++ww) {
+            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * 32 + n * 16 + r;
+            const float ms = a.part_ml[prow * 2];
+            const float wt = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+            lsum += wt * a.part_ml[prow * 2 + 1];
+            const float* po = a.part_o + prow * D + d0;
 #pragma unroll
-            for (int dd = 0; dd < D / 16; ++dd) acc[dd] += w * po[dd];
+            for (int dd = 0; dd < D / 16; ++dd) acc[dd] += wt * po[dd];
         }
         const int i = row / a.G;
         const int h = g * a.G + row % a.G;
@@ -330,11 +426,32 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
     }
 }
 
-int floor_pow2(long long x) {
-    int p = 1;
-    while (2LL * p <= x) p *= 2;
-    return p;
+// Persistent-grid size per (device, kernel instantiation): CUs x resident workgroups.
+int g_grid_memo[64][4];
+
+template <int D, int NT>
+int persistent_grid(int slot) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int& memo = g_grid_memo[dev][slot];
+    if (memo > 0) return memo;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_streamk_kernel<D, NT>, kAT, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int P = cus * (per_cu > 0 ? per_cu : 1);
+    if (P > kMaxP) P = kMaxP;
+    if (P < 1) P = 1;
+    memo = P;
+    return P;
 }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
@@ -344,18 +461,11 @@ AttnGeometry attn_geometry(int B, int k, int Hq, int Hkv, int D, int max_seq_len
     g.rows = (k + 1) * G;
     g.tiles = g.rows <= 16 ? 1 : 2;
     g.row_groups = (g.rows + 31) / 32;
-    // Aim for ~4096 workgroups at the longest context, with at most 64 splits per
-    // sequence (bounds the merge), chunks a power of two in [256, kMaxChunk].
-    const long long units = static_cast<long long>(B) * Hkv * g.row_groups;
-    long long target = static_cast<long long>(max_seq_len) * units / 4096;
-    int chunk = floor_pow2(target < 256 ? 256 : target);
-    while (chunk < kMaxChunk && (max_seq_len + chunk - 1) / chunk > 64) chunk *= 2;
-    if (chunk > kMaxChunk) chunk = kMaxChunk;
-    if (chunk < 256) chunk = 256;
-    g.chunk = chunk;
-    g.splits = (max_seq_len + chunk - 1) / chunk;
-    // a single split never writes partials
-    g.workspace = g.splits > 1 ? units * size_t(g.splits) * 32 * (size_t(D) + 2) * sizeof(float) : 0;
+    g.chunk = kIterKeys;
+    g.splits = (max_seq_len + kIterKeys - 1) / kIterKeys;
+    const size_t prefix_bytes = align256(sizeof(int32_t) * (size_t(B) + 1));
+    const size_t part = size_t(kMaxP) * 2 * 32;
+    g.workspace = prefix_bytes + part * size_t(D) * sizeof(float) + part * 2 * sizeof(float);
     return g;
 }
 
@@ -367,34 +477,50 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     a.bt = p.block_table;
     a.seq_lens = p.seq_lens;
     a.out = static_cast<uint16_t*>(p.out);
-    const size_t units = size_t(p.B) * p.Hkv * geo.row_groups;
-    a.part_o = static_cast<float*>(p.workspace);
-    a.part_ml = a.part_o + units * geo.splits * 32 * size_t(p.D);
+    char* ws = static_cast<char*>(p.workspace);
+    a.prefix = reinterpret_cast<int32_t*>(ws);
+    a.part_o = reinterpret_cast<float*>(ws + align256(sizeof(int32_t) * (size_t(p.B) + 1)));
+    a.part_ml = a.part_o + size_t(kMaxP) * 2 * 32 * p.D;
+    a.B = p.B;
     a.k = p.k;
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
     a.G = p.Hq / p.Hkv;
     a.rows = geo.rows;
     a.row_groups = geo.row_groups;
+    a.U = p.Hkv * geo.row_groups;
     a.max_blocks = p.max_blocks;
     int lg = 0;
     while ((1 << lg) < p.block_size) ++lg;
     a.bs_log2 = lg;
-    a.chunk = geo.chunk;
-    a.splits = geo.splits;
     a.scale_log2 = p.sm_scale * kLog2e;
 
-    const dim3 grid(geo.splits, p.Hkv * geo.row_groups, p.B), block(kAT);
+    if (p.B > kLdsPrefix) {
+        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAT), 0, stream, p.seq_lens, p.B, p.k, a.prefix);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 block(kAT);
     if (p.D == 128) {
-        if (geo.tiles == 1) hipLaunchKernelGGL((attn_partial_kernel<128, 1>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_partial_kernel<128, 2>), grid, block, 0, stream, a);
+        if (geo.tiles == 1) {
+            a.P = persistent_grid<128, 1>(0);
+            hipLaunchKernelGGL((attn_streamk_kernel<128, 1>), dim3(a.P), block, 0, stream, a);
+        } else {
+            a.P = persistent_grid<128, 2>(1);
+            hipLaunchKernelGGL((attn_streamk_kernel<128, 2>), dim3(a.P), block, 0, stream, a);
+        }
     } else {
-        if (geo.tiles == 1) hipLaunchKernelGGL((attn_partial_kernel<64, 1>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_partial_kernel<64, 2>), grid, block, 0, stream, a);
+        if (geo.tiles == 1) {
+            a.P = persistent_grid<64, 1>(2);
+            hipLaunchKernelGGL((attn_streamk_kernel<64, 1>), dim3(a.P), block, 0, stream, a);
+        } else {
+            a.P = persistent_grid<64, 2>(3);
+            hipLaunchKernelGGL((attn_streamk_kernel<64, 2>), dim3(a.P), block, 0, stream, a);
+        }
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || geo.splits <= 1) return e;
-    const dim3 mgrid(p.Hkv * geo.row_groups, p.B);
+    if (e != hipSuccess) return e;
+    const dim3 mgrid(a.U, p.B);
     if (p.D == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, block, 0, stream, a, geo.tiles);
     else hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, block, 0, stream, a, geo.tiles);
     return hipGetLastError();

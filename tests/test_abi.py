@@ -95,8 +95,10 @@ def test_workspace_sizes(lib):
     assert lib.spec_reject_sample_workspace_size(0, 3, 100, ctypes.byref(n)) == 2
     assert lib.spec_verify_attn_workspace_size(64, 3, 32, 8, 128, 8196, ctypes.byref(n)) == 0
     assert n.value > 0
+    small = n.value
     assert lib.spec_verify_attn_workspace_size(1, 3, 4, 2, 64, 100, ctypes.byref(n)) == 0
-    assert n.value == 0                   # one split: no partials
+    assert 0 < n.value < small            # work prefix + partial slots of the persistent grid
+    assert lib.spec_verify_attn_workspace_size(65535, 3, 4, 2, 64, 1 << 30, ctypes.byref(n)) == 2
     assert lib.spec_verify_attn_workspace_size(1, 3, 4, 2, 64, 100, None) == 1
 
 

@@ -79,6 +79,25 @@ def test_split_boundaries(device):
     _assert_close(run_attention(inp, device, max_seq_len=65536), _full_oracle(inp), "split-edges/msl")
 
 
+def test_many_tiny_sequences_split_everywhere(device):
+    """Hundreds of short sequences: work shares start and end inside segments everywhere."""
+    p = _preset(B=700, Hq=8, Hkv=2, D=64, k=3, ctx=("uniform", 0, 300))
+    inp = make_attention_inputs(p, seed=21)
+    _assert_close(run_attention(inp, device), _full_oracle(inp), "B700 tiny contexts")
+
+
+def test_batch_above_lds_prefix_limit(device):
+    """B = 5000 takes the separate planning launch for the per-sequence work prefix."""
+    p = _preset(B=5000, Hq=4, Hkv=1, D=64, k=1, ctx=("uniform", 0, 60))
+    inp = make_attention_inputs(p, seed=22)
+    got = run_attention(inp, device)
+    want = oatt.verify_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"],
+                                 inp["k"], inp["Hq"], inp["Hkv"], inp["block_size"], inp["sm_scale"],
+                                 pairs=[(b, 0) for b in range(0, 5000, 7)])
+    rows = list(range(0, 5000, 7))
+    _assert_close(got[rows], want[rows], "B5000")
+
+
 def _sampled_rows(inp, got, n_rows, seed, label):
     rng = np.random.default_rng(seed)
     B, Hq, k = inp["B"], inp["Hq"], inp["k"]
