@@ -20,9 +20,10 @@
  *    not checked.
  *  - Workspaces are caller-allocated device memory of at least the size the
  *    matching *_workspace_size call reports, ZERO-FILLED ONCE after allocation.
- *    Every call leaves the synchronisation counters inside a workspace at zero
- *    again, so a workspace is reused across calls without clearing; two calls
- *    in flight at the same time must not share one.
+ *    Every call leaves a workspace ready for the next one (the reject
+ *    workspace carries a call counter that tags its exchange slots), so a
+ *    workspace is reused across calls without clearing; two calls in flight
+ *    at the same time must not share one.
  *  - No C++ exception crosses this interface.
  *
  * Sources for what is computed (page titles; the pages print no API):
@@ -130,8 +131,14 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
  *  out_probs     fp32 [B][k+1] or NULL: p_i(out_tokens[b][i]) for i <= a_b, 0 after
  *  accept_probs  fp32 [B][k]   or NULL: min(1, p_j/q_j) at d_j for tested j, -1 for untested
  *
- * Shapes: B >= 1; 1 <= k <= 15; V >= 2; temperature finite and > 0.
- * Rows after a sequence's first rejection are not read.
+ * Shapes: 1 <= B <= 65535; 1 <= k <= 15; 2 <= V <= 1048576; temperature finite
+ * and > 0. Logits are finite (padding of -inf is allowed; NaN is not).
+ * Rows after a sequence's first rejection are not read, and no row is read twice.
+ * The wavefronts of one sequence exchange partial sums while running, so the
+ * grid is sized to what the device holds at once (SPEC_ERR_HIP if it cannot
+ * hold one sequence's ceil(V / 4096) wavefronts). Every wait is bounded: should
+ * residency ever be partial (other streams filling the device) and a wait time
+ * out, the affected sequence reports num_accepted = -1.
  * Workspace: spec_reject_sample_workspace_size(B, k, V).
  * ---------------------------------------------------------------------- */
 spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out);

@@ -93,7 +93,7 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
-# Per-device workspaces, zero-filled once; the library leaves its counters at zero.
+# Per-device workspaces, zero-filled once; every call leaves them ready for the next.
 _workspaces: dict = {}
 
 

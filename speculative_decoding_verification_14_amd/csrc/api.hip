@@ -110,7 +110,7 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
 
 spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out) {
     if (!bytes_out) return SPEC_ERR_NULL_POINTER;
-    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2) return SPEC_ERR_BAD_SHAPE;
+    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
     *bytes_out = reject_workspace_bytes(B, k, V);
     return SPEC_OK;
 }
@@ -125,7 +125,7 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
     if (!target_logits || !draft_logits || !draft_tokens || !seq_ids || !seq_lens || !out_tokens ||
         !num_accepted || !workspace)
         return SPEC_ERR_NULL_POINTER;
-    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2) return SPEC_ERR_BAD_SHAPE;
+    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
     if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
     if (workspace_bytes < reject_workspace_bytes(B, k, V)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
     spec_status s = check_device();

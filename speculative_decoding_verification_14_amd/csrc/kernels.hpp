@@ -48,6 +48,7 @@ struct RejectLaunch {
 };
 
 size_t reject_workspace_bytes(int B, int k, int V);
+int reject_max_vocab();   // largest V the reject kernel accepts
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream);
 
 hipError_t launch_commit(int32_t* seq_lens, const int32_t* num_accepted, int B, int capacity,

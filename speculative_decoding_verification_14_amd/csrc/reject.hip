@@ -9,54 +9,54 @@
 // u_acc < p_j(d_j)/q_j(d_j); at the first rejection sample max(0, p_j - q_j);
 // after full acceptance sample p_k. Sampling is inverse CDF in ascending token id.
 //
-// How (one MI355X):
-//  * The vocab of a row is cut into slices of kSlice = 4096 logits. Every launch
-//    is a grid of (W slices) x (B sequences) workgroups of 256 threads, so even
-//    B = 64 puts 2048 workgroups on the 256 CUs; a thread holds 16 logits per row
-//    in registers, fetched by 16-byte loads that are all in flight together.
-//  * Launch j = 0..k. Workgroups never talk to each other inside a launch: the
-//    kernel boundary is the only synchronisation (no atomics, no cache flushes).
-//    Launch j first re-derives decision j-1 of its sequence from the slice
-//    partials launch j-1 stored (a fixed-order combine, so every workgroup of the
-//    sequence reaches the same decision), then does one of:
-//      - accepted, j < k: max and sum of exps of its slice of rows p_j and q_j;
-//      - rejected at j-1: fp64 sub-chunk sums of max(0, p - q) of its slice;
-//      - accepted, j = k: sub-chunk sums of exps of its slice of the bonus row.
-//    Sequences that left the chain return at once, so rows after a sequence's
-//    first rejection are never read.
-//  * A final launch, one wavefront per sequence, finds the sub-chunk (256 logits)
-//    where the running sum crosses u_smp * total, rescans that sub-chunk with a
-//    wavefront prefix scan, and writes the sample and the padding.
-//  * Precision: exps of logits within kTheta nats of a slice maximum are taken
-//    in fp64, all others in fp32, and every sum is accumulated in fp64, so the
-//    normalisers and the CDF match an fp64 reference to ~1e-10 of their mass.
+// How (one MI355X, one launch for the whole batch):
+//  * A row of V logits is cut into units of 4096; unit u of every row of a
+//    sequence belongs to one wavefront, which holds it in registers (16 x 16-byte
+//    loads per lane per row, all in flight together). The U = ceil(V / 4096)
+//    wavefronts of a sequence form a group; groups take sequences in turn.
+//  * Level j: the group loads its units of p_j and q_j, each wavefront reduces
+//    its unit to (max, sum of exps) with an online softmax on the DPP network,
+//    publishes the pair and waits for the other U - 1. Every wavefront then
+//    combines the U pairs in the same fixed order, so all of them take the same
+//    acceptance decision without further communication.
+//  * Exchange is fence-free: each published 32-bit value travels in a 64-bit
+//    atomic slot together with the call's epoch, so a slot is either stale (old
+//    epoch, keep polling) or complete. No cache write-back or invalidation is
+//    needed and the workspace never has to be cleared between calls.
+//  * On the first rejection (or after k acceptances, on row p_k) the rows still
+//    in registers are turned into sampling weights: nothing is read twice. The
+//    group exchanges per-unit sums, every wavefront finds the unit where the
+//    running sum crosses u_smp * total, and the wavefront owning that unit scans
+//    its registers for the token.
+//  * Precision: the chain statistics use fp32 exps (relative error ~1e-7, ample
+//    for an acceptance test). The sampling pass takes logits whose probability
+//    exceeds 2^-14 in fp64 and the rest with an error-compensated fp32 exp,
+//    accumulating in fp64, so the sampling CDF is within ~1e-9 of an fp64 one.
+//  * Co-residency of a group is required: the grid is sized to what the device
+//    holds at once, and every wait is bounded so that a wavefront always
+//    terminates (a timed-out sequence reports num_accepted = -1).
 #include "common.hpp"
+#include "fastexp.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
 
 namespace specverify {
 namespace {
 
-constexpr int kRT = 256;                     // threads per workgroup
-constexpr int kWavesRT = kRT / kWave;        // 4
-constexpr int kEPT = 16;                     // logits per thread per row
-constexpr int kSlice = kRT * kEPT;           // 4096 logits per slice
-constexpr int kSub = 4 * kWave;              // 256 logits: one wave's 16-byte load
-constexpr int kSubPerSlice = kSlice / kSub;  // 16
-constexpr float kTheta = 8.0f;
+constexpr int kVecs = 16;                  // 16-byte loads per lane per row
+constexpr int kUnit = kWave * kVecs * 4;   // 4096 logits: one wavefront's share of a row
+constexpr int kStep = 4;                   // loads per online-softmax step (16 logits per lane)
+constexpr int kStatSlots = 6;              // M_p, M_q, Z_p (hi, lo), Z_q (hi, lo)
+constexpr int kSampSlots = 8;              // A, B, P, Q (hi, lo each)
+constexpr int kStatRes = 8;                // decision flags, M_p, M_q, Z_p (hi, lo), Z_q (hi, lo), unused
+constexpr int kSampRes = 16;               // flags | crossing unit, run, t, Z_p, Z_q (hi, lo each), unused
+constexpr int kMaxUnitsPerLane = 4;        // U <= 256, i.e. V <= 2^20
+constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this probability share use fp64
+constexpr unsigned kSpinLimit = 1u << 20;
 
-enum : int { kModeResidual = 0, kModeBonus = 1 };
+enum : unsigned { kCtlEpoch = 0, kCtlDone = 1, kCtlError = 2 };
 
-struct FinalRecord {       // written once per sequence, when its chain ends
-    int mode;
-    int a;
-    int pad0, pad1;
-    double Mp, Zp, Mq, Zq; // residual mode: normalisers of the rejected pair
-};
-
-constexpr int kChainPart = 4;                          // m_p, Z_p, m_q, Z_q
-constexpr int kSamplePart = 2 + 2 * kSubPerSlice + 2;  // m_w, R_w, S_r[16], P_w, S_p[16], pad
-constexpr int kOffR = 1, kOffSr = 2, kOffP = 2 + kSubPerSlice, kOffSp = 3 + kSubPerSlice;
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct RejectArgs {
     const float* target;
@@ -68,12 +68,14 @@ struct RejectArgs {
     int32_t* num_accepted;
     float* out_probs;
     float* accept_probs;
-    int32_t* active;       // [2][B], parity-double-buffered by launch index
-    FinalRecord* final_rec;
-    double* chain_part;    // [B][k][W][kChainPart]
-    double* sample_part;   // [B][W][kSamplePart]
-    int B, k, V, W;
-    float invT;
+    unsigned* ctl;                     // epoch of the last finished call, finished-wave count, error flag
+    unsigned long long* stat_slots;    // [B][k+1][U][kStatSlots]
+    unsigned long long* samp_slots;    // [B][U][kSampSlots]
+    unsigned long long* stat_res;      // [B][k+1][kStatRes]: unit 0's combined statistics and decision
+    unsigned long long* samp_res;      // [B][kSampRes]: unit 0's unit-level search result
+    int B, k, V, U, groups;
+    float invT;                        // 1 / T
+    float c2;                          // log2(e) / T
     double invT64;
     uint64_t seed;
 };
@@ -81,534 +83,814 @@ struct RejectArgs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RejectLayout {
-    size_t active, final_rec, chain_part, sample_part, total;
+    size_t ctl, stat, samp, stat_res, samp_res, total;
 };
 
-RejectLayout reject_layout(int B, int k, int W) {
+RejectLayout reject_layout(int B, int k, int U) {
     RejectLayout L;
     size_t o = 0;
-    L.active = o;      o = align256(o + sizeof(int32_t) * 2 * size_t(B));
-    L.final_rec = o;   o = align256(o + sizeof(FinalRecord) * size_t(B));
-    L.chain_part = o;  o = align256(o + sizeof(double) * size_t(B) * k * W * kChainPart);
-    L.sample_part = o; o = align256(o + sizeof(double) * size_t(B) * W * kSamplePart);
+    L.ctl = o;  o = align256(o + 4 * sizeof(unsigned));
+    L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * U * kStatSlots);
+    L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * kSampSlots);
+    L.stat_res = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * kStatRes);
+    L.samp_res = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * kSampRes);
     L.total = o;
     return L;
 }
 
-// Slice element e of this thread: e = i*1024 + tid*4 + c (i, c in 0..3), so each
-// (i, wave) pair is a contiguous run of 256 logits: the sub-chunk i*4 + wave.
-// Loads are unconditional (clamped addresses) so all of them are in flight together.
-template <bool kVec4>
-__device__ __forceinline__ void load_slice(const float* row, int V, int w, float (&v)[kEPT]) {
-    const int tid = threadIdx.x;
-    if (kVec4) {
-        float4 f[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int x0 = w * kSlice + i * (kRT * 4) + tid * 4;
-            f[i] = *reinterpret_cast<const float4*>(row + min(x0, V - 4));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = w * kSlice + i * (kRT * 4) + tid * 4 < V;
-            v[4 * i + 0] = ok ? f[i].x : -INFINITY;
-            v[4 * i + 1] = ok ? f[i].y : -INFINITY;
-            v[4 * i + 2] = ok ? f[i].z : -INFINITY;
-            v[4 * i + 3] = ok ? f[i].w : -INFINITY;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int x = w * kSlice + i * (kRT * 4) + tid * 4 + c;
-                const float val = row[min(x, V - 1)];
-                v[4 * i + c] = (x < V) ? val : -INFINITY;
-            }
-    }
+// ---------------------------------------------------------------- slots
+
+__device__ __forceinline__ void slot_store(unsigned long long* p, unsigned payload, unsigned epoch) {
+    const unsigned long long v = (static_cast<unsigned long long>(payload) << 32) | epoch;
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool kVec4>
-__device__ __forceinline__ void load_sub(const float* row, int V, int x0, float (&v)[4]) {
-    if (kVec4) {
-        const float4 f = *reinterpret_cast<const float4*>(row + min(x0, V - 4));
-        const bool ok = x0 < V;
-        v[0] = ok ? f.x : -INFINITY; v[1] = ok ? f.y : -INFINITY;
-        v[2] = ok ? f.z : -INFINITY; v[3] = ok ? f.w : -INFINITY;
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float val = row[min(x0 + c, V - 1)];
-            v[c] = (x0 + c < V) ? val : -INFINITY;
-        }
-    }
+__device__ __forceinline__ unsigned long long slot_load(unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// e^{(z - m)/T} in fp64 for one logit.
-__device__ __forceinline__ double exp_f64(float z, double m, double invT64) {
-    return exp((static_cast<double>(z) - m) * invT64);
+__device__ __forceinline__ unsigned hi32(double d) {
+    return static_cast<unsigned>(__builtin_bit_cast(unsigned long long, d) >> 32);
+}
+__device__ __forceinline__ unsigned lo32(double d) {
+    return static_cast<unsigned>(__builtin_bit_cast(unsigned long long, d));
+}
+__device__ __forceinline__ double join64(unsigned hi, unsigned lo) {
+    return __builtin_bit_cast(double, (static_cast<unsigned long long>(hi) << 32) | lo);
 }
 
-// e^{(z - m)/T} for N logits: fp32 for terms more than kTheta nats below m, fp64
-// otherwise. The fp64 terms are visited by a per-lane loop over a bitmask, so a
-// wave pays for max-over-lanes of its flagged count, not for every slot.
+// Lane 0 publishes the N payloads (N back-to-back single-lane stores).
 template <int N>
-__device__ __forceinline__ void exps_mixed(const float (&z)[N], float m, float invT, double invT64,
-                                           double (&out)[N]) {
-    unsigned flags = 0;
+__device__ __forceinline__ void publish(unsigned long long* slots, const unsigned (&payload)[N], unsigned epoch) {
+    if (lane_id() == 0) {
 #pragma unroll
-    for (int e = 0; e < N; ++e) {
-        const float x = (z[e] - m) * invT;
-        const bool near = x > -kTheta;
-        flags |= static_cast<unsigned>(near) << e;
-        out[e] = near ? 0.0 : static_cast<double>(expf(x));
-    }
-    const double m64 = static_cast<double>(m);
-    while (flags) {
-        const int e = __builtin_ctz(flags);
-        flags &= flags - 1;
-        float ze = 0.0f;
-#pragma unroll
-        for (int s = 0; s < N; ++s) ze = (s == e) ? z[s] : ze;
-        const double val = exp_f64(ze, m64, invT64);
-#pragma unroll
-        for (int s = 0; s < N; ++s) out[s] = (s == e) ? val : out[s];
+        for (int s = 0; s < N; ++s) slot_store(slots + s, payload[s], epoch);
     }
 }
 
-template <int N>
-__device__ __forceinline__ double sum_exps_mixed(const float (&z)[N], float m, float invT, double invT64) {
-    unsigned flags = 0;
-    float tail = 0.0f;
+// Waits until the N slots of every unit carry `epoch` and returns their payloads:
+// lane l gets units l, l + 64, ... (kUPL of them; units >= U read as zero).
+// Returns false if the bounded wait ran out (only possible if the group were not
+// co-resident, which the cooperative launch rules out).
+template <int N, int kUPL>
+__device__ __forceinline__ bool gather(unsigned long long* slots, int U, unsigned epoch, unsigned (&out)[kUPL][N]) {
+    const int lane = lane_id();
+    for (unsigned it = 0; it < kSpinLimit; ++it) {
+        bool ok = true;
 #pragma unroll
-    for (int e = 0; e < N; ++e) {
-        const float x = (z[e] - m) * invT;
-        const bool near = x > -kTheta;
-        flags |= static_cast<unsigned>(near) << e;
-        tail += near ? 0.0f : expf(x);
-    }
-    double acc = static_cast<double>(tail);
-    const double m64 = static_cast<double>(m);
-    while (flags) {
-        const int e = __builtin_ctz(flags);
-        flags &= flags - 1;
-        float ze = 0.0f;
+        for (int r = 0; r < kUPL; ++r) {
+            const int u = lane + r * kWave;
 #pragma unroll
-        for (int s = 0; s < N; ++s) ze = (s == e) ? z[s] : ze;
-        acc += exp_f64(ze, m64, invT64);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-    v = wave_max(v);
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < kWavesRT; ++i) r = fmaxf(r, red[i]);
-    return r;
-}
-
-__device__ __forceinline__ double block_sum(double v, double* red) {
-    v = wave_sum(v);
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    double r = red[0];
-#pragma unroll
-    for (int i = 1; i < kWavesRT; ++i) r += red[i];
-    return r;
-}
-
-// Inclusive prefix sum across the wavefront (Hillis-Steele, fixed order).
-__device__ __forceinline__ double wave_incl_scan(double v) {
-    const int lane = threadIdx.x % kWave;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(v, o, kWave);
-        if (lane >= o) v += y;
-    }
-    return v;
-}
-
-__device__ __forceinline__ double wave_excl_from_incl(double incl) {
-    const double e = __shfl_up(incl, 1, kWave);
-    return (threadIdx.x % kWave) == 0 ? 0.0 : e;
-}
-
-// Combine W slice partials (max m_w, sum of exps Z_w relative to m_w) into the row's
-// (M, Z) inside one wavefront: lanes take slices, butterflies reduce in a fixed order.
-__device__ void combine_row(const double* part, int stride, int offset, int W, double invT64,
-                            double* M_out, double* Z_out) {
-    const int lane = threadIdx.x % kWave;
-    double m = -INFINITY;
-    for (int w = lane; w < W; w += kWave) m = fmax(m, part[size_t(w) * stride + offset]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, kWave));
-    double z = 0.0;
-    for (int w = lane; w < W; w += kWave) {
-        const double mw = part[size_t(w) * stride + offset];
-        const double zw = part[size_t(w) * stride + offset + 1];
-        z += (zw > 0.0) ? zw * exp((mw - m) * invT64) : 0.0;
-    }
-    *M_out = m;
-    *Z_out = wave_sum(z);
-}
-
-// Sampling weights of a residual: max(0, p - q), also returning e^{(z_p - M_p)/T}
-// (the weights of the p-fallback).
-struct ResidualCtx {
-    float mp, mq;            // row maxima (exactly representable logits)
-    double invZp, invZq;
-};
-
-template <int N>
-__device__ __forceinline__ void residual_weights(const float (&zp)[N], const float (&zq)[N], const ResidualCtx& c,
-                                                 float invT, double invT64, double (&r)[N], double (&ep)[N]) {
-    double eq[N];
-    exps_mixed(zp, c.mp, invT, invT64, ep);
-    exps_mixed(zq, c.mq, invT, invT64, eq);
-#pragma unroll
-    for (int e = 0; e < N; ++e) r[e] = fmax(0.0, ep[e] * c.invZp - eq[e] * c.invZq);
-}
-
-struct Decision {
-    int accepted;
-    double Mp, Zp, Mq, Zq;
-};
-
-// Decision j of sequence b from the slice partials of launch j (one wavefront);
-// lane 0 also writes the outputs of that decision when `write` is set.
-__device__ Decision decide(const RejectArgs& a, int b, int j, bool write) {
-    const double* part = a.chain_part + (size_t(b) * a.k + j) * a.W * kChainPart;
-    Decision d;
-    combine_row(part, kChainPart, 0, a.W, a.invT64, &d.Mp, &d.Zp);
-    combine_row(part, kChainPart, 2, a.W, a.invT64, &d.Mq, &d.Zq);
-    const float* prow = a.target + (size_t(b) * (a.k + 1) + j) * a.V;
-    const float* qrow = a.draft + (size_t(b) * a.k + j) * a.V;
-    const int tok = a.draft_tokens[size_t(b) * a.k + j];
-    const bool ok = tok >= 0 && tok < a.V;   // out-of-range ids (a broken precondition) are rejected
-    const double p_d = ok ? exp((static_cast<double>(prow[ok ? tok : 0]) - d.Mp) * a.invT64) / d.Zp : 0.0;
-    const double q_d = ok ? exp((static_cast<double>(qrow[ok ? tok : 0]) - d.Mq) * a.invT64) / d.Zq : 0.0;
-    const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
-    double u_acc, u_smp;
-    verify_uniforms(a.seed, a.seq_ids[b], int64_t(a.seq_lens[b]) + 1 + j, &u_acc, &u_smp);
-    d.accepted = u_acc < ratio;
-    if (write && (threadIdx.x % kWave) == 0) {
-        if (a.accept_probs) a.accept_probs[size_t(b) * a.k + j] = static_cast<float>(fmin(1.0, ratio));
-        if (d.accepted) {
-            a.out_tokens[size_t(b) * (a.k + 1) + j] = tok;
-            if (a.out_probs) a.out_probs[size_t(b) * (a.k + 1) + j] = static_cast<float>(p_d);
-        }
-    }
-    return d;
-}
-
-enum : int { kWorkStats = 0, kWorkResidual = 1, kWorkBonus = 2 };
-
-template <bool kVec4>
-__global__ __launch_bounds__(kRT) void reject_level_kernel(RejectArgs a, int j) {
-    __shared__ float red_f[kWavesRT];
-    __shared__ double red_d[kWavesRT];
-    __shared__ double s_sub[2][kSubPerSlice];
-    __shared__ int s_work;
-    __shared__ double s_norm[4];
-    const int w = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    int32_t* active_in = a.active + size_t((j + 1) & 1) * a.B;
-    int32_t* active_out = a.active + size_t(j & 1) * a.B;
-    const bool leader = (w == 0);
-
-    int work = kWorkStats;
-    if (j > 0) {
-        if (active_in[b] == 0) {
-            if (leader && tid == 0) active_out[b] = 0;
-            return;
-        }
-        if (wave == 0) {
-            const Decision d = decide(a, b, j - 1, leader);
-            if (lane == 0) {
-                s_work = d.accepted ? (j < a.k ? kWorkStats : kWorkBonus) : kWorkResidual;
-                s_norm[0] = d.Mp; s_norm[1] = d.Zp; s_norm[2] = d.Mq; s_norm[3] = d.Zq;
-                if (leader) {
-                    active_out[b] = (d.accepted && j < a.k) ? 1 : 0;
-                    if (!d.accepted) {
-                        FinalRecord r;
-                        r.mode = kModeResidual; r.a = j - 1; r.pad0 = r.pad1 = 0;
-                        r.Mp = d.Mp; r.Zp = d.Zp; r.Mq = d.Mq; r.Zq = d.Zq;
-                        a.final_rec[b] = r;
-                    } else if (j == a.k) {
-                        FinalRecord r;
-                        r.mode = kModeBonus; r.a = a.k; r.pad0 = r.pad1 = 0;
-                        r.Mp = r.Zp = r.Mq = r.Zq = 0.0;
-                        a.final_rec[b] = r;
-                    }
+            for (int s = 0; s < N; ++s) {
+                unsigned long long v = 0;
+                if (u < U) {
+                    v = slot_load(slots + size_t(u) * N + s);
+                    ok = ok && static_cast<unsigned>(v) == epoch;
                 }
+                out[r][s] = static_cast<unsigned>(v >> 32);
             }
         }
-        __syncthreads();
-        work = s_work;
-    } else if (leader && tid == 0) {
-        active_out[b] = 1;
+        if (__all(ok)) return true;
+        __builtin_amdgcn_s_sleep(4);
     }
+    return false;
+}
 
-    if (work == kWorkStats) {
-        const float* prow = a.target + (size_t(b) * (a.k + 1) + j) * a.V;
-        const float* qrow = a.draft + (size_t(b) * a.k + j) * a.V;
-        float vp[kEPT], vq[kEPT];
-        load_slice<kVec4>(prow, a.V, w, vp);
-        load_slice<kVec4>(qrow, a.V, w, vq);
-        float tp = -INFINITY, tq = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e) { tp = fmaxf(tp, vp[e]); tq = fmaxf(tq, vq[e]); }
-        const float mp = block_max(tp, red_f);
-        const float mq = block_max(tq, red_f);
-        // a slice of -inf logits contributes nothing (and must not form -inf - -inf)
-        const double zp = block_sum(mp == -INFINITY ? 0.0 : sum_exps_mixed(vp, mp, a.invT, a.invT64), red_d);
-        const double zq = block_sum(mq == -INFINITY ? 0.0 : sum_exps_mixed(vq, mq, a.invT, a.invT64), red_d);
-        if (tid == 0) {
-            double* part = a.chain_part + ((size_t(b) * a.k + j) * a.W + w) * kChainPart;
-            part[0] = mp; part[1] = zp; part[2] = mq; part[3] = zq;
+// Waits until the N words of a result record carry `epoch` (lane i polls word i:
+// one cache line per poll) and returns the payloads, identical in every lane.
+template <int N>
+__device__ __forceinline__ bool await_result(unsigned long long* words, unsigned epoch, unsigned (&out)[N]) {
+    const int lane = lane_id();
+    unsigned mine = 0;
+    bool ready = false;
+    for (unsigned it = 0; it < kSpinLimit && !ready; ++it) {
+        bool ok = true;
+        if (lane < N) {
+            const unsigned long long v = slot_load(words + lane);
+            ok = static_cast<unsigned>(v) == epoch;
+            mine = static_cast<unsigned>(v >> 32);
         }
-        return;
+        ready = __all(ok);
+        if (!ready) __builtin_amdgcn_s_sleep(4);
     }
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_readlane(mine, i);
+    return ready;
+}
 
-    // Sampling work: sub-chunk sums of the weights over this slice.
-    double sr[4], sp[4];
-    double mw = 0.0;
-    if (work == kWorkResidual) {
-        const int r = j - 1;
-        const float* prow = a.target + (size_t(b) * (a.k + 1) + r) * a.V;
-        const float* qrow = a.draft + (size_t(b) * a.k + r) * a.V;
-        float vp[kEPT], vq[kEPT];
-        load_slice<kVec4>(prow, a.V, w, vp);
-        load_slice<kVec4>(qrow, a.V, w, vq);
-        ResidualCtx c;
-        c.mp = static_cast<float>(s_norm[0]);
-        c.mq = static_cast<float>(s_norm[2]);
-        c.invZp = 1.0 / s_norm[1];
-        c.invZq = 1.0 / s_norm[3];
+// Values that are equal in every lane (read by all lanes from one address, or
+// derived from wavefront reductions) made provably uniform, so that control flow
+// depending on them stays scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(v & 0xFFFFFFFFll));
+    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo));
+}
+
+// ---------------------------------------------------------------- loads
+
+// Four consecutive logits from x (x a multiple of 4 when kVec4), -inf past the
+// row. Lanes past the row issue no load (loads of one clamped address from many
+// lanes and waves serialise in the memory pipeline).
+template <bool kVec4>
+__device__ __forceinline__ f4 load4(const float* row, int V, int x) {
+    f4 f = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (kVec4) {
+        if (x < V) f = __builtin_nontemporal_load(reinterpret_cast<const f4*>(row + x));
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float zp4[4], zq4[4];
+        for (int c = 0; c < 4; ++c)
+            if (x + c < V) f[c] = __builtin_nontemporal_load(row + x + c);
+    }
+    return f;
+}
+
+// Element (i, c) of lane l in unit u is logit u*4096 + i*256 + 4*l + c: each load
+// of a wavefront is one contiguous 1 KB run. p and q loads are interleaved so the
+// online softmax can start on the first step while the rest are in flight. Only
+// the last unit of a row can reach past V; the others load without bounds tests.
+template <bool kVec4, bool kTwo>
+__device__ __forceinline__ void load_unit(const float* prow, const float* qrow, int V, int u,
+                                          f4 (&xp)[kVecs], f4 (&xq)[kVecs]) {
+    const int base = u * kUnit + lane_id() * 4;
+    if (kVec4 && (u + 1) * kUnit <= V) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { zp4[e] = vp[4 * i + e]; zq4[e] = vq[4 * i + e]; }
-            double rr[4], ep[4];
-            residual_weights(zp4, zq4, c, a.invT, a.invT64, rr, ep);
-            sr[i] = ((rr[0] + rr[1]) + rr[2]) + rr[3];
-            sp[i] = ((ep[0] + ep[1]) + ep[2]) + ep[3];
+        for (int i = 0; i < kVecs; ++i) {
+            xp[i] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(prow + base + i * (kWave * 4)));
+            if (kTwo) xq[i] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(qrow + base + i * (kWave * 4)));
         }
     } else {
-        const float* prow = a.target + (size_t(b) * (a.k + 1) + a.k) * a.V;
-        float vp[kEPT];
-        load_slice<kVec4>(prow, a.V, w, vp);
-        float t = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) t = fmaxf(t, vp[e]);
-        const float m = block_max(t, red_f);
-        mw = m;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float z4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z4[e] = vp[4 * i + e];
-            double ex[4] = {0.0, 0.0, 0.0, 0.0};
-            if (m != -INFINITY) exps_mixed(z4, m, a.invT, a.invT64, ex);
-            sr[i] = ((ex[0] + ex[1]) + ex[2]) + ex[3];
-            sp[i] = 0.0;
+        for (int i = 0; i < kVecs; ++i) {
+            xp[i] = load4<kVec4>(prow, V, base + i * (kWave * 4));
+            if (kTwo) xq[i] = load4<kVec4>(qrow, V, base + i * (kWave * 4));
         }
-    }
-    // sub-chunk (i, wave) = logits [i*1024 + wave*256, +256) of the slice
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const double r = wave_sum(sr[i]);
-        const double p = wave_sum(sp[i]);
-        if (lane == 0) { s_sub[0][i * kWavesRT + wave] = r; s_sub[1][i * kWavesRT + wave] = p; }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        double* part = a.sample_part + (size_t(b) * a.W + w) * kSamplePart;
-        double R = 0.0, P = 0.0;
-        for (int s = 0; s < kSubPerSlice; ++s) {
-            part[kOffSr + s] = s_sub[0][s];
-            part[kOffSp + s] = s_sub[1][s];
-            R += s_sub[0][s];
-            P += s_sub[1][s];
-        }
-        part[0] = mw;
-        part[kOffR] = R;
-        part[kOffP] = P;
     }
 }
 
-// One wavefront per sequence: locate and write the residual / bonus sample.
-// Slices, then sub-chunks, then logits are searched with wavefront prefix scans
-// in a fixed order; at each level the crossing is the first positive weight
-// whose running sum exceeds t = u_smp * total. If rounding leaves no crossing,
-// the last positive weight is taken (at the slice level: the largest token with
-// positive weight).
-template <bool kVec4>
-__global__ __launch_bounds__(kWave) void reject_finalize_kernel(RejectArgs a) {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    const FinalRecord rec = a.final_rec[b];
-    const int mode = rec.mode, aa = rec.a;
-    const float* prow = a.target + (size_t(b) * (a.k + 1) + aa) * a.V;
-    const float* qrow = a.draft + (size_t(b) * a.k + (aa < a.k ? aa : 0)) * a.V;
-    const double* part = a.sample_part + size_t(b) * a.W * kSamplePart;
+// ---------------------------------------------------------------- chain statistics
 
-    double M = 0.0;
-    if (mode == kModeBonus) {
-        double m = -INFINITY;
-        for (int ww = lane; ww < a.W; ww += kWave) m = fmax(m, part[size_t(ww) * kSamplePart]);
+// One online-softmax step over loads 4s..4s+3 of this lane: running max m and
+// running sum s of e^{(x - m)/T}, the exps as hardware exp2 of (x - m) * log2(e)/T.
+__device__ __forceinline__ void online_step(const f4 (&x)[kVecs], int s, float c2, float& m, double& acc) {
+    float gm = -INFINITY;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, kWave));
-        M = m;
+    for (int i = kStep * s; i < kStep * s + kStep; ++i)
+        gm = fmaxf(gm, fmaxf(fmaxf(x[i].x, x[i].y), fmaxf(x[i].z, x[i].w)));
+    const float mn = fmaxf(m, gm);
+    const float ref = (mn == -INFINITY) ? 0.0f : mn;   // all -inf so far: every term is 0
+    const float rescale = __builtin_amdgcn_exp2f((m - ref) * c2);
+    float part[kStep];
+#pragma unroll
+    for (int i = 0; i < kStep; ++i) {
+        const f4 v = x[kStep * s + i];
+        const float e0 = __builtin_amdgcn_exp2f((v.x - ref) * c2);
+        const float e1 = __builtin_amdgcn_exp2f((v.y - ref) * c2);
+        const float e2 = __builtin_amdgcn_exp2f((v.z - ref) * c2);
+        const float e3 = __builtin_amdgcn_exp2f((v.w - ref) * c2);
+        part[i] = (e0 + e1) + (e2 + e3);
     }
-    auto slice_weight = [&](int ww, int off) -> double {
-        if (ww >= a.W) return 0.0;
-        const double* pw = part + size_t(ww) * kSamplePart;
-        const double s = pw[off];
-        if (mode != kModeBonus) return s;
-        return (s > 0.0) ? s * exp((pw[0] - M) * a.invT64) : 0.0;
-    };
-    auto row_total = [&](int off) -> double {
-        double tot = 0.0;
-        for (int base = 0; base < a.W; base += kWave)
-            tot += __shfl(wave_incl_scan(slice_weight(base + lane, off)), kWave - 1, kWave);
-        return tot;
-    };
-    int use_p = 0;
-    double total = row_total(kOffR);
-    if (mode == kModeResidual && !(total > 0.0)) {   // zero residual: sample p_j instead
-        use_p = 1;
-        total = row_total(kOffP);
-    }
-    const int sum_off = use_p ? kOffP : kOffR;
-    const int sub_off = use_p ? kOffSp : kOffSr;
-    double u_acc, u_smp;
-    verify_uniforms(a.seed, a.seq_ids[b], int64_t(a.seq_lens[b]) + 1 + aa, &u_acc, &u_smp);
-    const double t = u_smp * total;
+    const float sum = (part[0] + part[1]) + (part[2] + part[3]);
+    acc = acc * static_cast<double>(rescale) + static_cast<double>(sum);
+    m = mn;
+}
 
-    // slice level
-    int ws = -1, last_pos = -1;
-    bool exact = true;
-    double run = 0.0;
-    {
-        double carry = 0.0;
-        for (int base = 0; base < a.W; base += kWave) {
-            const double s = slice_weight(base + lane, sum_off);
-            const double incl = wave_incl_scan(s);
-            const double excl = wave_excl_from_incl(incl);
-            const unsigned long long pos = __ballot(s > 0.0);
-            if (pos) last_pos = base + 63 - __builtin_clzll(pos);
-            const unsigned long long cross = __ballot(s > 0.0 && carry + incl > t);
-            if (cross) {
-                const int l0 = __ffsll(static_cast<long long>(cross)) - 1;
-                ws = base + l0;
-                run = carry + __shfl(excl, l0, kWave);
-                break;
+// (max, sum of e^{(x - max)/T}) of this wavefront's unit of one row.
+__device__ __forceinline__ void unit_reduce(float m, double acc, double invT64, float& M, double& Z) {
+    M = dpp_wave_max(m);
+    const double scaled = (acc > 0.0) ? acc * exp_nonpos_f64((static_cast<double>(m) - M) * invT64) : 0.0;
+    Z = dpp_wave_sum(scaled);
+}
+
+struct RowStats {
+    float Mp, Mq;     // row maxima (logits)
+    double Zp, Zq;    // sum of e^{(z - M)/T} over the row
+};
+
+// Combines the group's published unit statistics (identically in every wavefront).
+template <int kUPL>
+__device__ __forceinline__ RowStats combine_stats(const unsigned (&v)[kUPL][kStatSlots], int U, double invT64) {
+    float mp = -INFINITY, mq = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kUPL; ++r) {
+        if (lane_id() + r * kWave < U) {
+            mp = fmaxf(mp, __builtin_bit_cast(float, v[r][0]));
+            mq = fmaxf(mq, __builtin_bit_cast(float, v[r][1]));
+        }
+    }
+    RowStats st;
+    st.Mp = dpp_wave_max(mp);
+    st.Mq = dpp_wave_max(mq);
+    double zp = 0.0, zq = 0.0;
+#pragma unroll
+    for (int r = 0; r < kUPL; ++r) {
+        const double a = join64(v[r][2], v[r][3]);
+        const double b = join64(v[r][4], v[r][5]);
+        const double ma = __builtin_bit_cast(float, v[r][0]);
+        const double mb = __builtin_bit_cast(float, v[r][1]);
+        zp += (a > 0.0) ? a * exp_nonpos_f64((ma - st.Mp) * invT64) : 0.0;
+        zq += (b > 0.0) ? b * exp_nonpos_f64((mb - st.Mq) * invT64) : 0.0;
+    }
+    st.Zp = dpp_wave_sum(zp);
+    st.Zq = dpp_wave_sum(zq);
+    return st;
+}
+
+// ---------------------------------------------------------------- sampling weights
+
+struct SampleCtx {
+    float Mp, Mq, invT;
+    float hp, hq;        // ln(tau * Z): log-weights above these are taken in fp64
+    float dn;            // ln Z_p - ln Z_q: x in the residual support iff lp - lq > dn
+    double Mp64, Mq64, invT64;
+};
+
+// Log-weight of a logit in nats, (z - M) / T, and the residual-support test. The
+// operations are written with the no-contraction intrinsics so that every call
+// site rounds identically (the support must be the same set wherever it is judged).
+__device__ __forceinline__ float log_weight(float z, float M, float invT) { return __fmul_rn(__fsub_rn(z, M), invT); }
+__device__ __forceinline__ bool in_support(float xp, float xq, float dn) { return __fsub_rn(xp, xq) > dn; }
+
+// Light part of the unnormalised weights a = e^{(z_p - M_p)/T}, b = e^{(z_q - M_q)/T}
+// of the four logits of one load: compensated fp32 exps, zeroed (by a product, so
+// the exp is never moved into a branch) for heavy logits, whose probability under
+// the chain's normalisers exceeds tau. Their bits are set in `hmask` (bit 4*i + e)
+// and they are taken in fp64 by heavy_pass. Membership of the residual support
+// {p > q} is judged with the chain's normalisers.
+__device__ __forceinline__ void light_weights(bool residual, const f4& vp, const f4& vq, const SampleCtx& c, int i,
+                                              float (&la)[4], float (&lb)[4], bool (&in_s)[4],
+                                              unsigned long long& hmask) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float xp = log_weight(vp[e], c.Mp, c.invT);
+        const float xq = residual ? log_weight(vq[e], c.Mq, c.invT) : -INFINITY;
+        const bool h = (xp > c.hp) || (xq > c.hq);   // xq = -inf never passes
+        in_s[e] = residual ? in_support(xp, xq, c.dn) : true;   // NaN for padding: not in the support
+        const float keep = h ? 0.0f : 1.0f;
+        la[e] = exp_small_f32(xp) * keep;
+        lb[e] = residual ? exp_small_f32(xq) * keep : 0.0f;
+        hmask |= static_cast<unsigned long long>(h) << (4 * i + e);
+    }
+}
+
+// fp64 weights of this lane's heavy logits. They are re-read from memory (four
+// per lane per round trip; there are few, typically 0..4 per lane) rather than
+// picked out of the register arrays, which would need dynamic indexing and
+// force the arrays out of registers. `f` receives (load index, a, b, in support)
+// for each; the trip count is the largest per-lane count in the wavefront.
+template <bool kVec4, typename F>
+__device__ __forceinline__ void heavy_pass(bool residual, const float* prow, const float* qrow, int base,
+                                           const SampleCtx& c, unsigned long long hmask, F&& f) {
+    while (__any(hmask != 0ull)) {
+        int idx[4];
+        bool has[4];
+        float zp[4], zq[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            has[r] = hmask != 0ull;
+            idx[r] = has[r] ? __builtin_ctzll(hmask) : 0;
+            hmask &= has[r] ? hmask - 1 : hmask;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            // heavy logits are never padding (-inf), so x < V; lanes without one read logit 0
+            const int x = has[r] ? base + (idx[r] >> 2) * (kWave * 4) + (idx[r] & 3) : 0;
+            zp[r] = prow[x];
+            zq[r] = residual ? qrow[x] : -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const double va = exp_nonpos_f64((static_cast<double>(zp[r]) - c.Mp64) * c.invT64);
+            const double vb = residual ? exp_nonpos_f64((static_cast<double>(zq[r]) - c.Mq64) * c.invT64) : 0.0;
+            const bool ins = residual
+                ? in_support(log_weight(zp[r], c.Mp, c.invT), log_weight(zq[r], c.Mq, c.invT), c.dn) : true;
+            if (has[r]) f(idx[r] >> 2, va, vb, ins);
+        }
+    }
+}
+
+struct UnitSums {
+    double A, B, P, Q;   // sums over the support of a, b; sums over all logits of a, b
+};
+
+// Per-lane sums of a and b over the support for each of the lane's sixteen loads,
+// kept in LDS ([load][lane], 16 KB per wavefront) for the final scan. For the
+// bonus row only the a-sums are meaningful.
+typedef double2 LoadSums[kVecs][kWave];
+
+// Unit sums of the sampling weights and, in `ls`, the per-load sums.
+template <bool kVec4, bool kResidual>
+__device__ __forceinline__ UnitSums unit_sums(const f4 (&xp)[kVecs], const f4 (&xq)[kVecs], const SampleCtx& c,
+                                              const float* prow, const float* qrow, int base, LoadSums& ls) {
+    const int lane = lane_id();
+    double A = 0.0, Bs = 0.0, P = 0.0, Q = 0.0;
+    unsigned long long hmask = 0ull;
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+        float la[4], lb[4];
+        bool in_s[4];
+        light_weights(kResidual, xp[i], xq[i], c, i, la, lb, in_s, hmask);
+        float fa = 0.0f, fb = 0.0f, fp = 0.0f, fq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            fp += la[e];
+            fa += in_s[e] ? la[e] : 0.0f;
+            if (kResidual) {
+                fq += lb[e];
+                fb += in_s[e] ? lb[e] : 0.0f;
             }
-            carry += __shfl(incl, kWave - 1, kWave);
         }
-        if (ws < 0) { ws = last_pos < 0 ? 0 : last_pos; exact = false; }
-    }
-    const double scale = (mode == kModeBonus) ? exp((part[size_t(ws) * kSamplePart] - M) * a.invT64) : 1.0;
-    // sub-chunk level (16 sums on lanes 0..15)
-    int subc;
-    {
-        const double s = (lane < kSubPerSlice) ? part[size_t(ws) * kSamplePart + sub_off + lane] * scale : 0.0;
-        const double incl = wave_incl_scan(s);
-        const double excl = wave_excl_from_incl(incl);
-        const unsigned long long pos = __ballot(s > 0.0);
-        const unsigned long long cross = exact ? __ballot(s > 0.0 && run + incl > t) : 0ull;
-        if (cross) {
-            subc = __ffsll(static_cast<long long>(cross)) - 1;
-            run = run + __shfl(excl, subc, kWave);
-        } else {
-            subc = pos ? 63 - __builtin_clzll(pos) : 0;
-            exact = false;
+        A += static_cast<double>(fa);
+        P += static_cast<double>(fp);
+        if (kResidual) {
+            Bs += static_cast<double>(fb);
+            Q += static_cast<double>(fq);
         }
+        ls[i][lane] = make_double2(fa, fb);
     }
-    // logit level: the 256 logits of the crossing sub-chunk, 4 per lane
-    const int i_row = subc / kWavesRT, i_wave = subc % kWavesRT;
-    const int sub_base = ws * kSlice + i_row * (kRT * 4) + i_wave * kSub;
-    const int x0 = sub_base + lane * 4;
-    float zp4[4], zq4[4];
-    load_sub<kVec4>(prow, a.V, x0, zp4);
-    double wt[4];
-    if (mode == kModeResidual) {
-        load_sub<kVec4>(qrow, a.V, x0, zq4);
-        ResidualCtx c;
-        c.mp = static_cast<float>(rec.Mp);
-        c.mq = static_cast<float>(rec.Mq);
-        c.invZp = 1.0 / rec.Zp;
-        c.invZq = 1.0 / rec.Zq;
-        double r[4], ep[4];
-        residual_weights(zp4, zq4, c, a.invT, a.invT64, r, ep);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wt[e] = use_p ? ep[e] : r[e];
-    } else {
-        const float m = static_cast<float>(part[size_t(ws) * kSamplePart]);
-        exps_mixed(zp4, m, a.invT, a.invT64, wt);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wt[e] *= scale;
-    }
-    double pre[4];
-    pre[0] = wt[0];
-    pre[1] = pre[0] + wt[1];
-    pre[2] = pre[1] + wt[2];
-    pre[3] = pre[2] + wt[3];
-    const double incl = wave_incl_scan(pre[3]);
-    const double excl = wave_excl_from_incl(incl);
-    int hit = 4, lastc = -1;
-#pragma unroll
-    for (int e = 3; e >= 0; --e)
-        if (exact && wt[e] > 0.0 && (run + excl) + pre[e] > t) hit = e;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) if (wt[e] > 0.0) lastc = e;
-    const unsigned long long mhit = __ballot(hit < 4);
-    int y;
-    if (mhit) {
-        const int l0 = __ffsll(static_cast<long long>(mhit)) - 1;
-        y = sub_base + l0 * 4 + __shfl(hit, l0, kWave);
-    } else {
-        const unsigned long long mpos = __ballot(lastc >= 0);
-        const int l1 = mpos ? (63 - __builtin_clzll(mpos)) : 0;
-        const int c1 = __shfl(lastc, l1, kWave);
-        y = sub_base + l1 * 4 + (c1 < 0 ? 0 : c1);
-    }
-    if (lane != 0) return;
-    if (y >= a.V) y = a.V - 1;   // only reachable when every weight is zero
+    heavy_pass<kVec4>(kResidual, prow, qrow, base, c, hmask, [&](int i, double va, double vb, bool ins) {
+        P += va;
+        A += ins ? va : 0.0;
+        double2 g = ls[i][lane];
+        g.x += ins ? va : 0.0;
+        if (kResidual) {
+            Q += vb;
+            Bs += ins ? vb : 0.0;
+            g.y += ins ? vb : 0.0;
+        }
+        ls[i][lane] = g;
+    });
+    UnitSums s;
+    s.A = dpp_wave_sum(A);
+    s.P = dpp_wave_sum(P);
+    s.B = kResidual ? dpp_wave_sum(Bs) : 0.0;
+    s.Q = kResidual ? dpp_wave_sum(Q) : 0.0;
+    return s;
+}
 
-    double py;
-    if (mode == kModeBonus) py = exp((static_cast<double>(prow[y]) - M) * a.invT64) / total;
-    else py = exp((static_cast<double>(prow[y]) - rec.Mp) * a.invT64) / rec.Zp;
-    const size_t ob = size_t(b) * (a.k + 1);
-    a.out_tokens[ob + aa] = y;
-    if (a.out_probs) a.out_probs[ob + aa] = static_cast<float>(py);
-    for (int i = aa + 1; i <= a.k; ++i) {
+// Sampling weight of one logit from its unnormalised a, b: the residual
+// max(0, a/Z_p - b/Z_q) on the support, else a itself (p_j, or the bonus row).
+__device__ __forceinline__ double sample_weight(bool residual, bool in_s, double a, double b, double invZp,
+                                                double invZq) {
+    if (!residual) return a;
+    return in_s ? fmax(0.0, a * invZp - b * invZq) : 0.0;
+}
+
+// Weights of the four logits of one load, fp64 for the heavy ones.
+__device__ __forceinline__ void load_weights(bool two_rows, bool residual, const f4& vp, const f4& vq,
+                                             const SampleCtx& c, double invZp, double invZq, double (&w)[4]) {
+    float la[4], lb[4];
+    bool in_s[4];
+    unsigned long long hm = 0ull;
+    light_weights(two_rows, vp, vq, c, 0, la, lb, in_s, hm);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool heavy = (hm >> e) & 1ull;
+        const double va = heavy ? exp_nonpos_f64((static_cast<double>(vp[e]) - c.Mp64) * c.invT64) : la[e];
+        const double vb = (heavy && two_rows) ? exp_nonpos_f64((static_cast<double>(vq[e]) - c.Mq64) * c.invT64)
+                                              : lb[e];
+        w[e] = sample_weight(residual, in_s[e], va, vb, invZp, invZq);
+    }
+}
+
+// ---------------------------------------------------------------- per-sequence pieces
+
+struct SeqCtx {
+    int b, u;
+    unsigned epoch;
+    const float* prow_base;   // target logits of the sequence, [k+1][V]
+    const float* qrow_base;   // draft logits of the sequence, [k][V]
+    int64_t sid;
+    int32_t L;
+};
+
+// Draft token j and its target / draft logits (wave-uniform).
+struct TokenLogits {
+    int tok;
+    bool ok;           // 0 <= tok < V (out-of-range ids, a broken precondition, are rejected)
+    float zp, zq;
+};
+
+__device__ __forceinline__ void flag_error(const RejectArgs& a, int b) {
+    if (lane_id() == 0) {
+        __hip_atomic_fetch_or(a.ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.num_accepted[b] = -1;
+    }
+}
+
+// Draw from the weights of this unit (residual of row `row`; p_row when `use_p` or
+// for the bonus row), given the running sum `run` before this unit and the
+// target t. Only the wavefront owning the crossing unit calls this; lane 0 writes
+// the token, its probability and the padding of the sequence's outputs.
+template <bool kVec4>
+__device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, int row, bool two_rows,
+                                           const float* prow, const float* qrow, const SampleCtx& c,
+                                           const LoadSums& ls, bool use_p, bool exact, double run, double t,
+                                           double invZp, double invZq, double Zp_true) {
+    const int lane = lane_id();
+    const int base = s.u * kUnit + lane * 4;
+    const bool residual = two_rows && !use_p;
+    // load level (each load of a wavefront is 256 consecutive tokens)
+    bool found = false;
+    int istar = 0, ilast = -1;
+    double run_i = run;
+#pragma unroll 1
+    for (int i = 0; i < kVecs; ++i) {
+        double v;
+        if (!use_p) {
+            const double2 g = ls[i][lane];
+            v = residual ? g.x * invZp - g.y * invZq : g.x;
+        } else {                 // zero residual (rare): p-weights of this load, recomputed
+            double w[4];
+            const f4 vp = load4<kVec4>(prow, a.V, base + i * (kWave * 4));
+            load_weights(false, false, vp, vp, c, invZp, invZq, w);
+            v = (w[0] + w[1]) + (w[2] + w[3]);
+        }
+        const double Ti = dpp_wave_sum(v);
+        if (Ti > 0.0) ilast = i;
+        if (exact && !found && Ti > 0.0) {
+            if (run_i + Ti > t) {
+                found = true;
+                istar = i;
+            } else {
+                run_i += Ti;
+            }
+        }
+    }
+    if (!found) {          // rounding left no crossing here: take the last positive weight
+        exact = false;
+        istar = ilast < 0 ? 0 : ilast;
+    }
+    double w[4];
+    const f4 vp = load4<kVec4>(prow, a.V, base + istar * (kWave * 4));
+    const f4 vq = two_rows ? load4<kVec4>(qrow, a.V, base + istar * (kWave * 4)) : vp;
+    load_weights(two_rows, residual, vp, vq, c, invZp, invZq, w);
+    const double lsum = (w[0] + w[1]) + (w[2] + w[3]);
+    const double incl = dpp_wave_incl_scan(lsum);
+    const double excl = dpp_wave_shr1(incl);
+    int lstar, estar = -1;
+    const unsigned long long cross = exact ? __ballot(lsum > 0.0 && run_i + incl > t) : 0ull;
+    int elast = -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) if (w[e] > 0.0) elast = e;
+    if (cross) {
+        lstar = __ffsll(static_cast<long long>(cross)) - 1;
+        double r = run_i + excl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (w[e] > 0.0) {
+                r += w[e];
+                if (estar < 0 && r > t) estar = e;
+            }
+        }
+        if (estar < 0) estar = elast;
+    } else {
+        const unsigned long long pos = __ballot(lsum > 0.0);
+        lstar = pos ? 63 - __builtin_clzll(pos) : 0;
+        estar = elast;
+    }
+    estar = __shfl(estar, lstar, kWave);
+    if (lane != 0) return;
+    if (estar < 0) estar = 0;
+    int y = s.u * kUnit + istar * (kWave * 4) + lstar * 4 + estar;
+    if (y >= a.V) y = a.V - 1;   // only reachable when every weight is zero
+    const double py = exp_nonpos_f64((static_cast<double>(prow[y]) - c.Mp64) * c.invT64) / Zp_true;
+    const int k = a.k, b = s.b;
+    const size_t ob = size_t(b) * (k + 1);
+    a.out_tokens[ob + row] = y;
+    if (a.out_probs) a.out_probs[ob + row] = static_cast<float>(py);
+    for (int i = row + 1; i <= k; ++i) {
         a.out_tokens[ob + i] = -1;
         if (a.out_probs) a.out_probs[ob + i] = 0.0f;
     }
     if (a.accept_probs)
-        for (int i = aa + 1; i < a.k; ++i) a.accept_probs[size_t(b) * a.k + i] = -1.0f;
-    a.num_accepted[b] = aa;
+        for (int i = row + 1; i < k; ++i) a.accept_probs[size_t(b) * k + i] = -1.0f;
+    a.num_accepted[b] = row;
+}
+
+// Sampling after the chain ended at `row` (residual of row `row` if kResidual,
+// else the bonus row p_k). `st` holds the chain statistics of that row.
+template <bool kVec4, bool kResidual, int kUPL>
+__device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s, int row, const f4 (&xp)[kVecs],
+                           const f4 (&xq)[kVecs], const RowStats& st, LoadSums& ls) {
+    const float* prow = s.prow_base + size_t(row) * a.V;
+    const float* qrow = s.qrow_base + size_t(kResidual ? row : 0) * a.V;
+    SampleCtx c;
+    c.Mp = st.Mp;
+    c.Mq = st.Mq;
+    c.invT = a.invT;
+    c.Mp64 = st.Mp;
+    c.Mq64 = st.Mq;
+    c.invT64 = a.invT64;
+    const double lzp = log(st.Zp), lzq = kResidual ? log(st.Zq) : 0.0;
+    c.hp = static_cast<float>(kLnTau + lzp);
+    c.hq = static_cast<float>(kLnTau + lzq);
+    c.dn = static_cast<float>(lzp - lzq);
+
+    const UnitSums us = unit_sums<kVec4, kResidual>(xp, xq, c, prow, qrow, s.u * kUnit + lane_id() * 4, ls);
+    unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
+    const unsigned pay[kSampSlots] = {hi32(us.A), lo32(us.A), hi32(us.B), lo32(us.B),
+                                      hi32(us.P), lo32(us.P), hi32(us.Q), lo32(us.Q)};
+    publish(slots + size_t(s.u) * kSampSlots, pay, s.epoch);
+    unsigned long long* res = a.samp_res + size_t(s.b) * kSampRes;
+    unsigned r[kSampRes];
+    if (s.u == 0) {
+        // unit 0 gathers the unit sums and finds the crossing unit for everyone
+        unsigned v[kUPL][kSampSlots];
+        const bool ok = gather<kSampSlots, kUPL>(slots, a.U, s.epoch, v);
+        double Au[kUPL], Bu[kUPL], Pu[kUPL], zp = 0.0, zq = 0.0;
+#pragma unroll
+        for (int q = 0; q < kUPL; ++q) {
+            Au[q] = join64(v[q][0], v[q][1]);
+            Bu[q] = join64(v[q][2], v[q][3]);
+            Pu[q] = join64(v[q][4], v[q][5]);
+            zp += Pu[q];
+            zq += join64(v[q][6], v[q][7]);
+        }
+        const double Zp = dpp_wave_sum(zp);
+        const double Zq = kResidual ? dpp_wave_sum(zq) : 1.0;
+        const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
+        double Ru[kUPL], tot = 0.0;
+#pragma unroll
+        for (int q = 0; q < kUPL; ++q) {
+            Ru[q] = kResidual ? fmax(0.0, Au[q] * invZp - Bu[q] * invZq) : Pu[q];
+            tot += Ru[q];
+        }
+        double total = dpp_wave_sum(tot);
+        bool use_p = false;                   // the bonus row draws from its own a-weights
+        if (kResidual && !(total > 0.0)) {    // zero residual: draw from p_j instead
+            use_p = true;
+#pragma unroll
+            for (int q = 0; q < kUPL; ++q) Ru[q] = Pu[q];
+            total = Zp;
+        }
+        double u_acc, u_smp;
+        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
+        const double t = u_smp * total;
+        // first unit with positive weight whose running sum exceeds t
+        int cstar = -1, clast = -1;
+        double carry = 0.0, run = 0.0;
+#pragma unroll
+        for (int q = 0; q < kUPL; ++q) {
+            const double incl = dpp_wave_incl_scan(Ru[q]);
+            const double excl = dpp_wave_shr1(incl);
+            const unsigned long long pos = __ballot(Ru[q] > 0.0);
+            if (pos) clast = q * kWave + 63 - __builtin_clzll(pos);
+            const unsigned long long cross = (cstar < 0) ? __ballot(Ru[q] > 0.0 && carry + incl > t) : 0ull;
+            if (cross) {
+                const int l0 = __ffsll(static_cast<long long>(cross)) - 1;
+                cstar = q * kWave + l0;
+                run = carry + __shfl(excl, l0, kWave);
+            }
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+        const bool exact = cstar >= 0;
+        if (!exact) cstar = clast < 0 ? 0 : clast;
+        const unsigned flags = static_cast<unsigned>(cstar) | (use_p ? 1u << 20 : 0u) | (exact ? 1u << 21 : 0u) |
+                               (ok ? 0u : 1u << 22);
+        const unsigned out[kSampRes] = {flags, hi32(run), lo32(run), hi32(t), lo32(t), hi32(Zp), lo32(Zp),
+                                        hi32(Zq), lo32(Zq), 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        publish(res, out, s.epoch);
+#pragma unroll
+        for (int i = 0; i < kSampRes; ++i) r[i] = out[i];
+    } else if (!await_result<kSampRes>(res, s.epoch, r)) {
+        r[0] = 1u << 22;
+    }
+    if (r[0] & (1u << 22)) {
+        flag_error(a, s.b);
+        return;
+    }
+    if (static_cast<int>(r[0] & 0xFFFFFu) != s.u) return;
+    const bool use_p = (r[0] >> 20) & 1u, exact = (r[0] >> 21) & 1u;
+    const double run = join64(r[1], r[2]), t = join64(r[3], r[4]);
+    const double Zp = join64(r[5], r[6]), Zq = join64(r[7], r[8]);
+    const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
+    final_scan<kVec4>(a, s, row, kResidual, prow, qrow, c, ls, use_p, exact, run, t, invZp, invZq, Zp);
+}
+
+// Acceptance test of draft j from the combined statistics and the draft token's
+// two logits (loaded while the group was exchanging statistics); unit 0 writes
+// the outputs of the test.
+__device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, int j, const RowStats& st,
+                                            const TokenLogits& tl) {
+    const int k = a.k, b = s.b;
+    double p_d = 0.0, q_d = 0.0;
+    if (tl.ok) {
+        p_d = exp_nonpos_f64((static_cast<double>(tl.zp) - st.Mp) * a.invT64) / st.Zp;
+        q_d = exp_nonpos_f64((static_cast<double>(tl.zq) - st.Mq) * a.invT64) / st.Zq;
+    }
+    const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
+    double u_acc, u_smp;
+    verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + j, &u_acc, &u_smp);
+    const bool accepted = uniform(static_cast<int>(u_acc < ratio)) != 0;
+    if (s.u == 0 && lane_id() == 0) {
+        if (a.accept_probs) a.accept_probs[size_t(b) * k + j] = static_cast<float>(fmin(1.0, ratio));
+        if (accepted) {
+            a.out_tokens[size_t(b) * (k + 1) + j] = tl.tok;
+            if (a.out_probs) a.out_probs[size_t(b) * (k + 1) + j] = static_cast<float>(p_d);
+        }
+    }
+    return accepted;
+}
+
+enum : unsigned { kResAccepted = 1u, kResError = 2u };
+
+// Level `row` of the chain (rows p_row, q_row; or p_k alone for the bonus row):
+// this wavefront's unit statistics go to the group's slots; unit 0 gathers them,
+// combines them, takes the acceptance test (kTwo) and publishes one result record
+// that the other wavefronts wait on, so only one wavefront per group polls the
+// per-unit slots. Returns the result flags (kResAccepted, kResError).
+template <bool kVec4, bool kTwo, int kUPL>
+__device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
+                                               f4 (&xq)[kVecs], RowStats& st, const TokenLogits& tok) {
+    const float* prow = s.prow_base + size_t(row) * a.V;
+    const float* qrow = s.qrow_base + size_t(kTwo ? row : 0) * a.V;
+    // unit 0 takes the acceptance test: the draft token's two logits are loaded
+    // first, so they have long arrived when the group's statistics are in
+    float ztp = 0.0f, ztq = 0.0f;
+    if (kTwo && s.u == 0 && tok.ok) {
+        ztp = prow[tok.tok];
+        ztq = qrow[tok.tok];
+    }
+    load_unit<kVec4, kTwo>(prow, qrow, a.V, s.u, xp, xq);
+    float mp = -INFINITY, mq = -INFINITY;
+    double sp = 0.0, sq = 0.0;
+#pragma unroll
+    for (int g = 0; g < kVecs / kStep; ++g) {
+        online_step(xp, g, a.c2, mp, sp);
+        if (kTwo) online_step(xq, g, a.c2, mq, sq);
+    }
+    float Mp_u, Mq_u = -INFINITY;
+    double Zp_u, Zq_u = 0.0;
+    unit_reduce(mp, sp, a.invT64, Mp_u, Zp_u);
+    if (kTwo) unit_reduce(mq, sq, a.invT64, Mq_u, Zq_u);
+    const size_t level = size_t(s.b) * (a.k + 1) + row;
+    unsigned long long* slots = a.stat_slots + level * a.U * kStatSlots;
+    unsigned long long* res = a.stat_res + level * kStatRes;
+    const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_u), __builtin_bit_cast(unsigned, Mq_u),
+                                      hi32(Zp_u), lo32(Zp_u), hi32(Zq_u), lo32(Zq_u)};
+    publish(slots + size_t(s.u) * kStatSlots, pay, s.epoch);
+    if (s.u == 0) {
+        unsigned v[kUPL][kStatSlots];
+        unsigned flags = 0;
+        if (gather<kStatSlots, kUPL>(slots, a.U, s.epoch, v)) {
+            TokenLogits tl = tok;
+            tl.zp = uniform(ztp);
+            tl.zq = uniform(ztq);
+            st = combine_stats<kUPL>(v, a.U, a.invT64);
+            if (kTwo && accept_test(a, s, row, st, tl)) flags |= kResAccepted;
+        } else {
+            st.Mp = st.Mq = 0.0f;
+            st.Zp = st.Zq = 1.0;
+            flags |= kResError;
+        }
+        const unsigned out[kStatRes] = {flags, __builtin_bit_cast(unsigned, st.Mp), __builtin_bit_cast(unsigned, st.Mq),
+                                        hi32(st.Zp), lo32(st.Zp), hi32(st.Zq), lo32(st.Zq), 0u};
+        publish(res, out, s.epoch);
+        return flags;
+    }
+    unsigned r[kStatRes];
+    if (!await_result<kStatRes>(res, s.epoch, r)) return kResError;
+    st.Mp = __builtin_bit_cast(float, r[1]);
+    st.Mq = __builtin_bit_cast(float, r[2]);
+    st.Zp = join64(r[3], r[4]);
+    st.Zq = join64(r[5], r[6]);
+    return r[0];
+}
+
+template <bool kVec4, int kUPL>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
+    // Workgroups go to the eight XCDs round-robin; with a multiple of eight groups,
+    // group g takes the U waves on XCD g % 8 (they start together and share an
+    // L2). Any other count uses the plain mapping. Both are bijections.
+    const int w = blockIdx.x;
+    int group, unit;
+    if (a.groups % 8 == 0) {
+        const int l = w / 8;
+        group = (w % 8) + 8 * (l / a.U);
+        unit = l % a.U;
+    } else {
+        group = w / a.U;
+        unit = w % a.U;
+    }
+    SeqCtx s;
+    s.u = unit;
+    {
+        const unsigned last = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.epoch = (last + 1u == 0u) ? 1u : last + 1u;
+    }
+    bool counted = s.u != 0;
+    __shared__ LoadSums ls;
+    f4 xp[kVecs], xq[kVecs];
+    for (int b = group; b < a.B; b += a.groups) {
+        s.b = b;
+        s.prow_base = a.target + size_t(b) * (a.k + 1) * a.V;
+        s.qrow_base = a.draft + size_t(b) * a.k * a.V;
+        // per-lane copies (equal in every lane), first needed at the first acceptance
+        // test, so that no wait for them precedes the loads of the first level
+        s.sid = a.seq_ids[b];
+        s.L = a.seq_lens[b];
+        // the draft tokens of the sequence, lane j holding token j
+        const int lane = lane_id();
+        const int tok_lane = (lane < a.k) ? a.draft_tokens[size_t(b) * a.k + lane] : 0;
+        RowStats st;
+        bool done = false;
+        for (int j = 0; j < a.k && !done; ++j) {
+            TokenLogits tl;
+            tl.tok = __builtin_amdgcn_readlane(tok_lane, j);
+            tl.ok = tl.tok >= 0 && tl.tok < a.V;
+            tl.zp = tl.zq = 0.0f;
+            const unsigned res = level_step<kVec4, true, kUPL>(a, s, j, xp, xq, st, tl);
+            if (!counted) {
+                // every wavefront of the group has published (so has read the epoch)
+                // once unit 0's first gather is through; the last group to get there
+                // records the epoch for the next call
+                counted = true;
+                if (lane == 0) {
+                    const unsigned n = __hip_atomic_fetch_add(a.ctl + kCtlDone, 1u, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+                    if (n + 1 == static_cast<unsigned>(a.groups)) {
+                        __hip_atomic_store(a.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(a.ctl + kCtlEpoch, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+            if (res & kResError) {
+                flag_error(a, b);
+                done = true;
+            } else if (!(res & kResAccepted)) {
+                sample_row<kVec4, true, kUPL>(a, s, j, xp, xq, st, ls);
+                done = true;
+            }
+        }
+        if (done) continue;
+        TokenLogits none;
+        none.tok = 0;
+        none.ok = false;
+        none.zp = none.zq = 0.0f;
+        if (level_step<kVec4, false, kUPL>(a, s, a.k, xp, xq, st, none) & kResError) {
+            flag_error(a, b);
+            continue;
+        }
+        sample_row<kVec4, false, kUPL>(a, s, a.k, xp, xq, st, ls);
+    }
+}
+
+template <bool kVec4, int kUPL>
+hipError_t co_resident(int dev, int* waves) {
+    static int memo[64];
+    if (dev >= 0 && dev < 64 && memo[dev] > 0) {
+        *waves = memo[dev];
+        return hipSuccess;
+    }
+    int per_cu = 0, cus = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4, kUPL>, kWave, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    *waves = per_cu * cus;
+    if (dev >= 0 && dev < 64) memo[dev] = *waves;
+    return hipSuccess;
+}
+
+template <bool kVec4, int kUPL>
+hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int waves = 0;
+    e = co_resident<kVec4, kUPL>(dev, &waves);
+    if (e != hipSuccess) return e;
+    int groups = min(a.B, waves / a.U);
+    if (groups < 1) return hipErrorInvalidConfiguration;
+    if (groups > 8) groups -= groups % 8;   // a multiple of 8 (one XCD per group); rounds take the rest
+    a.groups = groups;
+    // A plain launch: the grid never exceeds what the device holds at once, so on
+    // a GPU not shared with other streams every group is resident together. (A
+    // cooperative launch would guarantee it, at ~13 us of extra launch latency
+    // per call on this stack; should residency ever be partial, the waits are
+    // bounded and the affected sequences report an error instead of hanging.)
+    hipLaunchKernelGGL((reject_kernel<kVec4, kUPL>), dim3(groups * a.U), dim3(kWave), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 size_t reject_workspace_bytes(int B, int k, int V) {
-    const int W = (V + kSlice - 1) / kSlice;
-    return reject_layout(B, k, W).total;
+    const int U = (V + kUnit - 1) / kUnit;
+    return reject_layout(B, k, U).total;
 }
 
+int reject_max_vocab() { return kUnit * kWave * kMaxUnitsPerLane; }
+
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
-    const int W = (p.V + kSlice - 1) / kSlice;
-    const RejectLayout lay = reject_layout(p.B, p.k, W);
+    const int U = (p.V + kUnit - 1) / kUnit;
+    if (U > kWave * kMaxUnitsPerLane) return hipErrorInvalidValue;
+    const RejectLayout lay = reject_layout(p.B, p.k, U);
     char* ws = static_cast<char*>(p.workspace);
     RejectArgs a;
     a.target = p.target_logits;
@@ -620,25 +902,19 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.num_accepted = p.num_accepted;
     a.out_probs = p.out_probs;
     a.accept_probs = p.accept_probs;
-    a.active = reinterpret_cast<int32_t*>(ws + lay.active);
-    a.final_rec = reinterpret_cast<FinalRecord*>(ws + lay.final_rec);
-    a.chain_part = reinterpret_cast<double*>(ws + lay.chain_part);
-    a.sample_part = reinterpret_cast<double*>(ws + lay.sample_part);
-    a.B = p.B; a.k = p.k; a.V = p.V; a.W = W;
+    a.ctl = reinterpret_cast<unsigned*>(ws + lay.ctl);
+    a.stat_slots = reinterpret_cast<unsigned long long*>(ws + lay.stat);
+    a.samp_slots = reinterpret_cast<unsigned long long*>(ws + lay.samp);
+    a.stat_res = reinterpret_cast<unsigned long long*>(ws + lay.stat_res);
+    a.samp_res = reinterpret_cast<unsigned long long*>(ws + lay.samp_res);
+    a.B = p.B; a.k = p.k; a.V = p.V; a.U = U; a.groups = 0;
     a.invT = 1.0f / p.temperature;
+    a.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(p.temperature));
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.seed = p.seed;
-    const dim3 grid(W, p.B), block(kRT);
     const bool vec4 = (p.V % 4) == 0;
-    for (int j = 0; j <= p.k; ++j) {
-        if (vec4) hipLaunchKernelGGL(reject_level_kernel<true>, grid, block, 0, stream, a, j);
-        else hipLaunchKernelGGL(reject_level_kernel<false>, grid, block, 0, stream, a, j);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (vec4) hipLaunchKernelGGL(reject_finalize_kernel<true>, dim3(p.B), dim3(kWave), 0, stream, a);
-    else hipLaunchKernelGGL(reject_finalize_kernel<false>, dim3(p.B), dim3(kWave), 0, stream, a);
-    return hipGetLastError();
+    if (U <= kWave) return vec4 ? launch_variant<true, 1>(a, stream) : launch_variant<false, 1>(a, stream);
+    return vec4 ? launch_variant<true, kMaxUnitsPerLane>(a, stream) : launch_variant<false, kMaxUnitsPerLane>(a, stream);
 }
 
 }  // namespace specverify
