@@ -15,9 +15,14 @@ work. Prints one JSON line:
 
 Other modes:
   --cpu-baseline-only          time the oracle (run in a single-threaded child)
-  --copy-calibration           also run a plain device copy of known size (for
-                               scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)
+  --copy-calibration           also run an elementwise kernel of known traffic
+                               (negation of 512 MiB fp32: 512 MiB read, 512 MiB
+                               written) for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
   --summarize-rocprof DIR      turn rocprofv3 output in DIR into a text summary
+  --write-counters             from a FETCH_SIZE run (--fetch-dir) and a WRITE_SIZE
+                               run (--write-dir), both with --copy-calibration,
+                               write the per-call HBM traffic file that the
+                               roofline's `traffic` field is read from
 """
 
 from __future__ import annotations
@@ -187,6 +192,53 @@ def summarize_rocprof(path: str, out: str, command: str) -> None:
     print("\n".join(lines))
 
 
+CALIB_BYTES = 1 << 29   # bytes read and bytes written by one calibration dispatch
+
+
+def _counter_means(path: str, counter: str) -> dict:
+    """Mean value per dispatch of one rocprofv3 counter, by kernel label."""
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {path}")
+    agg = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    agg.setdefault(_kernel_label(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, write_cmd: str) -> None:
+    """Per-call HBM bytes of the verify attention (and, for reference, the reject
+    kernel) from FETCH_SIZE / WRITE_SIZE runs, each scaled by what the same counter
+    reads for the calibration kernel of known traffic."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    calib = lambda d: [v for k, v in d.items() if "neg" in k.lower()]
+    cf, cw = calib(fetch), calib(write)
+    if not cf or not cw:
+        raise RuntimeError("calibration kernel not found in the counter runs (run them with --copy-calibration)")
+    f_scale = CALIB_BYTES / (max(cf) * 1024.0)   # counters are in KiB per dispatch
+    w_scale = CALIB_BYTES / (max(cw) * 1024.0)
+    attn = sorted(k for k in set(fetch) | set(write) if k.startswith("attn_"))
+    rej = sorted(k for k in set(fetch) | set(write) if k.startswith("reject_"))
+    per_call = lambda ks: sum(fetch.get(k, 0.0) * 1024.0 * f_scale + write.get(k, 0.0) * 1024.0 * w_scale for k in ks)
+    lines = ["# rocprofv3 hardware counters, 8b workload (B=64, k=3, V=128256), one call of each kernel per step",
+             f"# fetch command: {fetch_cmd}", f"# write command: {write_cmd}",
+             "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by the factor that maps the",
+             "# calibration kernel (fp32 negation: 512 MiB read, 512 MiB written) onto its known traffic.",
+             f"kernel_source_sha256_16: {kernel_source_hash()}",
+             f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}"]
+    for k in attn + rej:
+        lines.append(f"{k}: FETCH_SIZE {fetch.get(k, 0.0):.1f} KiB, WRITE_SIZE {write.get(k, 0.0):.1f} KiB per dispatch")
+    lines.append(f"hbm_bytes_per_call: {per_call(attn):.0f}")
+    lines.append(f"reject_hbm_bytes_per_call: {per_call(rej):.0f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ----------------------------------------------------------------------------- GPU benchmark
 
 def gpu_bench(args) -> dict:
@@ -270,13 +322,13 @@ def gpu_bench(args) -> dict:
 
     copy_info = None
     if args.copy_calibration:
-        n = 1 << 29   # 512 MiB copied = 512 MiB read + 512 MiB written
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        n = 1 << 27   # 128 Mi fp32 = 512 MiB read + 512 MiB written by one elementwise kernel
+        src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        copy_info = dict(bytes_read=n, bytes_written=n, calls=3)
+        copy_info = dict(kernel="elementwise neg (fp32)", bytes_read=4 * n, bytes_written=4 * n, calls=3)
 
     tokens = int(np.sum(acc + 1))
     a_bytes, r_bytes, c_bytes = algorithmic_bytes(p, np.asarray(seq_lens0.cpu()), acc)
@@ -299,7 +351,7 @@ def gpu_bench(args) -> dict:
                     global_batch=B, k=k, parallelism="none (1 GPU)"),
         roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=attn_gbs / HBM_PEAK_GBS, traffic=traffic,
-                      kernel="spec_verify_attn (attn_partial_kernel + attn_merge_kernel)",
+                      kernel="spec_verify_attn (attn_streamk_kernel + attn_merge_kernel)",
                       algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_avg_s * 1e6),
         verified_tokens_per_step=tokens,
         mean_emitted_per_sequence=tokens / B,
@@ -330,7 +382,17 @@ def main():
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--out", metavar="FILE")
     ap.add_argument("--command", default="", help="command line recorded in a rocprof summary")
+    ap.add_argument("--write-counters", action="store_true")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--fetch-command", default="")
+    ap.add_argument("--write-command", default="")
     args = ap.parse_args()
+
+    if args.write_counters:
+        write_counters(args.fetch_dir, args.write_dir, args.out or COUNTERS_FILE, args.fetch_command,
+                       args.write_command)
+        return
 
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.out or "/dev/stdout", args.command)
