@@ -69,8 +69,8 @@ struct RejectArgs {
     float* out_probs;
     float* accept_probs;
     unsigned* ctl;                     // epoch of the last finished call, finished-wave count, error flag
-    unsigned long long* stat_slots;    // [B][k+1][U][kStatSlots]
-    unsigned long long* samp_slots;    // [B][U][kSampSlots]
+    unsigned long long* stat_slots;    // [B][k+1][kStatSlots][U]
+    unsigned long long* samp_slots;    // [B][kSampSlots][U]
     unsigned long long* stat_res;      // [B][k+1][kStatRes]: unit 0's combined statistics and decision
     unsigned long long* samp_res;      // [B][kSampRes]: unit 0's unit-level search result
     int B, k, V, U, groups;
@@ -119,17 +119,20 @@ __device__ __forceinline__ double join64(unsigned hi, unsigned lo) {
     return __builtin_bit_cast(double, (static_cast<unsigned long long>(hi) << 32) | lo);
 }
 
-// Lane 0 publishes the N payloads (N back-to-back single-lane stores).
+// Lane 0 publishes the N payloads (N back-to-back single-lane stores) to
+// slots[s * stride], s = 0 .. N-1.
 template <int N>
-__device__ __forceinline__ void publish(unsigned long long* slots, const unsigned (&payload)[N], unsigned epoch) {
+__device__ __forceinline__ void publish(unsigned long long* slots, const unsigned (&payload)[N], unsigned epoch,
+                                        int stride = 1) {
     if (lane_id() == 0) {
 #pragma unroll
-        for (int s = 0; s < N; ++s) slot_store(slots + s, payload[s], epoch);
+        for (int s = 0; s < N; ++s) slot_store(slots + size_t(s) * stride, payload[s], epoch);
     }
 }
 
 // Waits until the N slots of every unit carry `epoch` and returns their payloads:
-// lane l gets units l, l + 64, ... (kUPL of them; units >= U read as zero).
+// lane l gets units l, l + 64, ... (kUPL of them; units >= U read as zero). Slot s
+// of unit u is slots[s * U + u], so each read instruction covers consecutive words.
 // Returns false if the bounded wait ran out (only possible if the group were not
 // co-resident, which the cooperative launch rules out).
 template <int N, int kUPL>
@@ -144,7 +147,7 @@ __device__ __forceinline__ bool gather(unsigned long long* slots, int U, unsigne
             for (int s = 0; s < N; ++s) {
                 unsigned long long v = 0;
                 if (u < U) {
-                    v = slot_load(slots + size_t(u) * N + s);
+                    v = slot_load(slots + size_t(s) * U + u);
                     ok = ok && static_cast<unsigned>(v) == epoch;
                 }
                 out[r][s] = static_cast<unsigned>(v >> 32);
@@ -473,6 +476,7 @@ struct TokenLogits {
     int tok;
     bool ok;           // 0 <= tok < V (out-of-range ids, a broken precondition, are rejected)
     float zp, zq;
+    double u_acc;      // the test's uniform, computed before the group's statistics arrive
 };
 
 __device__ __forceinline__ void flag_error(const RejectArgs& a, int b) {
@@ -595,7 +599,7 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
     unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
     const unsigned pay[kSampSlots] = {hi32(us.A), lo32(us.A), hi32(us.B), lo32(us.B),
                                       hi32(us.P), lo32(us.P), hi32(us.Q), lo32(us.Q)};
-    publish(slots + size_t(s.u) * kSampSlots, pay, s.epoch);
+    publish(slots + s.u, pay, s.epoch, a.U);
     unsigned long long* res = a.samp_res + size_t(s.b) * kSampRes;
     unsigned r[kSampRes];
     if (s.u == 0) {
@@ -684,9 +688,7 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
         q_d = exp_nonpos_f64((static_cast<double>(tl.zq) - st.Mq) * a.invT64) / st.Zq;
     }
     const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
-    double u_acc, u_smp;
-    verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + j, &u_acc, &u_smp);
-    const bool accepted = uniform(static_cast<int>(u_acc < ratio)) != 0;
+    const bool accepted = uniform(static_cast<int>(tl.u_acc < ratio)) != 0;
     if (s.u == 0 && lane_id() == 0) {
         if (a.accept_probs) a.accept_probs[size_t(b) * k + j] = static_cast<float>(fmin(1.0, ratio));
         if (accepted) {
@@ -733,12 +735,16 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
     unsigned long long* res = a.stat_res + level * kStatRes;
     const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_u), __builtin_bit_cast(unsigned, Mq_u),
                                       hi32(Zp_u), lo32(Zp_u), hi32(Zq_u), lo32(Zq_u)};
-    publish(slots + size_t(s.u) * kStatSlots, pay, s.epoch);
+    publish(slots + s.u, pay, s.epoch, a.U);
     if (s.u == 0) {
+        TokenLogits tl = tok;
+        if (kTwo) {
+            double u_smp;
+            verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &tl.u_acc, &u_smp);
+        }
         unsigned v[kUPL][kStatSlots];
         unsigned flags = 0;
         if (gather<kStatSlots, kUPL>(slots, a.U, s.epoch, v)) {
-            TokenLogits tl = tok;
             tl.zp = uniform(ztp);
             tl.zq = uniform(ztq);
             st = combine_stats<kUPL>(v, a.U, a.invT64);
@@ -804,6 +810,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             tl.tok = __builtin_amdgcn_readlane(tok_lane, j);
             tl.ok = tl.tok >= 0 && tl.tok < a.V;
             tl.zp = tl.zq = 0.0f;
+            tl.u_acc = 0.0;
             const unsigned res = level_step<kVec4, true, kUPL>(a, s, j, xp, xq, st, tl);
             if (!counted) {
                 // every wavefront of the group has published (so has read the epoch)
@@ -832,6 +839,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         none.tok = 0;
         none.ok = false;
         none.zp = none.zq = 0.0f;
+        none.u_acc = 0.0;
         if (level_step<kVec4, false, kUPL>(a, s, a.k, xp, xq, st, none) & kResError) {
             flag_error(a, b);
             continue;
