@@ -16,8 +16,9 @@
 //    accumulators of O^T[., r] on the same lanes (lane % 16 == r), so the online
 //    softmax needs only a 4-lane max. Operands are 16-byte global loads straight
 //    into MFMA registers: K pages are [block][Hkv][slot][D], V pages are
-//    [block][Hkv][D][slot]. Each K/V byte is read once; LDS holds only the
-//    block-table slice and the cross-wave combine.
+//    [block][Hkv][D][slot]. Each K/V byte is read once, with streaming
+//    (nontemporal) loads; LDS holds only the block-table slice and the
+//    cross-wave combine.
 //  * Persistent, balanced grid. Contexts are ragged, so a grid of fixed-size KV
 //    splits leaves half its workgroups empty and a ragged tail. Instead the work
 //    of all (sequence, KV head, 128-key iteration) triples is laid out in one
@@ -234,14 +235,14 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                     const uint16_t* kp = a.kc + (size_t(pg) * a.Hkv + g) * head_stride +
                                          size_t(key & (bs - 1)) * D + 8 * lg;
 #pragma unroll
-                    for (int ds = 0; ds < DS; ++ds) kr[t][ds] = load16(kp + 32 * ds);
+                    for (int ds = 0; ds < DS; ++ds) kr[t][ds] = load16_nt(kp + 32 * ds);
                 }
                 {
                     const int vkey0 = min(t0 + 8 * lg, (s1 - 1) & ~7);
                     const int pg = s_bt[(vkey0 >> a.bs_log2) - p0];
                     const uint16_t* vp = a.vc + (size_t(pg) * a.Hkv + g) * head_stride + (vkey0 & (bs - 1));
 #pragma unroll
-                    for (int j = 0; j < DJ; ++j) vr[j] = load16(vp + size_t(16 * j + l16) * bs);
+                    for (int j = 0; j < DJ; ++j) vr[j] = load16_nt(vp + size_t(16 * j + l16) * bs);
                 }
                 if (t0 + kBlockKeys > s1) {
                     // tail block: values of keys >= s1 (past the sequence, or another piece's) become 0

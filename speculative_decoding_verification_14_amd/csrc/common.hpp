@@ -16,6 +16,14 @@ __device__ __forceinline__ uint4 load16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte streaming load (nontemporal hint): for data read once per call, such
+// as the KV cache, it streams past the caches instead of displacing them.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }
