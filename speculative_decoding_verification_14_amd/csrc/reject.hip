@@ -494,7 +494,11 @@ template <bool kVec4>
 __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, int row, bool two_rows,
                                            const float* prow, const float* qrow, const SampleCtx& c,
                                            const LoadSums& ls, bool use_p, bool exact, double run, double t,
-                                           double invZp, double invZq, double Zp_true) {
+                                           double invZp, double invZq, double Zp_true, double wscale,
+                                           double M_ref) {
+    // wscale maps this unit's weights onto the scale of run and t (1, except for
+    // the bonus row, whose unit weights are relative to the unit's own maximum);
+    // M_ref is the row maximum the emitted probability is taken against.
     const int lane = lane_id();
     const int base = s.u * kUnit + lane * 4;
     const bool residual = two_rows && !use_p;
@@ -507,12 +511,12 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
         double v;
         if (!use_p) {
             const double2 g = ls[i][lane];
-            v = residual ? g.x * invZp - g.y * invZq : g.x;
+            v = (residual ? g.x * invZp - g.y * invZq : g.x) * wscale;
         } else {                 // zero residual (rare): p-weights of this load, recomputed
             double w[4];
             const f4 vp = load4<kVec4>(prow, a.V, base + i * (kWave * 4));
             load_weights(false, false, vp, vp, c, invZp, invZq, w);
-            v = (w[0] + w[1]) + (w[2] + w[3]);
+            v = ((w[0] + w[1]) + (w[2] + w[3])) * wscale;
         }
         const double Ti = dpp_wave_sum(v);
         if (Ti > 0.0) ilast = i;
@@ -533,6 +537,8 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     const f4 vp = load4<kVec4>(prow, a.V, base + istar * (kWave * 4));
     const f4 vq = two_rows ? load4<kVec4>(qrow, a.V, base + istar * (kWave * 4)) : vp;
     load_weights(two_rows, residual, vp, vq, c, invZp, invZq, w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] *= wscale;
     const double lsum = (w[0] + w[1]) + (w[2] + w[3]);
     const double incl = dpp_wave_incl_scan(lsum);
     const double excl = dpp_wave_shr1(incl);
@@ -562,7 +568,7 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     if (estar < 0) estar = 0;
     int y = s.u * kUnit + istar * (kWave * 4) + lstar * 4 + estar;
     if (y >= a.V) y = a.V - 1;   // only reachable when every weight is zero
-    const double py = exp_nonpos_f64((static_cast<double>(prow[y]) - c.Mp64) * c.invT64) / Zp_true;
+    const double py = exp_nonpos_f64((static_cast<double>(prow[y]) - M_ref) * c.invT64) / Zp_true;
     const int k = a.k, b = s.b;
     const size_t ob = size_t(b) * (k + 1);
     a.out_tokens[ob + row] = y;
@@ -673,7 +679,8 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
     const double run = join64(r[1], r[2]), t = join64(r[3], r[4]);
     const double Zp = join64(r[5], r[6]), Zq = join64(r[7], r[8]);
     const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
-    final_scan<kVec4>(a, s, row, kResidual, prow, qrow, c, ls, use_p, exact, run, t, invZp, invZq, Zp);
+    final_scan<kVec4>(a, s, row, kResidual, prow, qrow, c, ls, use_p, exact, run, t, invZp, invZq, Zp, 1.0,
+                      c.Mp64);
 }
 
 // Acceptance test of draft j from the combined statistics and the draft token's
@@ -768,6 +775,103 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
     return r[0];
 }
 
+// The bonus row p_k after k acceptances, with one group exchange instead of two:
+// each wavefront weighs its unit against the unit's own maximum M_u (heavy logits
+// judged with the unit's own normaliser, a superset of the row's heavy set) and
+// publishes (sum of weights, M_u); unit 0 rescales the sums by e^{(M_u - M)/T},
+// finds the crossing unit and publishes it with the row's Z and M.
+template <bool kVec4, int kUPL>
+__device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
+                                          LoadSums& ls) {
+    const int row = a.k;
+    const float* prow = s.prow_base + size_t(row) * a.V;
+    load_unit<kVec4, false>(prow, prow, a.V, s.u, xp, xq);
+    float m = -INFINITY;
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < kVecs / kStep; ++g) online_step(xp, g, a.c2, m, acc);
+    float Mu;
+    double Zu;
+    unit_reduce(m, acc, a.invT64, Mu, Zu);
+    SampleCtx c;
+    c.Mp = Mu;
+    c.Mq = 0.0f;
+    c.invT = a.invT;
+    c.Mp64 = Mu;
+    c.Mq64 = 0.0;
+    c.invT64 = a.invT64;
+    c.hp = static_cast<float>(kLnTau + log(Zu));
+    c.hq = kLnTau;
+    c.dn = 0.0f;
+    const UnitSums us = unit_sums<kVec4, false>(xp, xq, c, prow, prow, s.u * kUnit + lane_id() * 4, ls);
+    const double Mu64 = Mu;
+    unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
+    const unsigned pay[kSampSlots] = {hi32(us.P), lo32(us.P), hi32(Mu64), lo32(Mu64), 0u, 0u, 0u, 0u};
+    publish(slots + s.u, pay, s.epoch, a.U);
+    unsigned long long* res = a.samp_res + size_t(s.b) * kSampRes;
+    unsigned r[kSampRes];
+    if (s.u == 0) {
+        unsigned v[kUPL][kSampSlots];
+        const bool ok = gather<kSampSlots, kUPL>(slots, a.U, s.epoch, v);
+        double Pu[kUPL], Mv[kUPL];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kUPL; ++q) {
+            const bool valid = lane_id() + q * kWave < a.U;
+            Pu[q] = valid ? join64(v[q][0], v[q][1]) : 0.0;
+            Mv[q] = valid ? join64(v[q][2], v[q][3]) : -INFINITY;
+            mloc = fmaxf(mloc, static_cast<float>(Mv[q]));
+        }
+        const double M = dpp_wave_max(mloc);
+        double Wu[kUPL], tot = 0.0;
+#pragma unroll
+        for (int q = 0; q < kUPL; ++q) {
+            Wu[q] = (Pu[q] > 0.0) ? Pu[q] * exp_nonpos_f64((Mv[q] - M) * a.invT64) : 0.0;
+            tot += Wu[q];
+        }
+        const double Z = dpp_wave_sum(tot);
+        double u_acc, u_smp;
+        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
+        const double t = u_smp * Z;
+        int cstar = -1, clast = -1;
+        double carry = 0.0, run = 0.0;
+#pragma unroll
+        for (int q = 0; q < kUPL; ++q) {
+            const double incl = dpp_wave_incl_scan(Wu[q]);
+            const double excl = dpp_wave_shr1(incl);
+            const unsigned long long pos = __ballot(Wu[q] > 0.0);
+            if (pos) clast = q * kWave + 63 - __builtin_clzll(pos);
+            const unsigned long long cross = (cstar < 0) ? __ballot(Wu[q] > 0.0 && carry + incl > t) : 0ull;
+            if (cross) {
+                const int l0 = __ffsll(static_cast<long long>(cross)) - 1;
+                cstar = q * kWave + l0;
+                run = carry + __shfl(excl, l0, kWave);
+            }
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+        const bool exact = cstar >= 0;
+        if (!exact) cstar = clast < 0 ? 0 : clast;
+        const unsigned flags = static_cast<unsigned>(cstar) | (exact ? 1u << 21 : 0u) | (ok ? 0u : 1u << 22);
+        const unsigned out[kSampRes] = {flags, hi32(run), lo32(run), hi32(t), lo32(t), hi32(Z), lo32(Z),
+                                        hi32(M), lo32(M), 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        publish(res, out, s.epoch);
+#pragma unroll
+        for (int i = 0; i < kSampRes; ++i) r[i] = out[i];
+    } else if (!await_result<kSampRes>(res, s.epoch, r)) {
+        r[0] = 1u << 22;
+    }
+    if (r[0] & (1u << 22)) {
+        flag_error(a, s.b);
+        return;
+    }
+    if (static_cast<int>(r[0] & 0xFFFFFu) != s.u) return;
+    const bool exact = (r[0] >> 21) & 1u;
+    const double run = join64(r[1], r[2]), t = join64(r[3], r[4]);
+    const double Z = join64(r[5], r[6]), M = join64(r[7], r[8]);
+    const double wscale = exp_nonpos_f64((Mu64 - M) * a.invT64);
+    final_scan<kVec4>(a, s, row, false, prow, prow, c, ls, false, exact, run, t, 1.0 / Z, 1.0, Z, wscale, M);
+}
+
 template <bool kVec4, int kUPL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
     // Workgroups go to the eight XCDs round-robin; with a multiple of eight groups,
@@ -835,16 +939,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             }
         }
         if (done) continue;
-        TokenLogits none;
-        none.tok = 0;
-        none.ok = false;
-        none.zp = none.zq = 0.0f;
-        none.u_acc = 0.0;
-        if (level_step<kVec4, false, kUPL>(a, s, a.k, xp, xq, st, none) & kResError) {
-            flag_error(a, b);
-            continue;
-        }
-        sample_row<kVec4, false, kUPL>(a, s, a.k, xp, xq, st, ls);
+        bonus_row<kVec4, kUPL>(a, s, xp, xq, ls);
     }
 }
 
