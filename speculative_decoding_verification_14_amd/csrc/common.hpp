@@ -103,11 +103,11 @@ __device__ __forceinline__ double dpp_wave_incl_scan(double v) {
 // applied to an inclusive one.
 __device__ __forceinline__ double dpp_wave_shr1(double v) { return dpp_move_f64<0x138>(v); }   // wave_shr:1
 
-// threadIdx.x behind an empty asm, so that lane-id compares are computed where
-// they are used instead of being hoisted out of loops (a hoisted compare pins a
-// 64-bit lane mask in scalar registers for the whole loop).
+// The lane index within the wavefront behind an empty asm, so that lane-id
+// compares are computed where they are used instead of being hoisted out of loops
+// (a hoisted compare pins a 64-bit lane mask in scalar registers for the whole loop).
 __device__ __forceinline__ int lane_id() {
-    int l = static_cast<int>(threadIdx.x);
+    int l = static_cast<int>(threadIdx.x & 63u);
     asm volatile("" : "+v"(l));
     return l;
 }

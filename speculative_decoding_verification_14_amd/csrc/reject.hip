@@ -10,24 +10,27 @@
 // after full acceptance sample p_k. Sampling is inverse CDF in ascending token id.
 //
 // How (one MI355X, one launch for the whole batch):
-//  * A row of V logits is cut into units of 4096; unit u of every row of a
-//    sequence belongs to one wavefront, which holds it in registers (16 x 16-byte
-//    loads per lane per row, all in flight together). The U = ceil(V / 4096)
-//    wavefronts of a sequence form a group; groups take sequences in turn.
-//  * Level j: the group loads its units of p_j and q_j, each wavefront reduces
-//    its unit to (max, sum of exps) with an online softmax on the DPP network,
-//    publishes the pair and waits for the other U - 1. Every wavefront then
-//    combines the U pairs in the same fixed order, so all of them take the same
-//    acceptance decision without further communication.
+//  * A row of V logits is cut into units of 4096; each unit of the current row
+//    (pair) is held in the registers of one wavefront (16 x 16-byte loads per
+//    lane per row, all in flight together). Eight unit wavefronts form a
+//    512-thread workgroup (one per CU); the Q = ceil(U / 8) workgroups of a
+//    sequence form a group, and groups take sequences in turn.
+//  * Level j: every wavefront reduces its units of p_j and q_j to (max, sum of
+//    exps) with an online softmax on the DPP network; wave 0 of the workgroup
+//    combines the eight through LDS and publishes the workgroup's pair; then it
+//    gathers the Q pairs of the group, combines them in a fixed order and takes
+//    the acceptance test. Every workgroup computes the same decision from the
+//    same published bits, so one cross-CU exchange per level suffices.
 //  * Exchange is fence-free: each published 32-bit value travels in a 64-bit
 //    atomic slot together with the call's epoch, so a slot is either stale (old
 //    epoch, keep polling) or complete. No cache write-back or invalidation is
 //    needed and the workspace never has to be cleared between calls.
 //  * On the first rejection (or after k acceptances, on row p_k) the rows still
-//    in registers are turned into sampling weights: nothing is read twice. The
-//    group exchanges per-unit sums, every wavefront finds the unit where the
-//    running sum crosses u_smp * total, and the wavefront owning that unit scans
-//    its registers for the token.
+//    in registers are turned into sampling weights: nothing is read twice. Unit
+//    sums go through LDS to the workgroup leader, one exchange gives every
+//    leader the workgroup totals, the leaders find the crossing workgroup, and
+//    that workgroup's leader finds the crossing unit, whose wavefront scans its
+//    per-load sums in LDS for the token.
 //  * Precision: the chain statistics use fp32 exps (relative error ~1e-7, ample
 //    for an acceptance test). The sampling pass takes logits whose probability
 //    exceeds 2^-14 in fp64 and the rest with an error-compensated fp32 exp,
@@ -47,10 +50,10 @@ constexpr int kVecs = 16;                  // 16-byte loads per lane per row
 constexpr int kUnit = kWave * kVecs * 4;   // 4096 logits: one wavefront's share of a row
 constexpr int kStep = 4;                   // loads per online-softmax step (16 logits per lane)
 constexpr int kStatSlots = 6;              // M_p, M_q, Z_p (hi, lo), Z_q (hi, lo)
-constexpr int kSampSlots = 8;              // A, B, P, Q (hi, lo each)
-constexpr int kStatRes = 8;                // decision flags, M_p, M_q, Z_p (hi, lo), Z_q (hi, lo), unused
-constexpr int kSampRes = 16;               // flags | crossing unit, run, t, Z_p, Z_q (hi, lo each), unused
-constexpr int kMaxUnitsPerLane = 4;        // U <= 256, i.e. V <= 2^20
+constexpr int kSampSlots = 8;              // A, B, P, Q (hi, lo each); bonus row: weight sum, max
+constexpr int kUnitWaves = 8;              // unit wavefronts per workgroup
+constexpr int kRT = kUnitWaves * kWave;    // 512 threads
+constexpr int kMaxQ = 32;                  // workgroups per sequence: U <= 256, i.e. V <= 2^20
 constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this probability share use fp64
 constexpr unsigned kSpinLimit = 1u << 20;
 
@@ -69,11 +72,9 @@ struct RejectArgs {
     float* out_probs;
     float* accept_probs;
     unsigned* ctl;                     // epoch of the last finished call, finished-wave count, error flag
-    unsigned long long* stat_slots;    // [B][k+1][kStatSlots][U]
-    unsigned long long* samp_slots;    // [B][kSampSlots][U]
-    unsigned long long* stat_res;      // [B][k+1][kStatRes]: unit 0's combined statistics and decision
-    unsigned long long* samp_res;      // [B][kSampRes]: unit 0's unit-level search result
-    int B, k, V, U, groups;
+    unsigned long long* stat_slots;    // [B][k+1][kStatSlots][Q]: workgroup statistics per level
+    unsigned long long* samp_slots;    // [B][kSampSlots][Q]: workgroup sampling sums
+    int B, k, V, U, Q, groups;
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
     double invT64;
@@ -83,17 +84,15 @@ struct RejectArgs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RejectLayout {
-    size_t ctl, stat, samp, stat_res, samp_res, total;
+    size_t ctl, stat, samp, total;
 };
 
-RejectLayout reject_layout(int B, int k, int U) {
+RejectLayout reject_layout(int B, int k, int Q) {
     RejectLayout L;
     size_t o = 0;
     L.ctl = o;  o = align256(o + 4 * sizeof(unsigned));
-    L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * U * kStatSlots);
-    L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * kSampSlots);
-    L.stat_res = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * kStatRes);
-    L.samp_res = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * kSampRes);
+    L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * Q * kStatSlots);
+    L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * Q * kSampSlots);
     L.total = o;
     return L;
 }
@@ -130,55 +129,29 @@ __device__ __forceinline__ void publish(unsigned long long* slots, const unsigne
     }
 }
 
-// Waits until the N slots of every unit carry `epoch` and returns their payloads:
-// lane l gets units l, l + 64, ... (kUPL of them; units >= U read as zero). Slot s
-// of unit u is slots[s * U + u], so each read instruction covers consecutive words.
-// Returns false if the bounded wait ran out (only possible if the group were not
-// co-resident, which the cooperative launch rules out).
-template <int N, int kUPL>
-__device__ __forceinline__ bool gather(unsigned long long* slots, int U, unsigned epoch, unsigned (&out)[kUPL][N]) {
+// Waits until the N slots of each of the Q workgroups carry `epoch` and returns
+// their payloads: lane l gets workgroup l (lanes >= Q read zero). Slot s of
+// workgroup l is slots[s * Q + l], so each read instruction covers consecutive
+// words. Returns false if the bounded wait ran out (only possible if the group
+// were not resident at once).
+template <int N>
+__device__ __forceinline__ bool gather(unsigned long long* slots, int Q, unsigned epoch, unsigned (&out)[N]) {
     const int lane = lane_id();
     for (unsigned it = 0; it < kSpinLimit; ++it) {
         bool ok = true;
 #pragma unroll
-        for (int r = 0; r < kUPL; ++r) {
-            const int u = lane + r * kWave;
-#pragma unroll
-            for (int s = 0; s < N; ++s) {
-                unsigned long long v = 0;
-                if (u < U) {
-                    v = slot_load(slots + size_t(s) * U + u);
-                    ok = ok && static_cast<unsigned>(v) == epoch;
-                }
-                out[r][s] = static_cast<unsigned>(v >> 32);
+        for (int s = 0; s < N; ++s) {
+            unsigned long long v = 0;
+            if (lane < Q) {
+                v = slot_load(slots + size_t(s) * Q + lane);
+                ok = ok && static_cast<unsigned>(v) == epoch;
             }
+            out[s] = static_cast<unsigned>(v >> 32);
         }
         if (__all(ok)) return true;
         __builtin_amdgcn_s_sleep(4);
     }
     return false;
-}
-
-// Waits until the N words of a result record carry `epoch` (lane i polls word i:
-// one cache line per poll) and returns the payloads, identical in every lane.
-template <int N>
-__device__ __forceinline__ bool await_result(unsigned long long* words, unsigned epoch, unsigned (&out)[N]) {
-    const int lane = lane_id();
-    unsigned mine = 0;
-    bool ready = false;
-    for (unsigned it = 0; it < kSpinLimit && !ready; ++it) {
-        bool ok = true;
-        if (lane < N) {
-            const unsigned long long v = slot_load(words + lane);
-            ok = static_cast<unsigned>(v) == epoch;
-            mine = static_cast<unsigned>(v >> 32);
-        }
-        ready = __all(ok);
-        if (!ready) __builtin_amdgcn_s_sleep(4);
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_readlane(mine, i);
-    return ready;
 }
 
 // Values that are equal in every lane (read by all lanes from one address, or
@@ -192,6 +165,9 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
     const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(v & 0xFFFFFFFFll));
     const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32));
     return static_cast<int64_t>((static_cast<uint64_t>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo));
+}
+__device__ __forceinline__ double uniform(double v) {
+    return __builtin_bit_cast(double, uniform(__builtin_bit_cast(int64_t, v)));
 }
 
 // ---------------------------------------------------------------- loads
@@ -262,45 +238,17 @@ __device__ __forceinline__ void online_step(const f4 (&x)[kVecs], int s, float c
     m = mn;
 }
 
-// (max, sum of e^{(x - max)/T}) of this wavefront's unit of one row.
-__device__ __forceinline__ void unit_reduce(float m, double acc, double invT64, float& M, double& Z) {
-    M = dpp_wave_max(m);
-    const double scaled = (acc > 0.0) ? acc * exp_nonpos_f64((static_cast<double>(m) - M) * invT64) : 0.0;
-    Z = dpp_wave_sum(scaled);
-}
-
 struct RowStats {
     float Mp, Mq;     // row maxima (logits)
     double Zp, Zq;    // sum of e^{(z - M)/T} over the row
 };
 
-// Combines the group's published unit statistics (identically in every wavefront).
-template <int kUPL>
-__device__ __forceinline__ RowStats combine_stats(const unsigned (&v)[kUPL][kStatSlots], int U, double invT64) {
-    float mp = -INFINITY, mq = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < kUPL; ++r) {
-        if (lane_id() + r * kWave < U) {
-            mp = fmaxf(mp, __builtin_bit_cast(float, v[r][0]));
-            mq = fmaxf(mq, __builtin_bit_cast(float, v[r][1]));
-        }
-    }
-    RowStats st;
-    st.Mp = dpp_wave_max(mp);
-    st.Mq = dpp_wave_max(mq);
-    double zp = 0.0, zq = 0.0;
-#pragma unroll
-    for (int r = 0; r < kUPL; ++r) {
-        const double a = join64(v[r][2], v[r][3]);
-        const double b = join64(v[r][4], v[r][5]);
-        const double ma = __builtin_bit_cast(float, v[r][0]);
-        const double mb = __builtin_bit_cast(float, v[r][1]);
-        zp += (a > 0.0) ? a * exp_nonpos_f64((ma - st.Mp) * invT64) : 0.0;
-        zq += (b > 0.0) ? b * exp_nonpos_f64((mb - st.Mq) * invT64) : 0.0;
-    }
-    st.Zp = dpp_wave_sum(zp);
-    st.Zq = dpp_wave_sum(zq);
-    return st;
+// Combines per-lane partials (M_i, Z_i), lanes without one holding (-inf, 0),
+// into (M, Z) of their union, identically in every wavefront that holds the same
+// partials in the same lanes.
+__device__ __forceinline__ void combine_pair(float m, double z, double invT64, float& M, double& Z) {
+    M = dpp_wave_max(m);
+    Z = dpp_wave_sum((z > 0.0) ? z * exp_nonpos_f64((static_cast<double>(m) - M) * invT64) : 0.0);
 }
 
 // ---------------------------------------------------------------- sampling weights
@@ -463,7 +411,10 @@ __device__ __forceinline__ void load_weights(bool two_rows, bool residual, const
 // ---------------------------------------------------------------- per-sequence pieces
 
 struct SeqCtx {
-    int b, u;
+    int b;
+    int u;                    // unit of this wavefront: q * kUnitWaves + wave
+    int q;                    // workgroup of the group
+    int wave;                 // wavefront of the workgroup
     unsigned epoch;
     const float* prow_base;   // target logits of the sequence, [k+1][V]
     const float* qrow_base;   // draft logits of the sequence, [k][V]
@@ -479,11 +430,74 @@ struct TokenLogits {
     double u_acc;      // the test's uniform, computed before the group's statistics arrive
 };
 
-__device__ __forceinline__ void flag_error(const RejectArgs& a, int b) {
-    if (lane_id() == 0) {
+// Workgroup-shared state: per-wavefront partials going to wave 0, and wave 0's
+// results going back to all eight wavefronts.
+struct UnitStat {
+    float Mp, Mq;
+    double Zp, Zq;
+};
+struct LevelRes {
+    unsigned flags;
+    float Mp, Mq;
+    double Zp, Zq;
+};
+struct SampRes {
+    int owner;         // wavefront holding the crossing unit, -1 if in another workgroup
+    unsigned flags;    // kSampUseP, kSampExact, kSampError
+    double run, t, Z1, Z2;
+};
+struct Shared {
+    LoadSums ls[kUnitWaves];
+    UnitStat unit[kUnitWaves];
+    double4 usum[kUnitWaves];
+    LevelRes res;
+    SampRes samp;
+};
+
+enum : unsigned { kResAccepted = 1u, kResError = 2u };
+enum : unsigned { kSampUseP = 1u, kSampExact = 2u, kSampError = 4u };
+
+__device__ __forceinline__ void flag_error(const RejectArgs& a, const SeqCtx& s) {
+    if (s.wave == 0 && lane_id() == 0) {
         __hip_atomic_fetch_or(a.ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.num_accepted[b] = -1;
+        a.num_accepted[s.b] = -1;
     }
+}
+
+// The first group to see all its workgroups' first slots records it; the last
+// of all groups stores this call's epoch for the next call. By then every
+// wavefront of the grid has read the epoch (each workgroup publishes only after
+// a barrier that follows its wavefronts' reads).
+__device__ __forceinline__ void count_group(const RejectArgs& a, const SeqCtx& s, bool& counted) {
+    if (counted) return;
+    counted = true;
+    if (lane_id() == 0) {
+        const unsigned n = __hip_atomic_fetch_add(a.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n + 1 == static_cast<unsigned>(a.groups)) {
+            __hip_atomic_store(a.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ctl + kCtlEpoch, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// The first lane with positive weight w whose running sum carry + (inclusive
+// prefix of w) exceeds t, and the running sum before it. If rounding leaves no
+// such lane, the last lane with positive weight (lane 0 if none) and exact = false.
+__device__ __forceinline__ int find_crossing(double w, double carry, double t, double& run, bool& exact) {
+    const double incl = dpp_wave_incl_scan(w);
+    const double excl = dpp_wave_shr1(incl);
+    const unsigned long long cross = __ballot(w > 0.0 && carry + incl > t);
+    const unsigned long long pos = __ballot(w > 0.0);
+    int l;
+    if (cross) {
+        l = __ffsll(static_cast<long long>(cross)) - 1;
+        exact = true;
+    } else {
+        l = pos ? 63 - __builtin_clzll(pos) : 0;
+        exact = false;
+    }
+    run = carry + __shfl(excl, l, kWave);
+    return l;
 }
 
 // Draw from the weights of this unit (residual of row `row`; p_row when `use_p` or
@@ -582,13 +596,35 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     a.num_accepted[b] = row;
 }
 
-// Sampling after the chain ended at `row` (residual of row `row` if kResidual,
-// else the bonus row p_k). `st` holds the chain statistics of that row.
-template <bool kVec4, bool kResidual, int kUPL>
+// Reads wave 0's sampling decision and runs the final scan in the owning
+// wavefront (every wavefront of the workgroup calls this after the barrier).
+__device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, const Shared& sh, bool& use_p,
+                                          bool& exact, double& run, double& t, double& Z1, double& Z2) {
+    const unsigned flags = static_cast<unsigned>(uniform(static_cast<int>(sh.samp.flags)));
+    if (flags & kSampError) {
+        flag_error(a, s);
+        return false;
+    }
+    if (uniform(sh.samp.owner) != s.wave) return false;
+    use_p = flags & kSampUseP;
+    exact = flags & kSampExact;
+    run = uniform(sh.samp.run);
+    t = uniform(sh.samp.t);
+    Z1 = uniform(sh.samp.Z1);
+    Z2 = uniform(sh.samp.Z2);
+    return true;
+}
+
+// Sampling from the residual of row `row` after its draft was rejected; `st`
+// holds the chain statistics of that row. Each wavefront turns its unit (still in
+// registers) into weights; wave 0 sums the workgroup's units, one exchange gives
+// it every workgroup's sums, it finds the crossing workgroup and, if that is its
+// own, the crossing unit, whose wavefront then scans it for the token.
+template <bool kVec4>
 __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s, int row, const f4 (&xp)[kVecs],
-                           const f4 (&xq)[kVecs], const RowStats& st, LoadSums& ls) {
+                                           const f4 (&xq)[kVecs], const RowStats& st, Shared& sh) {
     const float* prow = s.prow_base + size_t(row) * a.V;
-    const float* qrow = s.qrow_base + size_t(kResidual ? row : 0) * a.V;
+    const float* qrow = s.qrow_base + size_t(row) * a.V;
     SampleCtx c;
     c.Mp = st.Mp;
     c.Mq = st.Mq;
@@ -596,96 +632,74 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
     c.Mp64 = st.Mp;
     c.Mq64 = st.Mq;
     c.invT64 = a.invT64;
-    const double lzp = log(st.Zp), lzq = kResidual ? log(st.Zq) : 0.0;
+    const double lzp = log(st.Zp), lzq = log(st.Zq);
     c.hp = static_cast<float>(kLnTau + lzp);
     c.hq = static_cast<float>(kLnTau + lzq);
     c.dn = static_cast<float>(lzp - lzq);
 
-    const UnitSums us = unit_sums<kVec4, kResidual>(xp, xq, c, prow, qrow, s.u * kUnit + lane_id() * 4, ls);
-    unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
-    const unsigned pay[kSampSlots] = {hi32(us.A), lo32(us.A), hi32(us.B), lo32(us.B),
-                                      hi32(us.P), lo32(us.P), hi32(us.Q), lo32(us.Q)};
-    publish(slots + s.u, pay, s.epoch, a.U);
-    unsigned long long* res = a.samp_res + size_t(s.b) * kSampRes;
-    unsigned r[kSampRes];
-    if (s.u == 0) {
-        // unit 0 gathers the unit sums and finds the crossing unit for everyone
-        unsigned v[kUPL][kSampSlots];
-        const bool ok = gather<kSampSlots, kUPL>(slots, a.U, s.epoch, v);
-        double Au[kUPL], Bu[kUPL], Pu[kUPL], zp = 0.0, zq = 0.0;
-#pragma unroll
-        for (int q = 0; q < kUPL; ++q) {
-            Au[q] = join64(v[q][0], v[q][1]);
-            Bu[q] = join64(v[q][2], v[q][3]);
-            Pu[q] = join64(v[q][4], v[q][5]);
-            zp += Pu[q];
-            zq += join64(v[q][6], v[q][7]);
+    const int lane = lane_id();
+    const UnitSums us = unit_sums<kVec4, true>(xp, xq, c, prow, qrow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
+    if (lane == 0) sh.usum[s.wave] = make_double4(us.A, us.B, us.P, us.Q);
+    __syncthreads();
+    if (s.wave == 0) {
+        double Au = 0.0, Bu = 0.0, Pu = 0.0, Qu = 0.0;
+        if (lane < kUnitWaves) {
+            const double4 v = sh.usum[lane];
+            Au = v.x; Bu = v.y; Pu = v.z; Qu = v.w;
         }
-        const double Zp = dpp_wave_sum(zp);
-        const double Zq = kResidual ? dpp_wave_sum(zq) : 1.0;
-        const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
-        double Ru[kUPL], tot = 0.0;
-#pragma unroll
-        for (int q = 0; q < kUPL; ++q) {
-            Ru[q] = kResidual ? fmax(0.0, Au[q] * invZp - Bu[q] * invZq) : Pu[q];
-            tot += Ru[q];
-        }
-        double total = dpp_wave_sum(tot);
-        bool use_p = false;                   // the bonus row draws from its own a-weights
-        if (kResidual && !(total > 0.0)) {    // zero residual: draw from p_j instead
-            use_p = true;
-#pragma unroll
-            for (int q = 0; q < kUPL; ++q) Ru[q] = Pu[q];
-            total = Zp;
-        }
+        const double Aw = dpp_wave_sum(Au), Bw = dpp_wave_sum(Bu), Pw = dpp_wave_sum(Pu), Qw = dpp_wave_sum(Qu);
+        unsigned long long* slots = a.samp_slots + size_t(s.b) * a.Q * kSampSlots;
+        const unsigned pay[kSampSlots] = {hi32(Aw), lo32(Aw), hi32(Bw), lo32(Bw),
+                                          hi32(Pw), lo32(Pw), hi32(Qw), lo32(Qw)};
+        publish(slots + s.q, pay, s.epoch, a.Q);
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
-        const double t = u_smp * total;
-        // first unit with positive weight whose running sum exceeds t
-        int cstar = -1, clast = -1;
-        double carry = 0.0, run = 0.0;
-#pragma unroll
-        for (int q = 0; q < kUPL; ++q) {
-            const double incl = dpp_wave_incl_scan(Ru[q]);
-            const double excl = dpp_wave_shr1(incl);
-            const unsigned long long pos = __ballot(Ru[q] > 0.0);
-            if (pos) clast = q * kWave + 63 - __builtin_clzll(pos);
-            const unsigned long long cross = (cstar < 0) ? __ballot(Ru[q] > 0.0 && carry + incl > t) : 0ull;
-            if (cross) {
-                const int l0 = __ffsll(static_cast<long long>(cross)) - 1;
-                cstar = q * kWave + l0;
-                run = carry + __shfl(excl, l0, kWave);
-            }
-            carry += __shfl(incl, kWave - 1, kWave);
+        unsigned v[kSampSlots];
+        const bool ok = gather<kSampSlots>(slots, a.Q, s.epoch, v);
+        // lane l < Q: workgroup l's sums (zero in the other lanes)
+        const double Ag = join64(v[0], v[1]), Bg = join64(v[2], v[3]);
+        const double Pg = join64(v[4], v[5]), Qg = join64(v[6], v[7]);
+        const double Zp = dpp_wave_sum(Pg), Zq = dpp_wave_sum(Qg);
+        const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
+        double Rg = fmax(0.0, Ag * invZp - Bg * invZq);
+        double total = dpp_wave_sum(Rg);
+        bool use_p = false;
+        if (!(total > 0.0)) {      // zero residual: draw from p_j instead
+            use_p = true;
+            Rg = Pg;
+            total = Zp;
         }
-        const bool exact = cstar >= 0;
-        if (!exact) cstar = clast < 0 ? 0 : clast;
-        const unsigned flags = static_cast<unsigned>(cstar) | (use_p ? 1u << 20 : 0u) | (exact ? 1u << 21 : 0u) |
-                               (ok ? 0u : 1u << 22);
-        const unsigned out[kSampRes] = {flags, hi32(run), lo32(run), hi32(t), lo32(t), hi32(Zp), lo32(Zp),
-                                        hi32(Zq), lo32(Zq), 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        publish(res, out, s.epoch);
-#pragma unroll
-        for (int i = 0; i < kSampRes; ++i) r[i] = out[i];
-    } else if (!await_result<kSampRes>(res, s.epoch, r)) {
-        r[0] = 1u << 22;
+        const double t = u_smp * total;
+        double run;
+        bool exact;
+        const int qstar = find_crossing(Rg, 0.0, t, run, exact);
+        int owner = -1;
+        if (qstar == s.q) {        // the crossing workgroup: find the crossing unit
+            const double Ru = use_p ? Pu : fmax(0.0, Au * invZp - Bu * invZq);
+            bool exact_u;
+            owner = find_crossing(Ru, run, t, run, exact_u);
+            exact = exact && exact_u;
+        }
+        if (lane == 0) {
+            sh.samp.owner = owner;
+            sh.samp.flags = (use_p ? kSampUseP : 0u) | (exact ? kSampExact : 0u) | (ok ? 0u : kSampError);
+            sh.samp.run = run;
+            sh.samp.t = t;
+            sh.samp.Z1 = Zp;
+            sh.samp.Z2 = Zq;
+        }
     }
-    if (r[0] & (1u << 22)) {
-        flag_error(a, s.b);
-        return;
-    }
-    if (static_cast<int>(r[0] & 0xFFFFFu) != s.u) return;
-    const bool use_p = (r[0] >> 20) & 1u, exact = (r[0] >> 21) & 1u;
-    const double run = join64(r[1], r[2]), t = join64(r[3], r[4]);
-    const double Zp = join64(r[5], r[6]), Zq = join64(r[7], r[8]);
-    const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
-    final_scan<kVec4>(a, s, row, kResidual, prow, qrow, c, ls, use_p, exact, run, t, invZp, invZq, Zp, 1.0,
-                      c.Mp64);
+    __syncthreads();
+    bool use_p, exact;
+    double run, t, Zp, Zq;
+    if (!read_samp(a, s, sh, use_p, exact, run, t, Zp, Zq)) return;
+    final_scan<kVec4>(a, s, row, true, prow, qrow, c, sh.ls[s.wave], use_p, exact, run, t, 1.0 / Zp, 1.0 / Zq, Zp,
+                      1.0, c.Mp64);
 }
 
 // Acceptance test of draft j from the combined statistics and the draft token's
-// two logits (loaded while the group was exchanging statistics); unit 0 writes
-// the outputs of the test.
+// two logits (loaded while the group was exchanging statistics); workgroup 0
+// writes the outputs of the test.
 __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, int j, const RowStats& st,
                                             const TokenLogits& tl) {
     const int k = a.k, b = s.b;
@@ -696,7 +710,7 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
     }
     const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
     const bool accepted = uniform(static_cast<int>(tl.u_acc < ratio)) != 0;
-    if (s.u == 0 && lane_id() == 0) {
+    if (s.q == 0 && lane_id() == 0) {
         if (a.accept_probs) a.accept_probs[size_t(b) * k + j] = static_cast<float>(fmin(1.0, ratio));
         if (accepted) {
             a.out_tokens[size_t(b) * (k + 1) + j] = tl.tok;
@@ -706,83 +720,96 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
     return accepted;
 }
 
-enum : unsigned { kResAccepted = 1u, kResError = 2u };
-
-// Level `row` of the chain (rows p_row, q_row; or p_k alone for the bonus row):
-// this wavefront's unit statistics go to the group's slots; unit 0 gathers them,
-// combines them, takes the acceptance test (kTwo) and publishes one result record
-// that the other wavefronts wait on, so only one wavefront per group polls the
-// per-unit slots. Returns the result flags (kResAccepted, kResError).
-template <bool kVec4, bool kTwo, int kUPL>
+// Level `row` of the chain (rows p_row and q_row): every wavefront reduces its
+// unit, wave 0 combines the workgroup's eight, publishes the pair and gathers the
+// group's, combines those in workgroup order and takes the acceptance test; every
+// workgroup reaches the same decision from the same bits. Returns the result flags
+// (kResAccepted, kResError) and the row's statistics in `st`.
+template <bool kVec4>
 __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
-                                               f4 (&xq)[kVecs], RowStats& st, const TokenLogits& tok) {
+                                               f4 (&xq)[kVecs], RowStats& st, const TokenLogits& tok, Shared& sh,
+                                               bool& counted) {
     const float* prow = s.prow_base + size_t(row) * a.V;
-    const float* qrow = s.qrow_base + size_t(kTwo ? row : 0) * a.V;
-    // unit 0 takes the acceptance test: the draft token's two logits are loaded
+    const float* qrow = s.qrow_base + size_t(row) * a.V;
+    // wave 0 takes the acceptance test: the draft token's two logits are loaded
     // first, so they have long arrived when the group's statistics are in
     float ztp = 0.0f, ztq = 0.0f;
-    if (kTwo && s.u == 0 && tok.ok) {
+    if (s.wave == 0 && tok.ok) {
         ztp = prow[tok.tok];
         ztq = qrow[tok.tok];
     }
-    load_unit<kVec4, kTwo>(prow, qrow, a.V, s.u, xp, xq);
+    load_unit<kVec4, true>(prow, qrow, a.V, s.u, xp, xq);
     float mp = -INFINITY, mq = -INFINITY;
     double sp = 0.0, sq = 0.0;
 #pragma unroll
     for (int g = 0; g < kVecs / kStep; ++g) {
         online_step(xp, g, a.c2, mp, sp);
-        if (kTwo) online_step(xq, g, a.c2, mq, sq);
+        online_step(xq, g, a.c2, mq, sq);
     }
-    float Mp_u, Mq_u = -INFINITY;
-    double Zp_u, Zq_u = 0.0;
-    unit_reduce(mp, sp, a.invT64, Mp_u, Zp_u);
-    if (kTwo) unit_reduce(mq, sq, a.invT64, Mq_u, Zq_u);
-    const size_t level = size_t(s.b) * (a.k + 1) + row;
-    unsigned long long* slots = a.stat_slots + level * a.U * kStatSlots;
-    unsigned long long* res = a.stat_res + level * kStatRes;
-    const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_u), __builtin_bit_cast(unsigned, Mq_u),
-                                      hi32(Zp_u), lo32(Zp_u), hi32(Zq_u), lo32(Zq_u)};
-    publish(slots + s.u, pay, s.epoch, a.U);
-    if (s.u == 0) {
-        TokenLogits tl = tok;
-        if (kTwo) {
-            double u_smp;
-            verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &tl.u_acc, &u_smp);
+    {
+        float Mp_u, Mq_u;
+        double Zp_u, Zq_u;
+        combine_pair(mp, sp, a.invT64, Mp_u, Zp_u);
+        combine_pair(mq, sq, a.invT64, Mq_u, Zq_u);
+        if (lane_id() == 0) sh.unit[s.wave] = UnitStat{Mp_u, Mq_u, Zp_u, Zq_u};
+    }
+    __syncthreads();
+    if (s.wave == 0) {
+        const int lane = lane_id();
+        float mpw = -INFINITY, mqw = -INFINITY;
+        double zpw = 0.0, zqw = 0.0;
+        if (lane < kUnitWaves) {
+            const UnitStat u = sh.unit[lane];
+            mpw = u.Mp; mqw = u.Mq; zpw = u.Zp; zqw = u.Zq;
         }
-        unsigned v[kUPL][kStatSlots];
+        float Mp_w, Mq_w;
+        double Zp_w, Zq_w;
+        combine_pair(mpw, zpw, a.invT64, Mp_w, Zp_w);
+        combine_pair(mqw, zqw, a.invT64, Mq_w, Zq_w);
+        const size_t level = size_t(s.b) * (a.k + 1) + row;
+        unsigned long long* slots = a.stat_slots + level * a.Q * kStatSlots;
+        const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_w), __builtin_bit_cast(unsigned, Mq_w),
+                                          hi32(Zp_w), lo32(Zp_w), hi32(Zq_w), lo32(Zq_w)};
+        publish(slots + s.q, pay, s.epoch, a.Q);
+        TokenLogits tl = tok;
+        double u_smp;
+        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &tl.u_acc, &u_smp);
+        unsigned v[kStatSlots];
         unsigned flags = 0;
-        if (gather<kStatSlots, kUPL>(slots, a.U, s.epoch, v)) {
+        if (gather<kStatSlots>(slots, a.Q, s.epoch, v)) {
+            count_group(a, s, counted);
             tl.zp = uniform(ztp);
             tl.zq = uniform(ztq);
-            st = combine_stats<kUPL>(v, a.U, a.invT64);
-            if (kTwo && accept_test(a, s, row, st, tl)) flags |= kResAccepted;
+            const bool have = lane < a.Q;
+            combine_pair(have ? __builtin_bit_cast(float, v[0]) : -INFINITY, have ? join64(v[2], v[3]) : 0.0,
+                         a.invT64, st.Mp, st.Zp);
+            combine_pair(have ? __builtin_bit_cast(float, v[1]) : -INFINITY, have ? join64(v[4], v[5]) : 0.0,
+                         a.invT64, st.Mq, st.Zq);
+            if (accept_test(a, s, row, st, tl)) flags |= kResAccepted;
         } else {
+            count_group(a, s, counted);
             st.Mp = st.Mq = 0.0f;
             st.Zp = st.Zq = 1.0;
             flags |= kResError;
         }
-        const unsigned out[kStatRes] = {flags, __builtin_bit_cast(unsigned, st.Mp), __builtin_bit_cast(unsigned, st.Mq),
-                                        hi32(st.Zp), lo32(st.Zp), hi32(st.Zq), lo32(st.Zq), 0u};
-        publish(res, out, s.epoch);
-        return flags;
+        if (lane == 0) sh.res = LevelRes{flags, st.Mp, st.Mq, st.Zp, st.Zq};
     }
-    unsigned r[kStatRes];
-    if (!await_result<kStatRes>(res, s.epoch, r)) return kResError;
-    st.Mp = __builtin_bit_cast(float, r[1]);
-    st.Mq = __builtin_bit_cast(float, r[2]);
-    st.Zp = join64(r[3], r[4]);
-    st.Zq = join64(r[5], r[6]);
-    return r[0];
+    __syncthreads();
+    st.Mp = uniform(sh.res.Mp);
+    st.Mq = uniform(sh.res.Mq);
+    st.Zp = uniform(sh.res.Zp);
+    st.Zq = uniform(sh.res.Zq);
+    return static_cast<unsigned>(uniform(static_cast<int>(sh.res.flags)));
 }
 
-// The bonus row p_k after k acceptances, with one group exchange instead of two:
-// each wavefront weighs its unit against the unit's own maximum M_u (heavy logits
-// judged with the unit's own normaliser, a superset of the row's heavy set) and
-// publishes (sum of weights, M_u); unit 0 rescales the sums by e^{(M_u - M)/T},
-// finds the crossing unit and publishes it with the row's Z and M.
-template <bool kVec4, int kUPL>
+// The bonus row p_k after k acceptances, with one exchange: each wavefront weighs
+// its unit against the unit's own maximum M_u (heavy logits judged with the
+// unit's own normaliser, a superset of the row's heavy set); wave 0 rescales its
+// units to the workgroup maximum and publishes (sum, maximum); the gathered pairs
+// are rescaled to the row maximum M, which also gives the row's Z.
+template <bool kVec4>
 __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
-                                          LoadSums& ls) {
+                                          Shared& sh, bool& counted) {
     const int row = a.k;
     const float* prow = s.prow_base + size_t(row) * a.V;
     load_unit<kVec4, false>(prow, prow, a.V, s.u, xp, xq);
@@ -792,7 +819,7 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
     for (int g = 0; g < kVecs / kStep; ++g) online_step(xp, g, a.c2, m, acc);
     float Mu;
     double Zu;
-    unit_reduce(m, acc, a.invT64, Mu, Zu);
+    combine_pair(m, acc, a.invT64, Mu, Zu);
     SampleCtx c;
     c.Mp = Mu;
     c.Mq = 0.0f;
@@ -803,98 +830,88 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
     c.hp = static_cast<float>(kLnTau + log(Zu));
     c.hq = kLnTau;
     c.dn = 0.0f;
-    const UnitSums us = unit_sums<kVec4, false>(xp, xq, c, prow, prow, s.u * kUnit + lane_id() * 4, ls);
+    const int lane = lane_id();
+    const UnitSums us = unit_sums<kVec4, false>(xp, xq, c, prow, prow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
     const double Mu64 = Mu;
-    unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
-    const unsigned pay[kSampSlots] = {hi32(us.P), lo32(us.P), hi32(Mu64), lo32(Mu64), 0u, 0u, 0u, 0u};
-    publish(slots + s.u, pay, s.epoch, a.U);
-    unsigned long long* res = a.samp_res + size_t(s.b) * kSampRes;
-    unsigned r[kSampRes];
-    if (s.u == 0) {
-        unsigned v[kUPL][kSampSlots];
-        const bool ok = gather<kSampSlots, kUPL>(slots, a.U, s.epoch, v);
-        double Pu[kUPL], Mv[kUPL];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < kUPL; ++q) {
-            const bool valid = lane_id() + q * kWave < a.U;
-            Pu[q] = valid ? join64(v[q][0], v[q][1]) : 0.0;
-            Mv[q] = valid ? join64(v[q][2], v[q][3]) : -INFINITY;
-            mloc = fmaxf(mloc, static_cast<float>(Mv[q]));
+    if (lane == 0) sh.usum[s.wave] = make_double4(us.P, Mu64, 0.0, 0.0);
+    __syncthreads();
+    if (s.wave == 0) {
+        double Pu = 0.0, Mv = -INFINITY;
+        if (lane < kUnitWaves) {
+            const double4 v = sh.usum[lane];
+            Pu = v.x;
+            Mv = v.y;
         }
-        const double M = dpp_wave_max(mloc);
-        double Wu[kUPL], tot = 0.0;
-#pragma unroll
-        for (int q = 0; q < kUPL; ++q) {
-            Wu[q] = (Pu[q] > 0.0) ? Pu[q] * exp_nonpos_f64((Mv[q] - M) * a.invT64) : 0.0;
-            tot += Wu[q];
-        }
-        const double Z = dpp_wave_sum(tot);
+        const double Mw = dpp_wave_max(static_cast<float>(Mv));
+        const double Ww = dpp_wave_sum((Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - Mw) * a.invT64) : 0.0);
+        unsigned long long* slots = a.samp_slots + size_t(s.b) * a.Q * kSampSlots;
+        const unsigned pay[4] = {hi32(Ww), lo32(Ww), hi32(Mw), lo32(Mw)};
+        publish(slots + s.q, pay, s.epoch, a.Q);
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
+        unsigned v[4];
+        const bool ok = gather<4>(slots, a.Q, s.epoch, v);
+        count_group(a, s, counted);
+        const bool have = lane < a.Q;
+        const double Wg = have ? join64(v[0], v[1]) : 0.0;
+        const double Mg = have ? join64(v[2], v[3]) : -INFINITY;
+        const double M = dpp_wave_max(static_cast<float>(Mg));
+        const double Wr = (Wg > 0.0) ? Wg * exp_nonpos_f64((Mg - M) * a.invT64) : 0.0;
+        const double Z = dpp_wave_sum(Wr);
         const double t = u_smp * Z;
-        int cstar = -1, clast = -1;
-        double carry = 0.0, run = 0.0;
-#pragma unroll
-        for (int q = 0; q < kUPL; ++q) {
-            const double incl = dpp_wave_incl_scan(Wu[q]);
-            const double excl = dpp_wave_shr1(incl);
-            const unsigned long long pos = __ballot(Wu[q] > 0.0);
-            if (pos) clast = q * kWave + 63 - __builtin_clzll(pos);
-            const unsigned long long cross = (cstar < 0) ? __ballot(Wu[q] > 0.0 && carry + incl > t) : 0ull;
-            if (cross) {
-                const int l0 = __ffsll(static_cast<long long>(cross)) - 1;
-                cstar = q * kWave + l0;
-                run = carry + __shfl(excl, l0, kWave);
-            }
-            carry += __shfl(incl, kWave - 1, kWave);
+        double run;
+        bool exact;
+        const int qstar = find_crossing(Wr, 0.0, t, run, exact);
+        int owner = -1;
+        if (qstar == s.q) {
+            const double Wu = (Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - M) * a.invT64) : 0.0;
+            bool exact_u;
+            owner = find_crossing(Wu, run, t, run, exact_u);
+            exact = exact && exact_u;
         }
-        const bool exact = cstar >= 0;
-        if (!exact) cstar = clast < 0 ? 0 : clast;
-        const unsigned flags = static_cast<unsigned>(cstar) | (exact ? 1u << 21 : 0u) | (ok ? 0u : 1u << 22);
-        const unsigned out[kSampRes] = {flags, hi32(run), lo32(run), hi32(t), lo32(t), hi32(Z), lo32(Z),
-                                        hi32(M), lo32(M), 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        publish(res, out, s.epoch);
-#pragma unroll
-        for (int i = 0; i < kSampRes; ++i) r[i] = out[i];
-    } else if (!await_result<kSampRes>(res, s.epoch, r)) {
-        r[0] = 1u << 22;
+        if (lane == 0) {
+            sh.samp.owner = owner;
+            sh.samp.flags = (exact ? kSampExact : 0u) | (ok ? 0u : kSampError);
+            sh.samp.run = run;
+            sh.samp.t = t;
+            sh.samp.Z1 = Z;
+            sh.samp.Z2 = M;
+        }
     }
-    if (r[0] & (1u << 22)) {
-        flag_error(a, s.b);
-        return;
-    }
-    if (static_cast<int>(r[0] & 0xFFFFFu) != s.u) return;
-    const bool exact = (r[0] >> 21) & 1u;
-    const double run = join64(r[1], r[2]), t = join64(r[3], r[4]);
-    const double Z = join64(r[5], r[6]), M = join64(r[7], r[8]);
+    __syncthreads();
+    bool use_p, exact;
+    double run, t, Z, M;
+    if (!read_samp(a, s, sh, use_p, exact, run, t, Z, M)) return;
     const double wscale = exp_nonpos_f64((Mu64 - M) * a.invT64);
-    final_scan<kVec4>(a, s, row, false, prow, prow, c, ls, false, exact, run, t, 1.0 / Z, 1.0, Z, wscale, M);
+    final_scan<kVec4>(a, s, row, false, prow, prow, c, sh.ls[s.wave], false, exact, run, t, 1.0 / Z, 1.0, Z, wscale,
+                      M);
 }
 
-template <bool kVec4, int kUPL>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
+template <bool kVec4>
+__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
     // Workgroups go to the eight XCDs round-robin; with a multiple of eight groups,
-    // group g takes the U waves on XCD g % 8 (they start together and share an
-    // L2). Any other count uses the plain mapping. Both are bijections.
+    // group g takes the Q workgroups on XCD g % 8 (they start together and share
+    // an L2). Any other count uses the plain mapping. Both are bijections.
     const int w = blockIdx.x;
-    int group, unit;
+    int group, q;
     if (a.groups % 8 == 0) {
         const int l = w / 8;
-        group = (w % 8) + 8 * (l / a.U);
-        unit = l % a.U;
+        group = (w % 8) + 8 * (l / a.Q);
+        q = l % a.Q;
     } else {
-        group = w / a.U;
-        unit = w % a.U;
+        group = w / a.Q;
+        q = w % a.Q;
     }
     SeqCtx s;
-    s.u = unit;
+    s.q = q;
+    s.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    s.u = q * kUnitWaves + s.wave;
     {
         const unsigned last = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s.epoch = (last + 1u == 0u) ? 1u : last + 1u;
     }
-    bool counted = s.u != 0;
-    __shared__ LoadSums ls;
+    bool counted = q != 0;   // workgroup 0's wave 0 counts the group
+    __shared__ Shared sh;
     f4 xp[kVecs], xq[kVecs];
     for (int b = group; b < a.B; b += a.groups) {
         s.b = b;
@@ -915,60 +932,46 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             tl.ok = tl.tok >= 0 && tl.tok < a.V;
             tl.zp = tl.zq = 0.0f;
             tl.u_acc = 0.0;
-            const unsigned res = level_step<kVec4, true, kUPL>(a, s, j, xp, xq, st, tl);
-            if (!counted) {
-                // every wavefront of the group has published (so has read the epoch)
-                // once unit 0's first gather is through; the last group to get there
-                // records the epoch for the next call
-                counted = true;
-                if (lane == 0) {
-                    const unsigned n = __hip_atomic_fetch_add(a.ctl + kCtlDone, 1u, __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT);
-                    if (n + 1 == static_cast<unsigned>(a.groups)) {
-                        __hip_atomic_store(a.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(a.ctl + kCtlEpoch, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-            }
+            const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, tl, sh, counted);
             if (res & kResError) {
-                flag_error(a, b);
+                flag_error(a, s);
                 done = true;
             } else if (!(res & kResAccepted)) {
-                sample_row<kVec4, true, kUPL>(a, s, j, xp, xq, st, ls);
+                sample_row<kVec4>(a, s, j, xp, xq, st, sh);
                 done = true;
             }
         }
         if (done) continue;
-        bonus_row<kVec4, kUPL>(a, s, xp, xq, ls);
+        bonus_row<kVec4>(a, s, xp, xq, sh, counted);
     }
 }
 
-template <bool kVec4, int kUPL>
-hipError_t co_resident(int dev, int* waves) {
+template <bool kVec4>
+hipError_t co_resident(int dev, int* wgs) {
     static int memo[64];
     if (dev >= 0 && dev < 64 && memo[dev] > 0) {
-        *waves = memo[dev];
+        *wgs = memo[dev];
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4, kUPL>, kWave, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4>, kRT, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    *waves = per_cu * cus;
-    if (dev >= 0 && dev < 64) memo[dev] = *waves;
+    *wgs = per_cu * cus;
+    if (dev >= 0 && dev < 64) memo[dev] = *wgs;
     return hipSuccess;
 }
 
-template <bool kVec4, int kUPL>
+template <bool kVec4>
 hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int waves = 0;
-    e = co_resident<kVec4, kUPL>(dev, &waves);
+    int wgs = 0;
+    e = co_resident<kVec4>(dev, &wgs);
     if (e != hipSuccess) return e;
-    int groups = min(a.B, waves / a.U);
+    int groups = min(a.B, wgs / a.Q);
     if (groups < 1) return hipErrorInvalidConfiguration;
     if (groups > 8) groups -= groups % 8;   // a multiple of 8 (one XCD per group); rounds take the rest
     a.groups = groups;
@@ -977,7 +980,7 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     // cooperative launch would guarantee it, at ~13 us of extra launch latency
     // per call on this stack; should residency ever be partial, the waits are
     // bounded and the affected sequences report an error instead of hanging.)
-    hipLaunchKernelGGL((reject_kernel<kVec4, kUPL>), dim3(groups * a.U), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL((reject_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -985,15 +988,17 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
 
 size_t reject_workspace_bytes(int B, int k, int V) {
     const int U = (V + kUnit - 1) / kUnit;
-    return reject_layout(B, k, U).total;
+    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
+    return reject_layout(B, k, Q).total;
 }
 
-int reject_max_vocab() { return kUnit * kWave * kMaxUnitsPerLane; }
+int reject_max_vocab() { return kUnit * kUnitWaves * kMaxQ; }
 
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
-    if (U > kWave * kMaxUnitsPerLane) return hipErrorInvalidValue;
-    const RejectLayout lay = reject_layout(p.B, p.k, U);
+    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
+    if (Q > kMaxQ) return hipErrorInvalidValue;
+    const RejectLayout lay = reject_layout(p.B, p.k, Q);
     char* ws = static_cast<char*>(p.workspace);
     RejectArgs a;
     a.target = p.target_logits;
@@ -1008,16 +1013,12 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.ctl = reinterpret_cast<unsigned*>(ws + lay.ctl);
     a.stat_slots = reinterpret_cast<unsigned long long*>(ws + lay.stat);
     a.samp_slots = reinterpret_cast<unsigned long long*>(ws + lay.samp);
-    a.stat_res = reinterpret_cast<unsigned long long*>(ws + lay.stat_res);
-    a.samp_res = reinterpret_cast<unsigned long long*>(ws + lay.samp_res);
-    a.B = p.B; a.k = p.k; a.V = p.V; a.U = U; a.groups = 0;
+    a.B = p.B; a.k = p.k; a.V = p.V; a.U = U; a.Q = Q; a.groups = 0;
     a.invT = 1.0f / p.temperature;
     a.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(p.temperature));
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.seed = p.seed;
-    const bool vec4 = (p.V % 4) == 0;
-    if (U <= kWave) return vec4 ? launch_variant<true, 1>(a, stream) : launch_variant<false, 1>(a, stream);
-    return vec4 ? launch_variant<true, kMaxUnitsPerLane>(a, stream) : launch_variant<false, kMaxUnitsPerLane>(a, stream);
+    return (p.V % 4) == 0 ? launch_variant<true>(a, stream) : launch_variant<false>(a, stream);
 }
 
 }  // namespace specverify
