@@ -78,6 +78,7 @@ struct RejectArgs {
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
     double invT64;
+    float T;
     uint64_t seed;
 };
 
@@ -170,43 +171,70 @@ __device__ __forceinline__ double uniform(double v) {
     return __builtin_bit_cast(double, uniform(__builtin_bit_cast(int64_t, v)));
 }
 
+// Element i of a read-only input at a wave-uniform address, through the constant
+// address space: a scalar load, counted apart from the vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p, size_t i) {
+    typedef const __attribute__((address_space(4))) T CT;
+    return ((CT*)p)[i];
+}
+
 // ---------------------------------------------------------------- loads
 
-// Four consecutive logits from x (x a multiple of 4 when kVec4), -inf past the
-// row. Lanes past the row issue no load (loads of one clamped address from many
-// lanes and waves serialise in the memory pipeline).
+// Logits rows are read through buffer resources: a load at an offset past the
+// row's V * 4 bytes returns zero without touching memory, so every lane loads
+// unconditionally. Without per-lane branches around the loads the compiler counts
+// the loads in flight exactly and can start on the first ones as they arrive.
+constexpr int kRsrcFlags = 0x00020000;   // raw 32-bit data, no swizzle
+constexpr int kNonTemporal = 2;          // streamed once: do not keep in the caches
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int V) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), static_cast<short>(0), V * 4, kRsrcFlags);
+}
+
+// Four consecutive logits from x (x a multiple of 4 when kVec4), without padding.
 template <bool kVec4>
-__device__ __forceinline__ f4 load4(const float* row, int V, int x) {
-    f4 f = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (kVec4) {
-        if (x < V) f = __builtin_nontemporal_load(reinterpret_cast<const f4*>(row + x));
-    } else {
+__device__ __forceinline__ f4 load4_raw(__amdgpu_buffer_rsrc_t r, int x) {
+    if (kVec4) return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, x * 4, 0, kNonTemporal));
+    f4 f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (x + c < V) f[c] = __builtin_nontemporal_load(row + x + c);
-    }
+    for (int c = 0; c < 4; ++c)
+        f[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (x + c) * 4, 0, kNonTemporal));
+    return f;
+}
+
+// -inf for the logits of f (from x) at or past V.
+__device__ __forceinline__ void pad4(f4& f, int x, int V) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (x + c >= V) f[c] = -INFINITY;
+}
+
+template <bool kVec4>
+__device__ __forceinline__ f4 load4(__amdgpu_buffer_rsrc_t r, int V, int x) {
+    f4 f = load4_raw<kVec4>(r, x);
+    pad4(f, x, V);
     return f;
 }
 
 // Element (i, c) of lane l in unit u is logit u*4096 + i*256 + 4*l + c: each load
 // of a wavefront is one contiguous 1 KB run. p and q loads are interleaved so the
 // online softmax can start on the first step while the rest are in flight. Only
-// the last unit of a row can reach past V; the others load without bounds tests.
+// the last unit of a row can reach past V; its padding is set after the loads.
 template <bool kVec4, bool kTwo>
-__device__ __forceinline__ void load_unit(const float* prow, const float* qrow, int V, int u,
+__device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq, int V, int u,
                                           f4 (&xp)[kVecs], f4 (&xq)[kVecs]) {
     const int base = u * kUnit + lane_id() * 4;
-    if (kVec4 && (u + 1) * kUnit <= V) {
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+        xp[i] = load4_raw<kVec4>(rp, base + i * (kWave * 4));
+        if (kTwo) xq[i] = load4_raw<kVec4>(rq, base + i * (kWave * 4));
+    }
+    if ((u + 1) * kUnit > V) {   // uniform
 #pragma unroll
         for (int i = 0; i < kVecs; ++i) {
-            xp[i] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(prow + base + i * (kWave * 4)));
-            if (kTwo) xq[i] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(qrow + base + i * (kWave * 4)));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kVecs; ++i) {
-            xp[i] = load4<kVec4>(prow, V, base + i * (kWave * 4));
-            if (kTwo) xq[i] = load4<kVec4>(qrow, V, base + i * (kWave * 4));
+            pad4(xp[i], base + i * (kWave * 4), V);
+            if (kTwo) pad4(xq[i], base + i * (kWave * 4), V);
         }
     }
 }
@@ -214,23 +242,30 @@ __device__ __forceinline__ void load_unit(const float* prow, const float* qrow, 
 // ---------------------------------------------------------------- chain statistics
 
 // One online-softmax step over loads 4s..4s+3 of this lane: running max m and
-// running sum s of e^{(x - m)/T}, the exps as hardware exp2 of (x - m) * log2(e)/T.
+// running sum s of e^{(x - m)/T}, the exps as hardware exp2 of x * log2(e)/T -
+// m * log2(e)/T. (The chain only needs relative accuracy well below 1e-6: the
+// statistics feed the acceptance ratio and the classification thresholds, never
+// the sampling weights themselves.)
 __device__ __forceinline__ void online_step(const f4 (&x)[kVecs], int s, float c2, float& m, double& acc) {
+    // maximum() rather than fmaxf(): the inputs are never NaN, and it takes loaded
+    // values without a canonicalising instruction each (three-input form on gfx950)
     float gm = -INFINITY;
 #pragma unroll
     for (int i = kStep * s; i < kStep * s + kStep; ++i)
-        gm = fmaxf(gm, fmaxf(fmaxf(x[i].x, x[i].y), fmaxf(x[i].z, x[i].w)));
-    const float mn = fmaxf(m, gm);
+        gm = __builtin_elementwise_maximum(gm, __builtin_elementwise_maximum(
+                 __builtin_elementwise_maximum(x[i].x, x[i].y), __builtin_elementwise_maximum(x[i].z, x[i].w)));
+    const float mn = __builtin_elementwise_maximum(m, gm);
     const float ref = (mn == -INFINITY) ? 0.0f : mn;   // all -inf so far: every term is 0
-    const float rescale = __builtin_amdgcn_exp2f((m - ref) * c2);
+    const float nr = -ref * c2;                        // exps as exp2(x * c2 - ref * c2), one fma each
+    const float rescale = __builtin_amdgcn_exp2f(fmaf(m, c2, nr));
     float part[kStep];
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
         const f4 v = x[kStep * s + i];
-        const float e0 = __builtin_amdgcn_exp2f((v.x - ref) * c2);
-        const float e1 = __builtin_amdgcn_exp2f((v.y - ref) * c2);
-        const float e2 = __builtin_amdgcn_exp2f((v.z - ref) * c2);
-        const float e3 = __builtin_amdgcn_exp2f((v.w - ref) * c2);
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(v.x, c2, nr));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(v.y, c2, nr));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(v.z, c2, nr));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(v.w, c2, nr));
         part[i] = (e0 + e1) + (e2 + e3);
     }
     const float sum = (part[0] + part[1]) + (part[2] + part[3]);
@@ -255,72 +290,140 @@ __device__ __forceinline__ void combine_pair(float m, double z, double invT64, f
 
 struct SampleCtx {
     float Mp, Mq, invT;
-    float hp, hq;        // ln(tau * Z): log-weights above these are taken in fp64
+    float tp, tq;        // heavy thresholds on the raw logits (probability above tau)
     float dn;            // ln Z_p - ln Z_q: x in the residual support iff lp - lq > dn
     double Mp64, Mq64, invT64;
 };
+
+// ln Z from the hardware log2 (a few ulp): it only places the heavy thresholds and
+// the support boundary, where any consistent value is correct and an error of
+// 1e-7 moves only logits whose weight is that small.
+__device__ __forceinline__ float ln_approx(double Z) {
+    return __builtin_amdgcn_logf(static_cast<float>(Z)) * 0.693147180559945f;
+}
+
+// Raw-logit threshold above which a logit's probability under (M, Z) exceeds tau:
+// p > tau  <=>  z > M + T (ln tau + ln Z). Monotone, so one compare per logit;
+// only its consistency matters (every site classifies with the same float).
+__device__ __forceinline__ float heavy_threshold(float M, double Z, float T) {
+    return fmaf(T, static_cast<float>(kLnTau) + ln_approx(Z), M);
+}
 
 // Log-weight of a logit in nats, (z - M) / T, and the residual-support test. The
 // operations are written with the no-contraction intrinsics so that every call
 // site rounds identically (the support must be the same set wherever it is judged).
 __device__ __forceinline__ float log_weight(float z, float M, float invT) { return __fmul_rn(__fsub_rn(z, M), invT); }
 __device__ __forceinline__ bool in_support(float xp, float xq, float dn) { return __fsub_rn(xp, xq) > dn; }
+// Heavy test as a sign bit: t - z < 0 exactly when z > t (the difference of two
+// distinct floats is never zero), so the bit is set iff z_p > t_p or z_q > t_q.
+// Kept in a vector register rather than as a lane mask, so that the 64 tests of a
+// unit can be packed into bits without tying up scalar registers. -inf padding is
+// never heavy.
+__device__ __forceinline__ unsigned heavy_sign(bool residual, float zp, float zq, const SampleCtx& c) {
+    const float d = residual ? fminf(c.tp - zp, c.tq - zq) : c.tp - zp;
+    return __builtin_bit_cast(unsigned, d);
+}
+__device__ __forceinline__ bool is_heavy(bool residual, float zp, float zq, const SampleCtx& c) {
+    return static_cast<int>(heavy_sign(residual, zp, zq, c)) < 0;
+}
 
 // Light part of the unnormalised weights a = e^{(z_p - M_p)/T}, b = e^{(z_q - M_q)/T}
 // of the four logits of one load: compensated fp32 exps, zeroed (by a product, so
-// the exp is never moved into a branch) for heavy logits, whose probability under
-// the chain's normalisers exceeds tau. Their bits are set in `hmask` (bit 4*i + e)
-// and they are taken in fp64 by heavy_pass. Membership of the residual support
-// {p > q} is judged with the chain's normalisers.
-__device__ __forceinline__ void light_weights(bool residual, const f4& vp, const f4& vq, const SampleCtx& c, int i,
-                                              float (&la)[4], float (&lb)[4], bool (&in_s)[4],
-                                              unsigned long long& hmask) {
+// the exp is never moved into a branch) for heavy logits, which are taken in fp64
+// separately. Membership of the residual support {p > q} is judged with the
+// chain's normalisers.
+__device__ __forceinline__ void light_weights(bool residual, const f4& vp, const f4& vq, const SampleCtx& c,
+                                              float (&la)[4], float (&lb)[4], bool (&in_s)[4], bool (&h)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float xp = log_weight(vp[e], c.Mp, c.invT);
         const float xq = residual ? log_weight(vq[e], c.Mq, c.invT) : -INFINITY;
-        const bool h = (xp > c.hp) || (xq > c.hq);   // xq = -inf never passes
+        h[e] = is_heavy(residual, vp[e], vq[e], c);
         in_s[e] = residual ? in_support(xp, xq, c.dn) : true;   // NaN for padding: not in the support
-        const float keep = h ? 0.0f : 1.0f;
+        const float keep = h[e] ? 0.0f : 1.0f;
         la[e] = exp_small_f32(xp) * keep;
         lb[e] = residual ? exp_small_f32(xq) * keep : 0.0f;
-        hmask |= static_cast<unsigned long long>(h) << (4 * i + e);
     }
 }
 
-// fp64 weights of this lane's heavy logits. They are re-read from memory (four
-// per lane per round trip; there are few, typically 0..4 per lane) rather than
-// picked out of the register arrays, which would need dynamic indexing and
-// force the arrays out of registers. `f` receives (load index, a, b, in support)
-// for each; the trip count is the largest per-lane count in the wavefront.
-template <bool kVec4, typename F>
-__device__ __forceinline__ void heavy_pass(bool residual, const float* prow, const float* qrow, int base,
-                                           const SampleCtx& c, unsigned long long hmask, F&& f) {
-    while (__any(hmask != 0ull)) {
-        int idx[4];
-        bool has[4];
-        float zp[4], zq[4];
+// The lane's heavy logits as two 32-bit masks: element k = 4i + e of the unit
+// (load i, component e) is bit 31 - k of lo for k < 32 and bit 63 - k of hi
+// otherwise (each mask is built by shifting in one bit per element).
+struct HeavyBits {
+    unsigned lo, hi;
+};
+
+__device__ __forceinline__ HeavyBits heavy_bits(bool residual, const f4 (&xp)[kVecs], const f4 (&xq)[kVecs],
+                                                const SampleCtx& c) {
+    HeavyBits hb{0u, 0u};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            has[r] = hmask != 0ull;
-            idx[r] = has[r] ? __builtin_ctzll(hmask) : 0;
-            hmask &= has[r] ? hmask - 1 : hmask;
-        }
+    for (int i = 0; i < kVecs; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // heavy logits are never padding (-inf), so x < V; lanes without one read logit 0
-            const int x = has[r] ? base + (idx[r] >> 2) * (kWave * 4) + (idx[r] & 3) : 0;
-            zp[r] = prow[x];
-            zq[r] = residual ? qrow[x] : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+            // (mask << 1) | sign bit, one funnel shift
+            const unsigned d = heavy_sign(residual, xp[i][e], residual ? xq[i][e] : -INFINITY, c);
+            if (i < kVecs / 2) hb.lo = __builtin_amdgcn_alignbit(hb.lo, d, 31u);
+            else hb.hi = __builtin_amdgcn_alignbit(hb.hi, d, 31u);
         }
+    }
+    return hb;
+}
+
+// Takes one heavy element off the masks: its index k in the unit, or -1.
+__device__ __forceinline__ int take_heavy(HeavyBits& hb) {
+    if (hb.lo != 0u) {
+        const int p = __builtin_ctz(hb.lo);
+        hb.lo &= hb.lo - 1u;
+        return 31 - p;
+    }
+    if (hb.hi != 0u) {
+        const int p = __builtin_ctz(hb.hi);
+        hb.hi &= hb.hi - 1u;
+        return 63 - p;
+    }
+    return -1;
+}
+
+// Up to four heavy logits of the lane, re-read from memory (rather than picked out
+// of the register arrays, which would need dynamic indexing and force the arrays
+// out of registers). Issued before the light pass so that the loads are in by the
+// time they are weighed.
+struct HeavyRound {
+    unsigned ks;         // element index in the unit per byte (0xFF: none)
+    float zp[4], zq[4];
+};
+
+__device__ __forceinline__ int round_k(const HeavyRound& r, int j) {
+    const unsigned b = (r.ks >> (8 * j)) & 0xFFu;
+    return b == 0xFFu ? -1 : static_cast<int>(b);
+}
+
+__device__ __forceinline__ void heavy_fetch(bool residual, const float* prow, const float* qrow, int base,
+                                            HeavyBits& hb, HeavyRound& r) {
+    r.ks = 0u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const double va = exp_nonpos_f64((static_cast<double>(zp[r]) - c.Mp64) * c.invT64);
-            const double vb = residual ? exp_nonpos_f64((static_cast<double>(zq[r]) - c.Mq64) * c.invT64) : 0.0;
-            const bool ins = residual
-                ? in_support(log_weight(zp[r], c.Mp, c.invT), log_weight(zq[r], c.Mq, c.invT), c.dn) : true;
-            if (has[r]) f(idx[r] >> 2, va, vb, ins);
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int k = take_heavy(hb);
+        r.ks |= static_cast<unsigned>(k & 0xFF) << (8 * j);
+        // heavy logits are never padding (-inf), so x < V; lanes without one read logit 0
+        const int x = k >= 0 ? base + (k >> 2) * (kWave * 4) + (k & 3) : 0;
+        r.zp[j] = prow[x];
+        r.zq[j] = residual ? qrow[x] : -INFINITY;
+    }
+}
+
+// fp64 weights of one round of heavy logits; `f` receives (load index, a, b, in
+// support) for each.
+template <typename F>
+__device__ __forceinline__ void heavy_weigh(bool residual, const SampleCtx& c, const HeavyRound& r, F&& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double va = exp_nonpos_f64((static_cast<double>(r.zp[j]) - c.Mp64) * c.invT64);
+        const double vb = residual ? exp_nonpos_f64((static_cast<double>(r.zq[j]) - c.Mq64) * c.invT64) : 0.0;
+        const bool ins = residual
+            ? in_support(log_weight(r.zp[j], c.Mp, c.invT), log_weight(r.zq[j], c.Mq, c.invT), c.dn) : true;
+        const int k = round_k(r, j);
+        if (k >= 0) f(k >> 2, va, vb, ins);
     }
 }
 
@@ -333,18 +436,22 @@ struct UnitSums {
 // bonus row only the a-sums are meaningful.
 typedef double2 LoadSums[kVecs][kWave];
 
-// Unit sums of the sampling weights and, in `ls`, the per-load sums.
+// Unit sums of the sampling weights and, in `ls`, the per-load sums. The heavy
+// logits are found first and their re-reads issued; the light pass over the
+// registers then hides the loads' latency.
 template <bool kVec4, bool kResidual>
 __device__ __forceinline__ UnitSums unit_sums(const f4 (&xp)[kVecs], const f4 (&xq)[kVecs], const SampleCtx& c,
                                               const float* prow, const float* qrow, int base, LoadSums& ls) {
     const int lane = lane_id();
+    HeavyBits hb = heavy_bits(kResidual, xp, xq, c);
+    HeavyRound hr;
+    heavy_fetch(kResidual, prow, qrow, base, hb, hr);
     double A = 0.0, Bs = 0.0, P = 0.0, Q = 0.0;
-    unsigned long long hmask = 0ull;
 #pragma unroll
     for (int i = 0; i < kVecs; ++i) {
         float la[4], lb[4];
-        bool in_s[4];
-        light_weights(kResidual, xp[i], xq[i], c, i, la, lb, in_s, hmask);
+        bool in_s[4], h[4];
+        light_weights(kResidual, xp[i], xq[i], c, la, lb, in_s, h);
         float fa = 0.0f, fb = 0.0f, fp = 0.0f, fq = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -363,7 +470,7 @@ __device__ __forceinline__ UnitSums unit_sums(const f4 (&xp)[kVecs], const f4 (&
         }
         ls[i][lane] = make_double2(fa, fb);
     }
-    heavy_pass<kVec4>(kResidual, prow, qrow, base, c, hmask, [&](int i, double va, double vb, bool ins) {
+    auto add = [&](int i, double va, double vb, bool ins) {
         P += va;
         A += ins ? va : 0.0;
         double2 g = ls[i][lane];
@@ -374,7 +481,12 @@ __device__ __forceinline__ UnitSums unit_sums(const f4 (&xp)[kVecs], const f4 (&
             g.y += ins ? vb : 0.0;
         }
         ls[i][lane] = g;
-    });
+    };
+    heavy_weigh(kResidual, c, hr, add);
+    while (__any((hb.lo | hb.hi) != 0u)) {   // lanes with more than four (rare)
+        heavy_fetch(kResidual, prow, qrow, base, hb, hr);
+        heavy_weigh(kResidual, c, hr, add);
+    }
     UnitSums s;
     s.A = dpp_wave_sum(A);
     s.P = dpp_wave_sum(P);
@@ -395,15 +507,13 @@ __device__ __forceinline__ double sample_weight(bool residual, bool in_s, double
 __device__ __forceinline__ void load_weights(bool two_rows, bool residual, const f4& vp, const f4& vq,
                                              const SampleCtx& c, double invZp, double invZq, double (&w)[4]) {
     float la[4], lb[4];
-    bool in_s[4];
-    unsigned long long hm = 0ull;
-    light_weights(two_rows, vp, vq, c, 0, la, lb, in_s, hm);
+    bool in_s[4], h[4];
+    light_weights(two_rows, vp, vq, c, la, lb, in_s, h);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const bool heavy = (hm >> e) & 1ull;
-        const double va = heavy ? exp_nonpos_f64((static_cast<double>(vp[e]) - c.Mp64) * c.invT64) : la[e];
-        const double vb = (heavy && two_rows) ? exp_nonpos_f64((static_cast<double>(vq[e]) - c.Mq64) * c.invT64)
-                                              : lb[e];
+        const double va = h[e] ? exp_nonpos_f64((static_cast<double>(vp[e]) - c.Mp64) * c.invT64) : la[e];
+        const double vb = (h[e] && two_rows) ? exp_nonpos_f64((static_cast<double>(vq[e]) - c.Mq64) * c.invT64)
+                                             : lb[e];
         w[e] = sample_weight(residual, in_s[e], va, vb, invZp, invZq);
     }
 }
@@ -502,8 +612,9 @@ __device__ __forceinline__ int find_crossing(double w, double carry, double t, d
 
 // Draw from the weights of this unit (residual of row `row`; p_row when `use_p` or
 // for the bonus row), given the running sum `run` before this unit and the
-// target t. Only the wavefront owning the crossing unit calls this; lane 0 writes
-// the token, its probability and the padding of the sequence's outputs.
+// target t. Only the wavefront owning the crossing unit calls this; the lane
+// holding the drawn token writes it, its probability and the padding of the
+// sequence's outputs.
 template <bool kVec4>
 __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, int row, bool two_rows,
                                            const float* prow, const float* qrow, const SampleCtx& c,
@@ -516,54 +627,66 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     const int lane = lane_id();
     const int base = s.u * kUnit + lane * 4;
     const bool residual = two_rows && !use_p;
-    // load level (each load of a wavefront is 256 consecutive tokens)
-    bool found = false;
-    int istar = 0, ilast = -1;
-    double run_i = run;
-#pragma unroll 1
-    for (int i = 0; i < kVecs; ++i) {
-        double v;
+    // Load level (each load of a wavefront is 256 consecutive tokens): load i's
+    // total T_i is summed by the four lanes 4i..4i+3, sixteen per-lane sums each.
+    double Ti;
+    {
+        const int i = lane >> 2, j0 = (lane & 3) * (kWave / 4);
+        double v = 0.0;
         if (!use_p) {
-            const double2 g = ls[i][lane];
-            v = (residual ? g.x * invZp - g.y * invZq : g.x) * wscale;
+#pragma unroll
+            for (int j = 0; j < kWave / 4; ++j) {
+                const double2 g = ls[i][j0 + j];
+                v += residual ? g.x * invZp - g.y * invZq : g.x;
+            }
         } else {                 // zero residual (rare): p-weights of this load, recomputed
-            double w[4];
-            const f4 vp = load4<kVec4>(prow, a.V, base + i * (kWave * 4));
-            load_weights(false, false, vp, vp, c, invZp, invZq, w);
-            v = ((w[0] + w[1]) + (w[2] + w[3])) * wscale;
-        }
-        const double Ti = dpp_wave_sum(v);
-        if (Ti > 0.0) ilast = i;
-        if (exact && !found && Ti > 0.0) {
-            if (run_i + Ti > t) {
-                found = true;
-                istar = i;
-            } else {
-                run_i += Ti;
+#pragma unroll 1
+            for (int j = 0; j < kWave / 4; ++j) {
+                const int x = s.u * kUnit + i * (kWave * 4) + (j0 + j) * 4;
+                double w[4];
+                load_weights(two_rows, false, load4<kVec4>(row_rsrc(prow, a.V), a.V, x),
+                             two_rows ? load4<kVec4>(row_rsrc(qrow, a.V), a.V, x)
+                             : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, c, invZp, invZq, w);
+                v += (w[0] + w[1]) + (w[2] + w[3]);
             }
         }
+        v *= wscale;
+        v += __shfl_xor(v, 1, kWave);
+        v += __shfl_xor(v, 2, kWave);
+        Ti = v;
     }
-    if (!found) {          // rounding left no crossing here: take the last positive weight
+    const bool head = (lane & 3) == 3;   // one lane per load carries its total
+    const double incl = dpp_wave_incl_scan(head ? Ti : 0.0);
+    const unsigned long long pos_i = __ballot(head && Ti > 0.0);
+    const unsigned long long cross_i = exact ? __ballot(head && Ti > 0.0 && run + incl > t) : 0ull;
+    int istar;
+    double run_i;
+    if (cross_i) {
+        const int l = __ffsll(static_cast<long long>(cross_i)) - 1;
+        istar = l >> 2;
+        run_i = run + __shfl(incl - Ti, l, kWave);
+    } else {               // rounding left no crossing here: take the last positive weight
         exact = false;
-        istar = ilast < 0 ? 0 : ilast;
+        istar = pos_i ? (63 - __builtin_clzll(pos_i)) >> 2 : 0;
+        run_i = run;
     }
     double w[4];
-    const f4 vp = load4<kVec4>(prow, a.V, base + istar * (kWave * 4));
-    const f4 vq = two_rows ? load4<kVec4>(qrow, a.V, base + istar * (kWave * 4)) : vp;
+    const f4 vp = load4<kVec4>(row_rsrc(prow, a.V), a.V, base + istar * (kWave * 4));
+    const f4 vq = two_rows ? load4<kVec4>(row_rsrc(qrow, a.V), a.V, base + istar * (kWave * 4)) : vp;
     load_weights(two_rows, residual, vp, vq, c, invZp, invZq, w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] *= wscale;
     const double lsum = (w[0] + w[1]) + (w[2] + w[3]);
-    const double incl = dpp_wave_incl_scan(lsum);
-    const double excl = dpp_wave_shr1(incl);
+    const double lincl = dpp_wave_incl_scan(lsum);
+    const double lexcl = dpp_wave_shr1(lincl);
     int lstar, estar = -1;
-    const unsigned long long cross = exact ? __ballot(lsum > 0.0 && run_i + incl > t) : 0ull;
+    const unsigned long long cross = exact ? __ballot(lsum > 0.0 && run_i + lincl > t) : 0ull;
     int elast = -1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) if (w[e] > 0.0) elast = e;
     if (cross) {
         lstar = __ffsll(static_cast<long long>(cross)) - 1;
-        double r = run_i + excl;
+        double r = run_i + lexcl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (w[e] > 0.0) {
@@ -578,11 +701,15 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
         estar = elast;
     }
     estar = __shfl(estar, lstar, kWave);
-    if (lane != 0) return;
+    if (lane != lstar) return;
     if (estar < 0) estar = 0;
     int y = s.u * kUnit + istar * (kWave * 4) + lstar * 4 + estar;
-    if (y >= a.V) y = a.V - 1;   // only reachable when every weight is zero
-    const double py = exp_nonpos_f64((static_cast<double>(prow[y]) - M_ref) * c.invT64) / Zp_true;
+    float zy = estar == 0 ? vp.x : (estar == 1 ? vp.y : (estar == 2 ? vp.z : vp.w));
+    if (y >= a.V) {        // only reachable when every weight is zero
+        y = a.V - 1;
+        zy = prow[y];
+    }
+    const double py = exp_nonpos_f64((static_cast<double>(zy) - M_ref) * c.invT64) / Zp_true;
     const int k = a.k, b = s.b;
     const size_t ob = size_t(b) * (k + 1);
     a.out_tokens[ob + row] = y;
@@ -632,10 +759,9 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
     c.Mp64 = st.Mp;
     c.Mq64 = st.Mq;
     c.invT64 = a.invT64;
-    const double lzp = log(st.Zp), lzq = log(st.Zq);
-    c.hp = static_cast<float>(kLnTau + lzp);
-    c.hq = static_cast<float>(kLnTau + lzq);
-    c.dn = static_cast<float>(lzp - lzq);
+    c.tp = heavy_threshold(st.Mp, st.Zp, a.T);
+    c.tq = heavy_threshold(st.Mq, st.Zq, a.T);
+    c.dn = ln_approx(st.Zp) - ln_approx(st.Zq);
 
     const int lane = lane_id();
     const UnitSums us = unit_sums<kVec4, true>(xp, xq, c, prow, qrow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
@@ -703,14 +829,17 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
 __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, int j, const RowStats& st,
                                             const TokenLogits& tl) {
     const int k = a.k, b = s.b;
-    double p_d = 0.0, q_d = 0.0;
+    double ep = 0.0, eq = 0.0;   // p and q of the token times Z_p and Z_q
     if (tl.ok) {
-        p_d = exp_nonpos_f64((static_cast<double>(tl.zp) - st.Mp) * a.invT64) / st.Zp;
-        q_d = exp_nonpos_f64((static_cast<double>(tl.zq) - st.Mq) * a.invT64) / st.Zq;
+        ep = exp_nonpos_f64((static_cast<double>(tl.zp) - st.Mp) * a.invT64);
+        eq = exp_nonpos_f64((static_cast<double>(tl.zq) - st.Mq) * a.invT64);
     }
-    const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
-    const bool accepted = uniform(static_cast<int>(tl.u_acc < ratio)) != 0;
+    // u < p/q without a division on the way to the decision: u q Z_p Z_q < p Z_p Z_q.
+    // (q = 0 makes the ratio +inf when p > 0 and 0 when p = 0, as the product form does.)
+    const bool accepted = uniform(static_cast<int>(tl.u_acc * (eq * st.Zp) < ep * st.Zq)) != 0;
     if (s.q == 0 && lane_id() == 0) {
+        const double p_d = ep / st.Zp, q_d = eq / st.Zq;
+        const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
         if (a.accept_probs) a.accept_probs[size_t(b) * k + j] = static_cast<float>(fmin(1.0, ratio));
         if (accepted) {
             a.out_tokens[size_t(b) * (k + 1) + j] = tl.tok;
@@ -727,18 +856,27 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
 // (kResAccepted, kResError) and the row's statistics in `st`.
 template <bool kVec4>
 __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
-                                               f4 (&xq)[kVecs], RowStats& st, const TokenLogits& tok, Shared& sh,
+                                               f4 (&xq)[kVecs], RowStats& st, Shared& sh,
                                                bool& counted) {
     const float* prow = s.prow_base + size_t(row) * a.V;
     const float* qrow = s.qrow_base + size_t(row) * a.V;
-    // wave 0 takes the acceptance test: the draft token's two logits are loaded
-    // first, so they have long arrived when the group's statistics are in
+    load_unit<kVec4, true>(row_rsrc(prow, a.V), row_rsrc(qrow, a.V), a.V, s.u, xp, xq);
+    // wave 0 takes the acceptance test: the draft token and its two logits are read
+    // behind the unit's loads, through the scalar cache (uniform addresses into
+    // read-only inputs), so that waiting for them waits for no vector load and
+    // holds none back; they have long arrived when the group's statistics are in
+    TokenLogits tok;
+    tok.tok = 0;
+    tok.ok = false;
     float ztp = 0.0f, ztq = 0.0f;
-    if (s.wave == 0 && tok.ok) {
-        ztp = prow[tok.tok];
-        ztq = qrow[tok.tok];
+    if (s.wave == 0) {
+        tok.tok = load_uniform(a.draft_tokens, size_t(s.b) * a.k + row);
+        tok.ok = tok.tok >= 0 && tok.tok < a.V;
+        if (tok.ok) {
+            ztp = load_uniform(prow, tok.tok);
+            ztq = load_uniform(qrow, tok.tok);
+        }
     }
-    load_unit<kVec4, true>(prow, qrow, a.V, s.u, xp, xq);
     float mp = -INFINITY, mq = -INFINITY;
     double sp = 0.0, sq = 0.0;
 #pragma unroll
@@ -812,7 +950,8 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
                                           Shared& sh, bool& counted) {
     const int row = a.k;
     const float* prow = s.prow_base + size_t(row) * a.V;
-    load_unit<kVec4, false>(prow, prow, a.V, s.u, xp, xq);
+    const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, a.V);
+    load_unit<kVec4, false>(rp, rp, a.V, s.u, xp, xq);
     float m = -INFINITY;
     double acc = 0.0;
 #pragma unroll
@@ -827,8 +966,8 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
     c.Mp64 = Mu;
     c.Mq64 = 0.0;
     c.invT64 = a.invT64;
-    c.hp = static_cast<float>(kLnTau + log(Zu));
-    c.hq = kLnTau;
+    c.tp = heavy_threshold(Mu, Zu, a.T);
+    c.tq = INFINITY;
     c.dn = 0.0f;
     const int lane = lane_id();
     const UnitSums us = unit_sums<kVec4, false>(xp, xq, c, prow, prow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
@@ -917,22 +1056,13 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s.b = b;
         s.prow_base = a.target + size_t(b) * (a.k + 1) * a.V;
         s.qrow_base = a.draft + size_t(b) * a.k * a.V;
-        // per-lane copies (equal in every lane), first needed at the first acceptance
-        // test, so that no wait for them precedes the loads of the first level
-        s.sid = a.seq_ids[b];
-        s.L = a.seq_lens[b];
-        // the draft tokens of the sequence, lane j holding token j
-        const int lane = lane_id();
-        const int tok_lane = (lane < a.k) ? a.draft_tokens[size_t(b) * a.k + lane] : 0;
+        // scalar loads, first waited for at the first acceptance test
+        s.sid = load_uniform(a.seq_ids, b);
+        s.L = load_uniform(a.seq_lens, b);
         RowStats st;
         bool done = false;
         for (int j = 0; j < a.k && !done; ++j) {
-            TokenLogits tl;
-            tl.tok = __builtin_amdgcn_readlane(tok_lane, j);
-            tl.ok = tl.tok >= 0 && tl.tok < a.V;
-            tl.zp = tl.zq = 0.0f;
-            tl.u_acc = 0.0;
-            const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, tl, sh, counted);
+            const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, sh, counted);
             if (res & kResError) {
                 flag_error(a, s);
                 done = true;
@@ -1017,6 +1147,7 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.invT = 1.0f / p.temperature;
     a.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(p.temperature));
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
+    a.T = p.temperature;
     a.seed = p.seed;
     return (p.V % 4) == 0 ? launch_variant<true>(a, stream) : launch_variant<false>(a, stream);
 }
