@@ -134,11 +134,11 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
  * Shapes: 1 <= B <= 65535; 1 <= k <= 15; 2 <= V <= 1048576; temperature finite
  * and > 0. Logits are finite (padding of -inf is allowed; NaN is not).
  * Rows after a sequence's first rejection are not read, and no row is read twice.
- * The wavefronts of one sequence exchange partial sums while running, so the
+ * The workgroups of one sequence exchange partial sums while running, so the
  * grid is sized to what the device holds at once (SPEC_ERR_HIP if it cannot
- * hold one sequence's ceil(V / 4096) wavefronts). Every wait is bounded: should
- * residency ever be partial (other streams filling the device) and a wait time
- * out, the affected sequence reports num_accepted = -1.
+ * hold one sequence's ceil(V / 32768) workgroups of 512 threads). Every wait is
+ * bounded: should residency ever be partial (other streams filling the device)
+ * and a wait time out, the affected sequence reports num_accepted = -1.
  * Workspace: spec_reject_sample_workspace_size(B, k, V).
  * ---------------------------------------------------------------------- */
 spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out);
