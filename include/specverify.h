@@ -25,6 +25,12 @@
  *    workspace is reused across calls without clearing; two calls in flight
  *    at the same time must not share one.
  *  - No C++ exception crosses this interface.
+ *  - k, the number of drafted tokens, is chosen per call, 0 <= k <= 15. k = 0
+ *    is plain (non-speculative) decoding through the same three calls: one
+ *    query row, one token drawn from the target distribution, the length
+ *    advanced by one. This is the switch between speculative and plain decoding
+ *    that [RESP] (adaptive server) and [EFR] (speculation toggled by regime)
+ *    make at run time, without a separate decode kernel.
  *
  * Sources for what is computed (page titles; the pages print no API):
  *  [ACC]  "Accelerating RL Post-Training Rollouts via System-Integrated
@@ -90,7 +96,7 @@ int32_t spec_abi_version(void);
  *  seq_lens     int32 [B]   committed length L_b (keys read: L_b + k + 1)
  *  out          bf16  [B][k+1][Hq][D]
  *
- * Shapes: B >= 1; 1 <= k <= 15; Hkv >= 1; Hq % Hkv == 0; D in {64, 128};
+ * Shapes: B >= 1; 0 <= k <= 15; Hkv >= 1; Hq % Hkv == 0; D in {64, 128};
  * block_size in {16, 32, 64}; max_blocks >= 1; num_blocks >= 1;
  * max_seq_len >= k + 1; sm_scale finite and > 0.
  * Device preconditions: L_b + k + 1 <= min(max_seq_len, max_blocks*block_size);
@@ -131,8 +137,11 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
  *  out_probs     fp32 [B][k+1] or NULL: p_i(out_tokens[b][i]) for i <= a_b, 0 after
  *  accept_probs  fp32 [B][k]   or NULL: min(1, p_j/q_j) at d_j for tested j, -1 for untested
  *
- * Shapes: 1 <= B <= 65535; 1 <= k <= 15; 2 <= V <= 1048576; temperature finite
+ * Shapes: 1 <= B <= 65535; 0 <= k <= 15; 2 <= V <= 1048576; temperature finite
  * and > 0. Logits are finite (padding of -inf is allowed; NaN is not).
+ * k = 0: no draft is tested; out_tokens[b][0] is drawn from p_0 with u_smp at
+ * P = L_b + 1 and num_accepted[b] = 0. draft_logits, draft_tokens and
+ * accept_probs are not read or written and may be NULL.
  * Rows after a sequence's first rejection are not read, and no row is read twice.
  * The workgroups of one sequence exchange partial sums while running, so the
  * grid is sized to what the device holds at once (SPEC_ERR_HIP if it cannot
@@ -159,7 +168,7 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
  * (overflow_flags[b] = 0 otherwise; overflow_flags may be NULL).
  *
  *  seq_lens int32 [B] in/out;  num_accepted int32 [B] in [0, k];  overflow_flags int32 [B] or NULL
- * Shapes: B >= 1; 1 <= k <= 15; capacity_tokens >= 1.
+ * Shapes: B >= 1; 0 <= k <= 15; capacity_tokens >= 1.
  * ---------------------------------------------------------------------- */
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
                                 int32_t capacity_tokens, int32_t* overflow_flags, void* stream);

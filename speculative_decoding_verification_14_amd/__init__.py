@@ -146,17 +146,22 @@ def verify_attn(q, k_cache, v_cache, block_table, seq_lens, out, max_seq_len: in
 def reject_sample(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, temperature: float, seed: int,
                   out_tokens, num_accepted, out_probs=None, accept_probs=None, workspace=None, stream=None):
     """spec_reject_sample. target fp32 [B][k+1][V]; draft fp32 [B][k][V]; draft_tokens int32 [B][k];
-    seq_ids int64 [B]; seq_lens int32 [B]; outputs as in include/specverify.h."""
+    seq_ids int64 [B]; seq_lens int32 [B]; outputs as in include/specverify.h.
+
+    k = 0 (plain decoding) reads no draft data: draft_logits, draft_tokens and
+    accept_probs may then be None (or empty) and are passed as NULL."""
     import torch
     B, k1, V = target_logits.shape
     k = k1 - 1
+    if k == 0:
+        draft_logits = draft_tokens = accept_probs = None
     lib = library()
     need = reject_sample_workspace_size(B, k, V)
     if workspace is None:
         workspace = _workspace("reject", target_logits.device, need)
     _check(lib.spec_reject_sample(_need(target_logits, torch.float32, "target_logits"),
-                                  _need(draft_logits, torch.float32, "draft_logits"),
-                                  _need(draft_tokens, torch.int32, "draft_tokens"),
+                                  _opt(draft_logits, torch.float32, "draft_logits"),
+                                  _opt(draft_tokens, torch.int32, "draft_tokens"),
                                   _need(seq_ids, torch.int64, "seq_ids"), _need(seq_lens, torch.int32, "seq_lens"),
                                   B, k, V, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
                                   _need(out_tokens, torch.int32, "out_tokens"),
@@ -190,5 +195,6 @@ def verify_step(q, k_cache, v_cache, block_table, seq_lens, attn_out, max_seq_le
     verify_attn(q, k_cache, v_cache, block_table, seq_lens, attn_out, max_seq_len, sm_scale, stream=stream)
     reject_sample(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, temperature, seed, out_tokens,
                   num_accepted, out_probs, accept_probs, stream=stream)
-    commit_lengths(seq_lens, num_accepted, draft_tokens.shape[1], capacity_tokens, overflow_flags, stream=stream)
+    commit_lengths(seq_lens, num_accepted, target_logits.shape[1] - 1, capacity_tokens, overflow_flags,
+                   stream=stream)
     return out_tokens, num_accepted

@@ -39,7 +39,7 @@ bool is_pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 
 
 spec_status attn_shape_check(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len) {
     if (B < 1 || B > 65535) return SPEC_ERR_BAD_SHAPE;
-    if (k < 1 || k > 15) return SPEC_ERR_BAD_SHAPE;
+    if (k < 0 || k > 15) return SPEC_ERR_BAD_SHAPE;   // k = 0: plain decode, one query row
     if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_BAD_SHAPE;
     if (D != 64 && D != 128) return SPEC_ERR_BAD_SHAPE;
     if (max_seq_len < k + 1) return SPEC_ERR_BAD_SHAPE;
@@ -110,7 +110,7 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
 
 spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out) {
     if (!bytes_out) return SPEC_ERR_NULL_POINTER;
-    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
+    if (B < 1 || B > 65535 || k < 0 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
     *bytes_out = reject_workspace_bytes(B, k, V);
     return SPEC_OK;
 }
@@ -122,10 +122,11 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
                                int32_t* out_tokens, int32_t* num_accepted,
                                float* out_probs, float* accept_probs,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    if (!target_logits || !draft_logits || !draft_tokens || !seq_ids || !seq_lens || !out_tokens ||
+    if (B < 1 || B > 65535 || k < 0 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
+    // k = 0 (plain decode: the bonus draw from p_0 only) reads no draft rows or tokens
+    if (!target_logits || (k > 0 && (!draft_logits || !draft_tokens)) || !seq_ids || !seq_lens || !out_tokens ||
         !num_accepted || !workspace)
         return SPEC_ERR_NULL_POINTER;
-    if (B < 1 || B > 65535 || k < 1 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
     if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
     if (workspace_bytes < reject_workspace_bytes(B, k, V)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
     spec_status s = check_device();
@@ -143,7 +144,7 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
                                 int32_t capacity_tokens, int32_t* overflow_flags, void* stream) {
     if (!seq_lens || !num_accepted) return SPEC_ERR_NULL_POINTER;
-    if (B < 1 || k < 1 || k > 15 || capacity_tokens < 1) return SPEC_ERR_BAD_SHAPE;
+    if (B < 1 || k < 0 || k > 15 || capacity_tokens < 1) return SPEC_ERR_BAD_SHAPE;
     const spec_status s = check_device();
     if (s != SPEC_OK) return s;
     return from_hip(launch_commit(seq_lens, num_accepted, B, capacity_tokens, overflow_flags,

@@ -133,8 +133,9 @@ def compare_reject(gpu: dict, oracle: dict, tally: Tally, k: int) -> Tally:
         if np.any(gpu["out_probs"][b, n:] != 0.0):
             tally.bad.append((b, "out_probs_pad", -1, 0.0))
         nt = len(res.accept_probs)
-        tally.prob_err = max(tally.prob_err,
-                             float(np.max(np.abs(gpu["accept_probs"][b, :nt] - res.accept_probs))))
+        if nt:
+            tally.prob_err = max(tally.prob_err,
+                                 float(np.max(np.abs(gpu["accept_probs"][b, :nt] - res.accept_probs))))
         if np.any(gpu["accept_probs"][b, nt:] != -1.0):
             tally.bad.append((b, "accept_probs_pad", -1, 0.0))
     return tally

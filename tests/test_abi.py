@@ -55,7 +55,7 @@ def _attn_args(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=NULL), 1), (dict(vc=NULL), 1), (dict(out=NULL), 1),
-    (dict(B=0), 2), (dict(k=0), 2), (dict(k=16), 2), (dict(Hq=6, Hkv=4), 2), (dict(D=96), 2),
+    (dict(B=0), 2), (dict(k=-1), 2), (dict(k=16), 2), (dict(Hq=6, Hkv=4), 2), (dict(D=96), 2),
     (dict(bs=8), 2), (dict(bs=48), 2), (dict(max_seq_len=3), 2), (dict(max_blocks=0), 2),
     (dict(scale=0.0), 3), (dict(scale=float("nan")), 3), (dict(scale=float("inf")), 3),
     (dict(wsb=16), 4), (dict(ws=NULL), 1),
@@ -74,7 +74,10 @@ def _rej_args(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(t=NULL), 1), (dict(dt=NULL), 1), (dict(na=NULL), 1), (dict(ws=NULL), 1),
-    (dict(B=0), 2), (dict(k=0), 2), (dict(k=16), 2), (dict(V=1), 2),
+    (dict(B=0), 2), (dict(k=-1), 2), (dict(k=16), 2), (dict(V=1), 2),
+    (dict(d=NULL), 1), (dict(k=0, t=NULL), 1),
+    # k = 0 (plain decoding) reads no draft data: NULL draft pointers pass validation
+    (dict(k=0, d=NULL, dt=NULL, wsb=8), 4),
     (dict(T=0.0), 3), (dict(T=-1.0), 3), (dict(T=float("nan")), 3), (dict(T=float("inf")), 3),
     (dict(wsb=8), 4),
 ])
@@ -86,6 +89,8 @@ def test_commit_validation(lib):
     assert lib.spec_commit_lengths(NULL, FAKE, 4, 3, 100, NULL, NULL) == 1
     assert lib.spec_commit_lengths(FAKE, FAKE, 0, 3, 100, NULL, NULL) == 2
     assert lib.spec_commit_lengths(FAKE, FAKE, 4, 3, 0, NULL, NULL) == 2
+    assert lib.spec_commit_lengths(FAKE, FAKE, 4, -1, 100, NULL, NULL) == 2
+    assert lib.spec_commit_lengths(FAKE, FAKE, 4, 16, 100, NULL, NULL) == 2
 
 
 def test_workspace_sizes(lib):
@@ -93,6 +98,8 @@ def test_workspace_sizes(lib):
     assert lib.spec_reject_sample_workspace_size(64, 3, 128256, ctypes.byref(n)) == 0
     assert n.value > 64 * 32 * 8          # per-slice partials for 32 slices of 4096 logits
     assert lib.spec_reject_sample_workspace_size(0, 3, 100, ctypes.byref(n)) == 2
+    assert lib.spec_reject_sample_workspace_size(64, 0, 128256, ctypes.byref(n)) == 0
+    assert lib.spec_reject_sample_workspace_size(64, -1, 128256, ctypes.byref(n)) == 2
     assert lib.spec_verify_attn_workspace_size(64, 3, 32, 8, 128, 8196, ctypes.byref(n)) == 0
     assert n.value > 0
     small = n.value

@@ -53,6 +53,9 @@ def test_tiny_full(device):
     (128, 16, 16, 1, 32),   # G = 1, k = 1: 2 rows
     (128, 64, 4, 7, 16),    # 128 rows: four row groups
     (64, 48, 4, 15, 64),    # k = 15, G = 12: 192 rows
+    (128, 32, 8, 0, 16),    # k = 0 (plain decoding), 8B heads: 4 rows
+    (128, 16, 16, 0, 32),   # k = 0, G = 1: a single query row
+    (64, 48, 4, 0, 64),     # k = 0, G = 12: 12 rows
 ])
 def test_shapes(device, D, Hq, Hkv, k, bs):
     p = _preset(D=D, Hq=Hq, Hkv=Hkv, k=k, block_size=bs, B=3, ctx=("uniform", 300, 5000))

@@ -174,6 +174,44 @@ def test_exhaustive_grid_acceptance_and_inverse_cdf():
         assert all(a <= b for a, b in zip(ys, ys[1:]))
 
 
+def test_plain_decoding_k0_is_inverse_cdf_of_p0_over_the_whole_grid():
+    """k = 0 tests no draft: the step emits one token, the inverse CDF of p_0 at u_smp
+    (word 1 of the uniforms at P = L+1, never u_acc). Over all 2^24 grid values of u_smp
+    each token's count is its interval width ceil(C(y) 2^24) - ceil(C(y-1) 2^24), and
+    u_acc changes nothing."""
+    rng = np.random.default_rng(11)
+    V = 7
+    target = (rng.standard_normal((1, V)) * 1.5).astype(np.float32)
+    rows = orej.SequenceRows(target, np.zeros((0, V), np.float32), 1.0)
+    p0 = np.exp(target[0].astype(np.float64) - target[0].max())
+    p0 /= math.fsum(p0)
+    C = np.cumsum(p0)
+    edges = [_first_grid_point(lambda m, y=y: orej.decide(rows, [], 0, [(0.5, m / GRID)]).tokens[0] > y)
+             for y in range(V)]
+    counts = np.diff([0] + edges)
+    want = np.diff(np.concatenate([[0], np.minimum([math.ceil(C[y] / C[-1] * GRID) for y in range(V)], GRID)]))
+    np.testing.assert_array_equal(counts, want)
+    for u_acc in (0.0, 0.3, 1.0 - 2.0 ** -24):
+        for m in rng.integers(0, GRID, 50):
+            r0 = orej.decide(rows, [], 0, [(0.5, m / GRID)])
+            r1 = orej.decide(rows, [], 0, [(u_acc, m / GRID)])
+            assert r1.tokens == r0.tokens and r1.num_accepted == 0 and len(r1.tokens) == 1
+            assert [d.kind for d in r1.decisions] == ["sample"] and r1.accept_probs == []
+    # batch form: positions L+1, outputs [B][1], no acceptance outputs; commit adds one
+    B = 5
+    tl = (rng.standard_normal((B, 1, 40)) * 2).astype(np.float32)
+    sid = np.arange(B, dtype=np.int64) * 31 + 7
+    L = rng.integers(0, 1000, B).astype(np.int32)
+    out = orej.verify_batch(tl, np.zeros((B, 0, 40), np.float32), np.zeros((B, 0), np.int32), sid, L, 0, 1.0, 77)
+    assert out["out_tokens"].shape == (B, 1) and out["accept_probs"].shape == (B, 0)
+    assert np.all(out["num_accepted"] == 0)
+    for b in range(B):
+        u_acc, u_smp = philox.verify_uniforms(77, int(sid[b]), int(L[b]) + 1)
+        pb = orej.softmax_t(tl[b, 0], 1.0)
+        assert out["out_tokens"][b, 0] == orej.inverse_cdf(pb, u_smp)[0]
+    np.testing.assert_array_equal(ocommit.commit_lengths(L, out["num_accepted"], 10**6)[0], L + 1)
+
+
 def test_exact_boundary_hits_are_strict():
     """Dyadic weights make u * R land exactly on a CDF edge: the rule is C(y) > u * R (strict),
     zero-weight tokens are never emitted, and acceptance is u < p/q (strict)."""
@@ -276,7 +314,7 @@ def _markov_rollout(A, Bm, x0, seq_id, seed, k, n_tokens, rng, log_positions=Non
             drafts.append(d)
             ctx = d
         p_logits = [A[last]] + [A[d] for d in drafts]
-        rows = orej.SequenceRows(np.array(p_logits, np.float32), np.array(q_logits, np.float32), 1.0)
+        rows = orej.SequenceRows(np.array(p_logits, np.float32), np.array(q_logits, np.float32).reshape(k, V), 1.0)
         unis = orej.sequence_uniforms(seed, seq_id, L, k)
         res = orej.decide(rows, drafts, k, unis)
         if log_positions is not None:   # positions whose uniforms this round consumed
@@ -287,9 +325,12 @@ def _markov_rollout(A, Bm, x0, seq_id, seed, k, n_tokens, rng, log_positions=Non
     return tokens[1: n_tokens + 1]
 
 
-def test_monte_carlo_lossless_across_rounds_with_commit():
-    rng = np.random.default_rng(7)
-    V, k, n_tok, n = 3, 2, 4, 20_000
+@pytest.mark.parametrize("k", [2, 0])
+def test_monte_carlo_lossless_across_rounds_with_commit(k):
+    """k = 2 is speculative decoding; k = 0 is plain decoding (one token per round, the
+    length advanced by one): both must generate the target chain's joint law."""
+    rng = np.random.default_rng(7 + k)
+    V, n_tok, n = 3, 4, 20_000
     A = (rng.standard_normal((V, V)) * 1.2).astype(np.float32)
     Bm = (A + rng.standard_normal((V, V)) * 1.0).astype(np.float32)
     x0 = 1
