@@ -15,6 +15,11 @@ Memory layouts read here (the same bytes the GPU reads):
 * k_cache  bf16 [num_blocks][Hkv][block_size][D]
 * v_cache  bf16 [num_blocks][Hkv][D][block_size]
 * block_table int32 [B][max_blocks]: logical page -> physical page
+
+Ragged draft lengths (per-sequence k_b, "EfficientRollout: System-Aware
+Self-Speculative Decoding for RL Rollouts", abstract: acceptance-aware draft
+length) change only which rows exist: sequence b contributes rows i = 0 .. k_b,
+packed at row cu[b] + b + i of q [R][Hq][D], and reads L_b + k_b + 1 keys.
 """
 
 from __future__ import annotations
@@ -80,3 +85,24 @@ def verify_attention_row(q, k_cache, v_cache, block_table, seq_lens, k: int, Hq:
     L = int(seq_lens[b])
     K, Vv = gather_sequence_kv(k_cache, v_cache, block_table, b, g, L + i + 1, block_size)
     return attend(bf16_to_f64(q[b, i, h, :]), K, Vv, sm_scale)
+
+
+def verify_attention_ragged(q, k_cache, v_cache, block_table, seq_lens, cu_drafts, Hq: int, Hkv: int,
+                            block_size: int, sm_scale: float) -> np.ndarray:
+    """fp64 output [R][Hq][D] for packed rows: sequence b has k_b = cu[b+1] - cu[b] drafts and
+    its query row i (0 <= i <= k_b) is row cu[b] + b + i; row i attends keys 0 .. L_b + i."""
+    B = len(seq_lens)
+    R, _, D = q.shape
+    G = Hq // Hkv
+    out = np.full((R, Hq, D), np.nan, dtype=np.float64)
+    for b in range(B):
+        kb = int(cu_drafts[b + 1]) - int(cu_drafts[b])
+        r0 = int(cu_drafts[b]) + b
+        L = int(seq_lens[b])
+        for g in range(Hkv):
+            K, Vv = gather_sequence_kv(k_cache, v_cache, block_table, b, g, L + kb + 1, block_size)
+            for i in range(kb + 1):
+                visible = L + i + 1
+                for h in range(g * G, (g + 1) * G):
+                    out[r0 + i, h, :] = attend(bf16_to_f64(q[r0 + i, h, :]), K[:visible], Vv[:visible], sm_scale)
+    return out

@@ -189,3 +189,35 @@ def verify_batch(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, k
         results.append(res)
     return dict(out_tokens=out_tokens, num_accepted=num_accepted, out_probs=out_probs,
                 accept_probs=accept_probs, results=results)
+
+
+def verify_batch_ragged(target_logits, draft_logits, draft_tokens, cu_drafts, seq_ids, seq_lens,
+                        temperature: float, seed: int, rows_cache=None):
+    """Ragged draft lengths ("EfficientRollout: System-Aware Self-Speculative Decoding for RL
+    Rollouts", abstract: the draft length adapts to acceptance): sequence b has
+    k_b = cu[b+1] - cu[b] drafts and runs the same chain over them. Rows are packed:
+    target_logits / out_tokens / out_probs row cu[b] + b + j (j = 0 .. k_b), draft_logits /
+    draft_tokens / accept_probs row cu[b] + j (j < k_b). Unused entries are -1 (tokens,
+    accept_probs) or 0 (out_probs), as in the uniform layout."""
+    cu = [int(c) for c in cu_drafts]
+    B = len(seq_ids)
+    T, K = cu[B] + B, cu[B]
+    out_tokens = np.full(T, -1, dtype=np.int32)
+    out_probs = np.zeros(T, dtype=np.float64)
+    accept_probs = np.full(K, -1.0, dtype=np.float64)
+    num_accepted = np.zeros(B, dtype=np.int32)
+    results = []
+    for b in range(B):
+        kb, t0, d0 = cu[b + 1] - cu[b], cu[b] + b, cu[b]
+        rows = rows_cache[b] if rows_cache is not None else SequenceRows(
+            target_logits[t0:t0 + kb + 1], draft_logits[d0:d0 + kb], temperature)
+        res = decide(rows, draft_tokens[d0:d0 + kb], kb,
+                     sequence_uniforms(seed, int(seq_ids[b]), int(seq_lens[b]), kb))
+        n = len(res.tokens)
+        out_tokens[t0:t0 + n] = res.tokens
+        out_probs[t0:t0 + n] = res.out_probs
+        accept_probs[d0:d0 + len(res.accept_probs)] = res.accept_probs
+        num_accepted[b] = res.num_accepted
+        results.append(res)
+    return dict(out_tokens=out_tokens, num_accepted=num_accepted, out_probs=out_probs,
+                accept_probs=accept_probs, results=results)

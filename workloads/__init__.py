@@ -8,3 +8,5 @@ attention, no counter-based uniforms).
 
 from .gen import PRESETS, Preset, make_attention_inputs, make_reject_inputs, make_inputs  # noqa: F401
 from .gen import bf16_bits, verify_seed, draft_from_logits  # noqa: F401
+from .ragged import (make_ragged_attention_inputs, make_ragged_reject_inputs, pack_reject_inputs,  # noqa: F401
+                     ragged_draft_lengths, offsets)
