@@ -116,6 +116,32 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Verify attention with ragged draft lengths  [EFR] (abstract: the draft length
+ * adapts to acceptance), [RESP] (GAP 1 and the Adaptive Server: the speculation
+ * configuration is chosen per batch as it shrinks).
+ *
+ * As spec_verify_attn, except that sequence b has its own draft count
+ * k_b = cu_drafts[b+1] - cu_drafts[b] (0 <= k_b <= max_k) and the query and
+ * output rows are packed: sequence b's rows i = 0 .. k_b are rows
+ * cu_drafts[b] + b + i of
+ *
+ *  q    bf16 [R][Hq][D],  out  bf16 [R][Hq][D],  R = cu_drafts[B] + B
+ *  cu_drafts  int32 [B+1] device array, cu_drafts[0] = 0, non-decreasing
+ *
+ * Row i of sequence b attends keys 0 .. L_b + i; L_b + k_b + 1 keys are read.
+ * The offsets are a device-side precondition (not checked; k_b is clamped into
+ * [0, max_k]). Shapes and workspace are those of spec_verify_attn with k = max_k
+ * (spec_verify_attn_workspace_size(B, max_k, ...)); SPEC_ERR_NULL_POINTER if
+ * cu_drafts is NULL. With every k_b = max_k the result equals spec_verify_attn's.
+ * ---------------------------------------------------------------------- */
+spec_status spec_verify_attn_ragged(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_drafts,
+                                    void* out, int32_t B, int32_t max_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t block_size, int32_t max_blocks, int32_t num_blocks,
+                                    int32_t max_seq_len, float sm_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Rejection sampling  [ACC], [ODC], [EFR].
  *
  * p_j = softmax(target_logits[b][j] / T), q_j = softmax(draft_logits[b][j] / T).
@@ -159,6 +185,35 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
                                int32_t* out_tokens, int32_t* num_accepted,
                                float* out_probs, float* accept_probs,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rejection sampling with ragged draft lengths  [EFR] (acceptance-aware draft
+ * length), [RESP] (GAP 1, Adaptive Server).
+ *
+ * As spec_reject_sample, with sequence b's k_b = cu_drafts[b+1] - cu_drafts[b]
+ * (0 <= k_b <= max_k) and its rows packed (T = cu_drafts[B] + B, K = cu_drafts[B]):
+ *
+ *  target_logits fp32 [T][V]   rows cu_drafts[b] + b + j, j = 0 .. k_b
+ *  draft_logits  fp32 [K][V]   rows cu_drafts[b] + j,     j = 0 .. k_b - 1
+ *  draft_tokens  int32 [K]     same indexing as draft_logits
+ *  out_tokens    int32 [T], out_probs fp32 [T] or NULL: same indexing as target_logits
+ *  accept_probs  fp32 [K] or NULL: same indexing as draft_logits
+ *  num_accepted  int32 [B]: a_b in [0, k_b]
+ *
+ * The chain of sequence b runs over its own k_b drafts (positions L_b + 1 + j);
+ * k_b = 0 is plain decoding for that sequence. Shapes and workspace are those of
+ * spec_reject_sample with k = max_k (spec_reject_sample_workspace_size(B, max_k,
+ * V)); draft_logits and draft_tokens may be NULL when max_k = 0. The offsets are
+ * a device-side precondition (not checked; k_b is clamped into [0, max_k]).
+ * With every k_b = max_k the outputs equal spec_reject_sample's.
+ * ---------------------------------------------------------------------- */
+spec_status spec_reject_sample_ragged(const float* target_logits, const float* draft_logits,
+                                      const int32_t* draft_tokens, const int32_t* cu_drafts,
+                                      const int64_t* seq_ids, const int32_t* seq_lens, int32_t B, int32_t max_k,
+                                      int32_t V, float temperature, uint64_t seed,
+                                      int32_t* out_tokens, int32_t* num_accepted,
+                                      float* out_probs, float* accept_probs,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Commit  [ACC] (accepted length per step), [RESP] (KV cache extended in place).

@@ -16,7 +16,8 @@ import os
 import threading
 
 __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", "reject_sample",
-           "reject_sample_workspace_size", "commit_lengths", "verify_step", "LIB_PATH", "SYMBOLS"]
+           "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
+           "reject_sample_ragged", "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
 
@@ -33,6 +34,9 @@ SYMBOLS = {
     "spec_reject_sample": (_c_int32, [_vp] * 5 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
                            + [_vp] * 5 + [_c_size, _vp]),
     "spec_commit_lengths": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _c_int32, _vp, _vp]),
+    "spec_verify_attn_ragged": (_c_int32, [_vp] * 7 + [_c_int32] * 9 + [ctypes.c_float, _vp, _c_size, _vp]),
+    "spec_reject_sample_ragged": (_c_int32, [_vp] * 6 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
+                                  + [_vp] * 5 + [_c_size, _vp]),
 }
 
 
@@ -141,6 +145,64 @@ def verify_attn(q, k_cache, v_cache, block_table, seq_lens, out, max_seq_len: in
                                 B, k1 - 1, Hq, Hkv, D, bs, max_blocks, NB, int(max_seq_len), scale,
                                 wptr, wbytes, _stream_handle(stream)), "spec_verify_attn")
     return out
+
+
+def verify_attn_ragged(q, k_cache, v_cache, block_table, seq_lens, cu_drafts, out, max_k: int, max_seq_len: int,
+                       sm_scale: float | None = None, workspace=None, stream=None):
+    """spec_verify_attn_ragged. q/out bf16 [R][Hq][D] with R = cu_drafts[B] + B (sequence b's
+    rows at cu_drafts[b] + b + i); cu_drafts int32 [B+1] on the device; max_k >= every k_b."""
+    import torch
+    R, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    B = seq_lens.shape[0]
+    max_blocks = block_table.shape[1]
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    lib = library()
+    need = verify_attn_workspace_size(B, max_k, Hq, Hkv, D, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = _workspace("attn", q.device, need)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.spec_verify_attn_ragged(_need(q, torch.bfloat16, "q"), _need(k_cache, torch.bfloat16, "k_cache"),
+                                       _need(v_cache, torch.bfloat16, "v_cache"),
+                                       _need(block_table, torch.int32, "block_table"),
+                                       _need(seq_lens, torch.int32, "seq_lens"), _need(cu_drafts, torch.int32, "cu_drafts"),
+                                       _need(out, torch.bfloat16, "out"),
+                                       B, int(max_k), Hq, Hkv, D, bs, max_blocks, NB, int(max_seq_len), scale,
+                                       wptr, wbytes, _stream_handle(stream)), "spec_verify_attn_ragged")
+    return out
+
+
+def reject_sample_ragged(target_logits, draft_logits, draft_tokens, cu_drafts, seq_ids, seq_lens, max_k: int,
+                         temperature: float, seed: int, out_tokens, num_accepted, out_probs=None, accept_probs=None,
+                         workspace=None, stream=None):
+    """spec_reject_sample_ragged. target fp32 [T][V], out_tokens int32 [T], out_probs fp32 [T]
+    (T = cu_drafts[B] + B); draft fp32 [K][V], draft_tokens int32 [K], accept_probs fp32 [K]
+    (K = cu_drafts[B]); cu_drafts int32 [B+1] on the device; max_k >= every k_b."""
+    import torch
+    V = target_logits.shape[1]
+    B = seq_ids.shape[0]
+    lib = library()
+    need = reject_sample_workspace_size(B, max_k, V)
+    if workspace is None:
+        workspace = _workspace("reject", target_logits.device, need)
+    if max_k == 0 or draft_logits is None or draft_logits.numel() == 0:
+        draft_logits = draft_tokens = None
+    if accept_probs is not None and accept_probs.numel() == 0:
+        accept_probs = None
+    _check(lib.spec_reject_sample_ragged(_need(target_logits, torch.float32, "target_logits"),
+                                         _opt(draft_logits, torch.float32, "draft_logits"),
+                                         _opt(draft_tokens, torch.int32, "draft_tokens"),
+                                         _need(cu_drafts, torch.int32, "cu_drafts"),
+                                         _need(seq_ids, torch.int64, "seq_ids"), _need(seq_lens, torch.int32, "seq_lens"),
+                                         B, int(max_k), V, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                         _need(out_tokens, torch.int32, "out_tokens"),
+                                         _need(num_accepted, torch.int32, "num_accepted"),
+                                         _opt(out_probs, torch.float32, "out_probs"),
+                                         _opt(accept_probs, torch.float32, "accept_probs"),
+                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream)), "spec_reject_sample_ragged")
+    return out_tokens, num_accepted
 
 
 def reject_sample(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, temperature: float, seed: int,

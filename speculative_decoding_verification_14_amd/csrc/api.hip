@@ -45,13 +45,67 @@ spec_status attn_shape_check(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int3
     if (max_seq_len < k + 1) return SPEC_ERR_BAD_SHAPE;
     const long long rows = static_cast<long long>(k + 1) * (Hq / Hkv);
     if (static_cast<long long>(Hkv) * ((rows + 31) / 32) > 65535) return SPEC_ERR_BAD_SHAPE;
-    // the per-sequence work prefix (128-key iterations) is kept in int32
-    if (static_cast<long long>(B) * ((static_cast<long long>(max_seq_len) + 127) / 128) > 0x7FFFFFFFLL)
+    // the per-sequence work prefix (128-key iterations x row groups x KV heads) is kept in int32
+    if (static_cast<long long>(B) * Hkv * ((rows + 31) / 32) * ((static_cast<long long>(max_seq_len) + 127) / 128) >
+        0x7FFFFFFFLL)
         return SPEC_ERR_BAD_SHAPE;
     return SPEC_OK;
 }
 
 spec_status from_hip(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
+
+}  // namespace
+
+namespace {
+
+spec_status verify_attn_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* cu_drafts, void* out, int32_t B, int32_t k,
+                             int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
+                             int32_t num_blocks, int32_t max_seq_len, float sm_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return SPEC_ERR_NULL_POINTER;
+    spec_status s = attn_shape_check(B, k, Hq, Hkv, D, max_seq_len);
+    if (s != SPEC_OK) return s;
+    if (!is_pow2_in(block_size, 16, 64)) return SPEC_ERR_BAD_SHAPE;
+    if (max_blocks < 1 || num_blocks < 1) return SPEC_ERR_BAD_SHAPE;
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return SPEC_ERR_BAD_VALUE;
+    const AttnGeometry geo = attn_geometry(B, k, Hq, Hkv, D, max_seq_len);
+    if (geo.workspace > 0 && !workspace) return SPEC_ERR_NULL_POINTER;
+    if (workspace_bytes < geo.workspace) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    if ((s = check_device()) != SPEC_OK) return s;
+    AttnLaunch p;
+    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
+    p.block_table = block_table; p.seq_lens = seq_lens; p.cu_drafts = cu_drafts; p.out = out;
+    p.B = B; p.k = k; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
+    p.block_size = block_size; p.max_blocks = max_blocks; p.num_blocks = num_blocks;
+    p.max_seq_len = max_seq_len; p.sm_scale = sm_scale;
+    p.workspace = workspace;
+    return from_hip(launch_attn(p, geo, static_cast<hipStream_t>(stream)));
+}
+
+spec_status reject_impl(const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,
+                        const int32_t* cu_drafts, const int64_t* seq_ids, const int32_t* seq_lens, int32_t B,
+                        int32_t k, int32_t V, float temperature, uint64_t seed, int32_t* out_tokens,
+                        int32_t* num_accepted, float* out_probs, float* accept_probs, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (B < 1 || B > 65535 || k < 0 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
+    // k = 0 (plain decode: the bonus draw from p_0 only) reads no draft rows or tokens
+    if (!target_logits || (k > 0 && (!draft_logits || !draft_tokens)) || !seq_ids || !seq_lens || !out_tokens ||
+        !num_accepted || !workspace)
+        return SPEC_ERR_NULL_POINTER;
+    if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
+    if (workspace_bytes < reject_workspace_bytes(B, k, V)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    RejectLaunch p;
+    p.target_logits = target_logits; p.draft_logits = draft_logits; p.draft_tokens = draft_tokens;
+    p.seq_ids = seq_ids; p.seq_lens = seq_lens; p.cu_drafts = cu_drafts;
+    p.B = B; p.k = k; p.V = V; p.temperature = temperature; p.seed = seed;
+    p.out_tokens = out_tokens; p.num_accepted = num_accepted;
+    p.out_probs = out_probs; p.accept_probs = accept_probs;
+    p.workspace = workspace;
+    return from_hip(launch_reject(p, static_cast<hipStream_t>(stream)));
+}
 
 }  // namespace
 
@@ -82,30 +136,27 @@ spec_status spec_verify_attn_workspace_size(int32_t B, int32_t k, int32_t Hq, in
     return SPEC_OK;
 }
 
+
 spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_table, const int32_t* seq_lens, void* out,
                              int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D,
                              int32_t block_size, int32_t max_blocks, int32_t num_blocks,
                              int32_t max_seq_len, float sm_scale,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return SPEC_ERR_NULL_POINTER;
-    spec_status s = attn_shape_check(B, k, Hq, Hkv, D, max_seq_len);
-    if (s != SPEC_OK) return s;
-    if (!is_pow2_in(block_size, 16, 64)) return SPEC_ERR_BAD_SHAPE;
-    if (max_blocks < 1 || num_blocks < 1) return SPEC_ERR_BAD_SHAPE;
-    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f)) return SPEC_ERR_BAD_VALUE;
-    const AttnGeometry geo = attn_geometry(B, k, Hq, Hkv, D, max_seq_len);
-    if (geo.workspace > 0 && !workspace) return SPEC_ERR_NULL_POINTER;
-    if (workspace_bytes < geo.workspace) return SPEC_ERR_WORKSPACE_TOO_SMALL;
-    if ((s = check_device()) != SPEC_OK) return s;
-    AttnLaunch p;
-    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
-    p.block_table = block_table; p.seq_lens = seq_lens; p.out = out;
-    p.B = B; p.k = k; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
-    p.block_size = block_size; p.max_blocks = max_blocks; p.num_blocks = num_blocks;
-    p.max_seq_len = max_seq_len; p.sm_scale = sm_scale;
-    p.workspace = workspace;
-    return from_hip(launch_attn(p, geo, static_cast<hipStream_t>(stream)));
+    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, nullptr, out, B, k, Hq, Hkv, D, block_size,
+                            max_blocks, num_blocks, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+}
+
+spec_status spec_verify_attn_ragged(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_drafts,
+                                    void* out, int32_t B, int32_t max_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t block_size, int32_t max_blocks, int32_t num_blocks,
+                                    int32_t max_seq_len, float sm_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_drafts) return SPEC_ERR_NULL_POINTER;
+    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, cu_drafts, out, B, max_k, Hq, Hkv, D,
+                            block_size, max_blocks, num_blocks, max_seq_len, sm_scale, workspace, workspace_bytes,
+                            stream);
 }
 
 spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out) {
@@ -122,23 +173,21 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
                                int32_t* out_tokens, int32_t* num_accepted,
                                float* out_probs, float* accept_probs,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 1 || B > 65535 || k < 0 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
-    // k = 0 (plain decode: the bonus draw from p_0 only) reads no draft rows or tokens
-    if (!target_logits || (k > 0 && (!draft_logits || !draft_tokens)) || !seq_ids || !seq_lens || !out_tokens ||
-        !num_accepted || !workspace)
-        return SPEC_ERR_NULL_POINTER;
-    if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
-    if (workspace_bytes < reject_workspace_bytes(B, k, V)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
-    spec_status s = check_device();
-    if (s != SPEC_OK) return s;
-    RejectLaunch p;
-    p.target_logits = target_logits; p.draft_logits = draft_logits; p.draft_tokens = draft_tokens;
-    p.seq_ids = seq_ids; p.seq_lens = seq_lens;
-    p.B = B; p.k = k; p.V = V; p.temperature = temperature; p.seed = seed;
-    p.out_tokens = out_tokens; p.num_accepted = num_accepted;
-    p.out_probs = out_probs; p.accept_probs = accept_probs;
-    p.workspace = workspace;
-    return from_hip(launch_reject(p, static_cast<hipStream_t>(stream)));
+    return reject_impl(target_logits, draft_logits, draft_tokens, nullptr, seq_ids, seq_lens, B, k, V, temperature,
+                       seed, out_tokens, num_accepted, out_probs, accept_probs, workspace, workspace_bytes, stream);
+}
+
+spec_status spec_reject_sample_ragged(const float* target_logits, const float* draft_logits,
+                                      const int32_t* draft_tokens, const int32_t* cu_drafts,
+                                      const int64_t* seq_ids, const int32_t* seq_lens, int32_t B, int32_t max_k,
+                                      int32_t V, float temperature, uint64_t seed,
+                                      int32_t* out_tokens, int32_t* num_accepted,
+                                      float* out_probs, float* accept_probs,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_drafts) return SPEC_ERR_NULL_POINTER;
+    return reject_impl(target_logits, draft_logits, draft_tokens, cu_drafts, seq_ids, seq_lens, B, max_k, V,
+                       temperature, seed, out_tokens, num_accepted, out_probs, accept_probs, workspace,
+                       workspace_bytes, stream);
 }
 
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,

@@ -29,6 +29,10 @@
 //    segment in workgroup order (deterministic).
 //  * Inside a piece the four waves take interleaved 32-key blocks; at the end the
 //    waves' (max, sum, O) are combined through LDS.
+//  * Ragged draft lengths (k_b per sequence, rows packed by an offsets array) use
+//    the same kernels: a sequence contributes (k_b+1) x G rows, ceil of that / 32
+//    row groups per KV head, and L_b + k_b + 1 keys to the flat work order, so
+//    short drafts cost no padding work.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,13 +55,36 @@ struct AttnArgs {
     const uint16_t* vc;
     const int32_t* bt;
     const int32_t* seq_lens;
+    const int32_t* cu;   // [B+1] draft-count offsets, or null: every sequence has k drafts
     uint16_t* out;
     float* part_o;     // [kMaxP][2][32 rows][D]
     float* part_ml;    // [kMaxP][2][32 rows][2]
-    int32_t* prefix;   // [B+1] exclusive prefix of iterations per sequence
-    int B, k, Hq, Hkv, G, rows, row_groups, U, max_blocks, bs_log2, P;
+    int32_t* prefix;   // [B+1] exclusive prefix of work (iterations x row groups x KV heads) per sequence
+    int B, k, Hq, Hkv, G, rows, row_groups, U, max_blocks, bs_log2, P;   // rows, row_groups, U: at k
     float scale_log2;
 };
+
+// Per-sequence shape: k_b drafts, its first query row in the packed [rows][Hq][D]
+// layout, its query rows per KV head and its row groups. Without offsets every
+// sequence has k drafts and starts at b (k+1).
+struct SeqShape {
+    int kb, row0, rows, row_groups;
+};
+
+__device__ __forceinline__ SeqShape seq_shape(const int32_t* cu, int b, int k, int G) {
+    SeqShape s;
+    if (cu) {
+        const int c0 = cu[b], c1 = cu[b + 1];
+        s.kb = min(max(c1 - c0, 0), k);
+        s.row0 = c0 + b;
+    } else {
+        s.kb = k;
+        s.row0 = b * (k + 1);
+    }
+    s.rows = (s.kb + 1) * G;
+    s.row_groups = (s.rows + 31) / 32;
+    return s;
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     const __bf16 h = static_cast<__bf16>(x);
@@ -89,6 +116,12 @@ __device__ __forceinline__ int iters_of(int seq_len, int k) {
     return n <= 0 ? 0 : (n + kIterKeys - 1) / kIterKeys;
 }
 
+// Flat work of sequence b: 128-key iterations x row groups x KV heads.
+__device__ __forceinline__ int work_of(const int32_t* seq_lens, const int32_t* cu, int b, int k, int G, int Hkv) {
+    const SeqShape sh = seq_shape(cu, b, k, G);
+    return iters_of(seq_lens[b], sh.kb) * sh.row_groups * Hkv;
+}
+
 // Workgroup w of P owns flat positions [range_start(w), range_start(w+1)).
 __device__ __forceinline__ long long range_start(int w, long long total, int P) {
     const long long q = total / P, r = total % P;
@@ -101,14 +134,15 @@ __device__ __forceinline__ int range_owner(long long x, long long total, int P) 
     return static_cast<int>(r + (x - r * (q + 1)) / q);
 }
 
-// Exclusive prefix of iterations per sequence, built by one 256-thread workgroup
-// into `dst` (LDS or global); dst[B] is the total.
-__device__ void build_prefix(const int32_t* seq_lens, int B, int k, int32_t* dst, int* s_wave) {
+// Exclusive prefix of work per sequence, built by one 256-thread workgroup into
+// `dst` (LDS or global); dst[B] is the total.
+__device__ void build_prefix(const int32_t* seq_lens, const int32_t* cu, int B, int k, int G, int Hkv,
+                             int32_t* dst, int* s_wave) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     int carry = 0;
     for (int base = 0; base < B; base += kAT) {
         const int b = base + tid;
-        int v = (b < B) ? iters_of(seq_lens[b], k) : 0;
+        int v = (b < B) ? work_of(seq_lens, cu, b, k, G, Hkv) : 0;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
             const int y = __shfl_up(v, o, kWave);
@@ -128,9 +162,10 @@ __device__ void build_prefix(const int32_t* seq_lens, int B, int k, int32_t* dst
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kAT) void attn_plan_kernel(const int32_t* seq_lens, int B, int k, int32_t* prefix) {
+__global__ __launch_bounds__(kAT) void attn_plan_kernel(const int32_t* seq_lens, const int32_t* cu, int B, int k,
+                                                        int G, int Hkv, int32_t* prefix) {
     __shared__ int s_wave[kAWaves];
-    build_prefix(seq_lens, B, k, prefix, s_wave);
+    build_prefix(seq_lens, cu, B, k, G, Hkv, prefix, s_wave);
 }
 
 template <int D, int NT>
@@ -151,24 +186,27 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 
     const int32_t* prefix = a.prefix;
     if (a.B <= kLdsPrefix) {
-        build_prefix(a.seq_lens, a.B, a.k, s_prefix, s_wave);
+        build_prefix(a.seq_lens, a.cu, a.B, a.k, a.G, a.Hkv, s_prefix, s_wave);
         if (w == 0)
             for (int i = tid; i <= a.B; i += kAT) a.prefix[i] = s_prefix[i];
         prefix = s_prefix;
     }
-    const long long total = static_cast<long long>(a.U) * prefix[a.B];
+    const long long total = prefix[a.B];
     const long long r0 = range_start(w, total, a.P), r1 = range_start(w + 1, total, a.P);
     if (r0 >= r1) return;
 
-    // segment (b, u) starts at U * prefix[b] + u * iters_b; find the last b whose start is <= r0
+    // segment (b, u) starts at prefix[b] + u * iters_b; find the last b whose start is <= r0
+    // (sequences without work have equal prefixes and are passed over)
     int lo = 0, hi = a.B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (static_cast<long long>(a.U) * prefix[mid] <= r0) lo = mid; else hi = mid - 1;
+        if (prefix[mid] <= r0) lo = mid; else hi = mid - 1;
     }
     int b = lo;
-    int iters_b = prefix[b + 1] - prefix[b];
-    const long long off = r0 - static_cast<long long>(a.U) * prefix[b];
+    SeqShape sh = seq_shape(a.cu, b, a.k, a.G);
+    int U_b = sh.row_groups * a.Hkv;
+    int iters_b = (prefix[b + 1] - prefix[b]) / U_b;
+    const long long off = r0 - prefix[b];
     int u = static_cast<int>(off / iters_b);
     int it0 = static_cast<int>(off % iters_b);
 
@@ -177,9 +215,9 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
     bool first_piece = true;
     while (cur < r1) {
         const int it1 = static_cast<int>(min(static_cast<long long>(iters_b), it0 + (r1 - cur)));
-        const int g = u / a.row_groups, rg = u % a.row_groups;
+        const int g = u / sh.row_groups, rg = u % sh.row_groups;
         const int L = a.seq_lens[b];
-        const int N = L + a.k + 1;
+        const int N = L + sh.kb + 1;
         const int c0 = it0 * kIterKeys;
         const int c1 = min(N, it1 * kIterKeys);
 
@@ -189,10 +227,10 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int r = rg * 32 + n * 16 + l16;
-            if (r < a.rows) {
+            if (r < sh.rows) {
                 const int i = r / a.G;
                 const int h = g * a.G + r % a.G;
-                const uint16_t* qp = a.q + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + 8 * lg;
+                const uint16_t* qp = a.q + ((size_t(sh.row0) + i) * a.Hq + h) * D + 8 * lg;
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(load16(qp + 32 * ds));
                 lim[n] = L + i;
@@ -347,10 +385,10 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                 }
                 const int row = rg * 32 + n * 16 + r;
                 if (whole) {
-                    if (row < a.rows) {
+                    if (row < sh.rows) {
                         const int i = row / a.G;
                         const int h = g * a.G + row % a.G;
-                        uint16_t* op = a.out + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + d0;
+                        uint16_t* op = a.out + ((size_t(sh.row0) + i) * a.Hq + h) * D + d0;
                         const float inv = 1.0f / lsum;
 #pragma unroll
                         for (int dd = 0; dd < D / 16; ++dd) op[dd] = f32_to_bf16_bits(acc[dd] * inv);
@@ -372,10 +410,15 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
         cur += it1 - it0;
         first_piece = false;
         it0 = 0;
-        if (++u == a.U) {
+        if (++u == U_b) {
             u = 0;
-            if (++b >= a.B) break;
-            iters_b = prefix[b + 1] - prefix[b];
+            do {   // the next sequence with work (its share starts where this one ended)
+                if (++b >= a.B) break;
+            } while (prefix[b + 1] == prefix[b]);
+            if (b >= a.B) break;
+            sh = seq_shape(a.cu, b, a.k, a.G);
+            U_b = sh.row_groups * a.Hkv;
+            iters_b = (prefix[b + 1] - prefix[b]) / U_b;
         }
     }
 }
@@ -385,21 +428,24 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) {
     const int u = blockIdx.x, b = blockIdx.y;
-    const long long total = static_cast<long long>(a.U) * a.prefix[a.B];
-    const int iters_b = a.prefix[b + 1] - a.prefix[b];
+    const SeqShape sh = seq_shape(a.cu, b, a.k, a.G);
+    const int U_b = sh.row_groups * a.Hkv;
+    if (u >= U_b) return;
+    const long long total = a.prefix[a.B];
+    const int iters_b = (a.prefix[b + 1] - a.prefix[b]) / U_b;
     if (iters_b <= 0) return;
-    const long long S = static_cast<long long>(a.U) * a.prefix[b] + static_cast<long long>(u) * iters_b;
+    const long long S = static_cast<long long>(a.prefix[b]) + static_cast<long long>(u) * iters_b;
     const long long E = S + iters_b;
     const int w0 = range_owner(S, total, a.P), w1 = range_owner(E - 1, total, a.P);
     if (w0 == w1) return;                      // one workgroup wrote the output directly
     const int first_slot = (S == range_start(w0, total, a.P)) ? 0 : 1;
-    const int g = u / a.row_groups, rg = u % a.row_groups;
+    const int g = u / sh.row_groups, rg = u % sh.row_groups;
     const int tid = threadIdx.x;
     for (int n = 0; n < tiles; ++n) {
         const int r = tid / 16;
         const int d0 = (tid % 16) * (D / 16);
         const int row = rg * 32 + n * 16 + r;
-        if (row >= a.rows) continue;
+        if (row >= sh.rows) continue;
         float M = -INFINITY;
         for (int ww = w0; ww <= w1; ++ww) {
             const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * 32 + n * 16 + r;
@@ -420,7 +466,7 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
         }
         const int i = row / a.G;
         const int h = g * a.G + row % a.G;
-        uint16_t* op = a.out + ((size_t(b) * (a.k + 1) + i) * a.Hq + h) * D + d0;
+        uint16_t* op = a.out + ((size_t(sh.row0) + i) * a.Hq + h) * D + d0;
         const float inv = 1.0f / lsum;
 #pragma unroll
         for (int dd = 0; dd < D / 16; ++dd) op[dd] = f32_to_bf16_bits(acc[dd] * inv);
@@ -477,6 +523,7 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     a.vc = static_cast<const uint16_t*>(p.v_cache);
     a.bt = p.block_table;
     a.seq_lens = p.seq_lens;
+    a.cu = p.cu_drafts;
     a.out = static_cast<uint16_t*>(p.out);
     char* ws = static_cast<char*>(p.workspace);
     a.prefix = reinterpret_cast<int32_t*>(ws);
@@ -497,7 +544,8 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     a.scale_log2 = p.sm_scale * kLog2e;
 
     if (p.B > kLdsPrefix) {
-        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAT), 0, stream, p.seq_lens, p.B, p.k, a.prefix);
+        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAT), 0, stream, p.seq_lens, p.cu_drafts, p.B, p.k, a.G,
+                           p.Hkv, a.prefix);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -13,8 +13,9 @@ struct AttnLaunch {
     const void* v_cache;
     const int32_t* block_table;
     const int32_t* seq_lens;
+    const int32_t* cu_drafts;   // [B+1] draft-count offsets (ragged k), or NULL: k drafts each
     void* out;
-    int B, k, Hq, Hkv, D, block_size, max_blocks, num_blocks, max_seq_len;
+    int B, k, Hq, Hkv, D, block_size, max_blocks, num_blocks, max_seq_len;   // k: the largest k_b
     float sm_scale;
     void* workspace;
 };
@@ -37,7 +38,8 @@ struct RejectLaunch {
     const int32_t* draft_tokens;
     const int64_t* seq_ids;
     const int32_t* seq_lens;
-    int B, k, V;
+    const int32_t* cu_drafts;   // [B+1] draft-count offsets (ragged k), or NULL: k drafts each
+    int B, k, V;                // k: the largest k_b
     float temperature;
     uint64_t seed;
     int32_t* out_tokens;

@@ -67,6 +67,7 @@ struct RejectArgs {
     const int32_t* draft_tokens;
     const int64_t* seq_ids;
     const int32_t* seq_lens;
+    const int32_t* cu;                 // [B+1] draft-count offsets, or null: k drafts each
     int32_t* out_tokens;
     int32_t* num_accepted;
     float* out_probs;
@@ -522,6 +523,8 @@ __device__ __forceinline__ void load_weights(bool two_rows, bool residual, const
 
 struct SeqCtx {
     int b;
+    int kb;                   // drafts of this sequence
+    size_t tb, db;            // its first target (and output) row, its first draft row
     int u;                    // unit of this wavefront: q * kUnitWaves + wave
     int q;                    // workgroup of the group
     int wave;                 // wavefront of the workgroup
@@ -710,8 +713,8 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
         zy = prow[y];
     }
     const double py = exp_nonpos_f64((static_cast<double>(zy) - M_ref) * c.invT64) / Zp_true;
-    const int k = a.k, b = s.b;
-    const size_t ob = size_t(b) * (k + 1);
+    const int k = s.kb;
+    const size_t ob = s.tb;
     a.out_tokens[ob + row] = y;
     if (a.out_probs) a.out_probs[ob + row] = static_cast<float>(py);
     for (int i = row + 1; i <= k; ++i) {
@@ -719,8 +722,8 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
         if (a.out_probs) a.out_probs[ob + i] = 0.0f;
     }
     if (a.accept_probs)
-        for (int i = row + 1; i < k; ++i) a.accept_probs[size_t(b) * k + i] = -1.0f;
-    a.num_accepted[b] = row;
+        for (int i = row + 1; i < k; ++i) a.accept_probs[s.db + i] = -1.0f;
+    a.num_accepted[s.b] = row;
 }
 
 // Reads wave 0's sampling decision and runs the final scan in the owning
@@ -828,7 +831,6 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
 // writes the outputs of the test.
 __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, int j, const RowStats& st,
                                             const TokenLogits& tl) {
-    const int k = a.k, b = s.b;
     double ep = 0.0, eq = 0.0;   // p and q of the token times Z_p and Z_q
     if (tl.ok) {
         ep = exp_nonpos_f64((static_cast<double>(tl.zp) - st.Mp) * a.invT64);
@@ -840,10 +842,10 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
     if (s.q == 0 && lane_id() == 0) {
         const double p_d = ep / st.Zp, q_d = eq / st.Zq;
         const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
-        if (a.accept_probs) a.accept_probs[size_t(b) * k + j] = static_cast<float>(fmin(1.0, ratio));
+        if (a.accept_probs) a.accept_probs[s.db + j] = static_cast<float>(fmin(1.0, ratio));
         if (accepted) {
-            a.out_tokens[size_t(b) * (k + 1) + j] = tl.tok;
-            if (a.out_probs) a.out_probs[size_t(b) * (k + 1) + j] = static_cast<float>(p_d);
+            a.out_tokens[s.tb + j] = tl.tok;
+            if (a.out_probs) a.out_probs[s.tb + j] = static_cast<float>(p_d);
         }
     }
     return accepted;
@@ -870,7 +872,7 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
     tok.ok = false;
     float ztp = 0.0f, ztq = 0.0f;
     if (s.wave == 0) {
-        tok.tok = load_uniform(a.draft_tokens, size_t(s.b) * a.k + row);
+        tok.tok = load_uniform(a.draft_tokens, s.db + row);
         tok.ok = tok.tok >= 0 && tok.tok < a.V;
         if (tok.ok) {
             ztp = load_uniform(prow, tok.tok);
@@ -948,7 +950,7 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
 template <bool kVec4>
 __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
                                           Shared& sh, bool& counted) {
-    const int row = a.k;
+    const int row = s.kb;
     const float* prow = s.prow_base + size_t(row) * a.V;
     const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, a.V);
     load_unit<kVec4, false>(rp, rp, a.V, s.u, xp, xq);
@@ -1054,14 +1056,24 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f4 xp[kVecs], xq[kVecs];
     for (int b = group; b < a.B; b += a.groups) {
         s.b = b;
-        s.prow_base = a.target + size_t(b) * (a.k + 1) * a.V;
-        s.qrow_base = a.draft + size_t(b) * a.k * a.V;
+        if (a.cu) {   // ragged: k_b drafts, rows packed by the offsets
+            const int c0 = load_uniform(a.cu, b), c1 = load_uniform(a.cu, size_t(b) + 1);
+            s.kb = min(max(c1 - c0, 0), a.k);
+            s.db = static_cast<size_t>(c0);
+            s.tb = static_cast<size_t>(c0) + b;
+        } else {
+            s.kb = a.k;
+            s.db = size_t(b) * a.k;
+            s.tb = size_t(b) * (a.k + 1);
+        }
+        s.prow_base = a.target + s.tb * a.V;
+        s.qrow_base = a.draft + s.db * a.V;
         // scalar loads, first waited for at the first acceptance test
         s.sid = load_uniform(a.seq_ids, b);
         s.L = load_uniform(a.seq_lens, b);
         RowStats st;
         bool done = false;
-        for (int j = 0; j < a.k && !done; ++j) {
+        for (int j = 0; j < s.kb && !done; ++j) {
             const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, sh, counted);
             if (res & kResError) {
                 flag_error(a, s);
@@ -1136,6 +1148,7 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.draft_tokens = p.draft_tokens;
     a.seq_ids = p.seq_ids;
     a.seq_lens = p.seq_lens;
+    a.cu = p.cu_drafts;
     a.out_tokens = p.out_tokens;
     a.num_accepted = p.num_accepted;
     a.out_probs = p.out_probs;
