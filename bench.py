@@ -13,7 +13,13 @@ work. Prints one JSON line:
             average duration from HIP events on the launch stream, vs 8 TB/s
   cpu_baseline  the fp64 oracle on this host's cores, on a bounded sample
 
+Also in that line, `cold_cache`: per-call HIP-event times of the same step with
+a 512 MiB write between steps, so that no logits or cache lines are left in
+the L2 or the 256 MiB MALL (the flush is outside the timed calls).
+
 Other modes:
+  --variant plain              k = 0 on the same workload: plain decoding
+  --variant ragged             per-sequence draft lengths k_b ~ U{0..7}
   --cpu-baseline-only          time the oracle (run in a single-threaded child)
   --copy-calibration           also run an elementwise kernel of known traffic
                                (negation of 512 MiB fp32: 512 MiB read, 512 MiB
@@ -29,6 +35,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -58,17 +65,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(preset, seq_lens, num_accepted):
-    """Bytes the method itself must move (each K/V row, Q/O row, examined logits row once)."""
+def algorithmic_bytes(preset, seq_lens, num_accepted, draft_lens=None):
+    """Bytes the method itself must move (each K/V row, Q/O row, examined logits row once).
+
+    draft_lens: per-sequence k_b (ragged); the preset's k for every sequence if None."""
     import numpy as np
     L = np.asarray(seq_lens, dtype=np.int64)
     a = np.asarray(num_accepted, dtype=np.int64)
-    B, k, Hq, Hkv, D, bs, V = preset.B, preset.k, preset.Hq, preset.Hkv, preset.D, preset.block_size, preset.V
+    B, Hq, Hkv, D, bs, V = preset.B, preset.Hq, preset.Hkv, preset.D, preset.block_size, preset.V
+    k = np.full(B, preset.k, dtype=np.int64) if draft_lens is None else np.asarray(draft_lens, dtype=np.int64)
     n_keys = L + k + 1
-    attn = int(np.sum(n_keys) * Hkv * D * 2 * 2 + 2 * B * (k + 1) * Hq * D * 2
-               + np.sum((n_keys + bs - 1) // bs) * 4 + B * 4)
+    attn = int(np.sum(n_keys) * Hkv * D * 2 * 2 + 2 * np.sum(k + 1) * Hq * D * 2
+               + np.sum((n_keys + bs - 1) // bs) * 4 + B * 4 + (0 if draft_lens is None else (B + 1) * 4))
     rows = (a + 1) + np.minimum(a + 1, k)
-    reject = int(np.sum(rows) * V * 4 + B * (k * 4 + 8 + 4) + B * (k + 1) * 8 + B * (4 + k * 4))
+    reject = int(np.sum(rows) * V * 4 + np.sum(k) * 4 + B * (8 + 4) + np.sum(k + 1) * 8 + B * 4 + np.sum(k) * 4
+                 + (0 if draft_lens is None else (B + 1) * 4))
     commit = int(B * 4 * 3)
     return attn, reject, commit
 
@@ -241,6 +252,122 @@ def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, wri
 
 # ----------------------------------------------------------------------------- GPU benchmark
 
+def cold_cache_calls(step, dev, n: int) -> dict | None:
+    """Per-call HIP-event times over n steps, each preceded by a 512 MiB write that
+    evicts the L2 and the MALL (the write itself is outside the timed calls)."""
+    import torch
+    if n <= 0:
+        return None
+    scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for _ in range(n):
+        scratch.fill_(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        rows.append(ev)
+    torch.cuda.synchronize()
+    del scratch
+    us = lambda i: sum(e[i].elapsed_time(e[i + 1]) for e in rows) / len(rows) * 1e3
+    return dict(steps=n, flush_bytes=1 << 29, verify_attn=dict(avg_us=us(0)), reject_sample=dict(avg_us=us(1)),
+                commit_lengths=dict(avg_us=us(2)))
+
+
+def gpu_bench_ragged(args, p, dev) -> dict:
+    """The 8B step with per-sequence draft lengths k_b ~ U{0..7} (packed rows)."""
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_14_amd as sv
+    from workloads import make_ragged_attention_inputs, make_ragged_reject_inputs
+
+    k_max = 7
+    print(f"[bench] generating ragged {args.workload} inputs (k_b in 0..{k_max})", file=sys.stderr, flush=True)
+    a = make_ragged_attention_inputs(p, k_max)
+    r = make_ragged_reject_inputs(p, k_max, draft_lens=a["draft_lens"])
+    assert np.array_equal(a["seq_lens"], r["seq_lens"])
+    bf16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    B = p.B
+    q, kc, vc, bt = bf16(a["q"]), bf16(a["k_cache"]), bf16(a["v_cache"]), t(a["block_table"])
+    del a["k_cache"], a["v_cache"]
+    cu = t(a["cu_drafts"])
+    seq_lens0 = t(a["seq_lens"])
+    seq_lens = seq_lens0.clone()
+    tl, dl, dt, sid = t(r["target_logits"]), t(r["draft_logits"]), t(r["draft_tokens"]), t(r["seq_ids"])
+    T, K = tl.shape[0], dl.shape[0]
+    attn_out = torch.empty_like(q)
+    out_tokens = torch.empty(T, dtype=torch.int32, device=dev)
+    out_probs = torch.empty(T, dtype=torch.float32, device=dev)
+    acc_probs = torch.empty(K, dtype=torch.float32, device=dev)
+    num_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    overflow = torch.empty(B, dtype=torch.int32, device=dev)
+    cap = a["max_blocks"] * p.block_size
+    msl = a["max_seq_len"]
+    attn_ws = torch.zeros(max(256, sv.verify_attn_workspace_size(B, k_max, p.Hq, p.Hkv, p.D, msl)),
+                          dtype=torch.uint8, device=dev)
+    rej_ws = torch.zeros(sv.reject_sample_workspace_size(B, k_max, p.V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        seq_lens.copy_(seq_lens0)
+        if events is not None:
+            events[0].record(stream)
+        sv.verify_attn_ragged(q, kc, vc, bt, seq_lens, cu, attn_out, k_max, msl, None, attn_ws, stream)
+        if events is not None:
+            events[1].record(stream)
+        sv.reject_sample_ragged(tl, dl, dt, cu, sid, seq_lens, k_max, p.temperature, r["seed"], out_tokens,
+                                num_acc, out_probs, acc_probs, rej_ws, stream)
+        if events is not None:
+            events[2].record(stream)
+        sv.commit_lengths(seq_lens, num_acc, k_max, cap, overflow, stream)
+        if events is not None:
+            events[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    acc_ref = num_acc.cpu().numpy().copy()
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    acc = num_acc.cpu().numpy()
+    if not np.array_equal(acc, acc_ref):
+        raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
+    mean = lambda v: sum(v) / len(v)
+    attn_s = mean([e[0].elapsed_time(e[1]) for e in evs.values()]) / 1e3
+    rej_s = mean([e[1].elapsed_time(e[2]) for e in evs.values()]) / 1e3
+    com_s = mean([e[2].elapsed_time(e[3]) for e in evs.values()]) / 1e3
+    a_bytes, r_bytes, _ = algorithmic_bytes(p, a["seq_lens"], acc, a["draft_lens"])
+    tokens = int(np.sum(acc + 1))
+    step_s = wall / args.steps
+    attn_gbs, rej_gbs = a_bytes / attn_s / 1e9, r_bytes / rej_s / 1e9
+    return dict(
+        metric=METRIC, value=tokens / step_s, unit="verified tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=step_s * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=(f"{args.workload} with ragged draft lengths: B={B}, k_b ~ U{{0..{k_max}}} "
+                              f"(sum {int(np.sum(a['draft_lens']))}), Hq={p.Hq}, Hkv={p.Hkv}, D={p.D}, "
+                              f"contexts {p.ctx}, block_size={p.block_size}, V={p.V}, T={p.temperature}, "
+                              "one attention layer + rejection sampling + commit"),
+                    global_batch=B, k="ragged", parallelism="none (1 GPU)"),
+        roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
+                      traffic=None, kernel="spec_verify_attn_ragged (attn_streamk_kernel + attn_merge_kernel)",
+                      algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_s * 1e6),
+        verified_tokens_per_step=tokens,
+        kernels=dict(verify_attn=dict(avg_us=attn_s * 1e6, bytes=a_bytes, gbs=attn_gbs,
+                                      frac_of_peak=attn_gbs / HBM_PEAK_GBS),
+                     reject_sample=dict(avg_us=rej_s * 1e6, bytes=r_bytes, gbs=rej_gbs,
+                                        frac_of_peak=rej_gbs / HBM_PEAK_GBS),
+                     commit_lengths=dict(avg_us=com_s * 1e6)),
+        cold_cache=cold_cache_calls(step, dev, args.cold_steps),
+    )
+
+
 def gpu_bench(args) -> dict:
     import numpy as np
     import torch
@@ -252,8 +379,12 @@ def gpu_bench(args) -> dict:
     sv.library()
     dev = torch.device("cuda:0")
     p = PRESETS[args.workload]
-    print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
-    inp = make_inputs(args.workload)
+    if args.variant == "plain":
+        p = dataclasses.replace(p, k=0)
+    if args.variant == "ragged":
+        return gpu_bench_ragged(args, p, dev)
+    print(f"[bench] generating {args.workload} inputs (k = {p.k})", file=sys.stderr, flush=True)
+    inp = make_inputs(args.workload, preset=p)
 
     def bf16(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -265,13 +396,15 @@ def gpu_bench(args) -> dict:
     bt = t(inp["block_table"])
     seq_lens0 = t(inp["seq_lens"])
     seq_lens = seq_lens0.clone()
-    tl, dl, dt, sid = t(inp["target_logits"]), t(inp["draft_logits"]), t(inp["draft_tokens"]), t(inp["seq_ids"])
+    tl, sid = t(inp["target_logits"]), t(inp["seq_ids"])
+    dl = t(inp["draft_logits"]) if p.k > 0 else None
+    dt = t(inp["draft_tokens"]) if p.k > 0 else None
     B, k = p.B, p.k
     attn_out = torch.empty_like(q)
     out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
     num_acc = torch.empty(B, dtype=torch.int32, device=dev)
     out_probs = torch.empty((B, k + 1), dtype=torch.float32, device=dev)
-    acc_probs = torch.empty((B, k), dtype=torch.float32, device=dev)
+    acc_probs = torch.empty((B, k), dtype=torch.float32, device=dev) if k > 0 else None
     overflow = torch.empty(B, dtype=torch.int32, device=dev)
     cap = inp["max_blocks"] * p.block_size
     msl = inp["max_seq_len"]
@@ -319,6 +452,7 @@ def gpu_bench(args) -> dict:
     acc = num_acc.cpu().numpy()
     if not np.array_equal(acc, acc_ref):
         raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
+    cold = cold_cache_calls(step, dev, args.cold_steps)
 
     copy_info = None
     if args.copy_calibration:
@@ -365,6 +499,13 @@ def gpu_bench(args) -> dict:
         event_sum_ms_per_step=(attn_avg_s + rej_avg_s + com_avg_s) * 1e3,
         event_sampled_steps=len(evs),
     )
+    if cold:
+        cold["verify_attn"]["frac_of_peak"] = a_bytes / (cold["verify_attn"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+        cold["reject_sample"]["frac_of_peak"] = r_bytes / (cold["reject_sample"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+        result["cold_cache"] = cold
+    if args.variant == "plain":
+        result["config"]["workload"] = result["config"]["workload"].replace(
+            "one attention layer", "k = 0 (plain decoding): one attention layer")
     if copy_info:
         result["copy_calibration"] = copy_info
     return result
@@ -376,6 +517,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="8b")
+    ap.add_argument("--variant", choices=["uniform", "plain", "ragged"], default="uniform")
+    ap.add_argument("--cold-steps", type=int, default=30,
+                    help="steps timed per call after a cache-evicting write (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -401,13 +545,13 @@ def main():
         print(json.dumps(cpu_baseline(args.workload)))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the verify step is data parallel over sequences; see the sharding notes in DESIGN.md)",
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the verify step is data parallel over sequences, one GPU's share is measured here)",
               file=sys.stderr)
         sys.exit(2)
 
     result = gpu_bench(args)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.variant == "uniform":
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = run_cpu_baseline_child(args.workload)
         if cb is not None:

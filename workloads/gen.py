@@ -214,8 +214,9 @@ def make_reject_inputs(preset: Preset, seed: int | None = None, B: int | None = 
                 seed=verify_seed(preset))
 
 
-def make_inputs(name: str, seed: int | None = None, B: int | None = None, garbage: str = "finite") -> dict:
-    preset = PRESETS[name]
+def make_inputs(name: str, seed: int | None = None, B: int | None = None, garbage: str = "finite",
+                preset: Preset | None = None) -> dict:
+    preset = PRESETS[name] if preset is None else preset
     a = make_attention_inputs(preset, seed=seed, B=B, garbage=garbage)
     r = make_reject_inputs(preset, seed=seed, B=B, seq_lens=a["seq_lens"])
     out = dict(a)
