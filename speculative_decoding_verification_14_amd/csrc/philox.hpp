@@ -43,15 +43,23 @@ __host__ __device__ __forceinline__ double word_to_unit(uint32_t w) {
     return static_cast<double>(w >> 8) * (1.0 / 16777216.0);
 }
 
-// (u_acc, u_smp) for the token decided at absolute position `pos` of sequence `seq_id`.
-__host__ __device__ __forceinline__ void verify_uniforms(uint64_t seed, int64_t seq_id, int64_t pos,
-                                                         double* u_acc, double* u_smp) {
+// Words 0 and 1 as uniforms for counter (pos, seq_id lo, seq_id hi, stream).
+__host__ __device__ __forceinline__ void stream_uniforms(uint64_t seed, int64_t seq_id, int64_t pos, uint32_t stream,
+                                                         double* u0, double* u1) {
     const uint64_t sid = static_cast<uint64_t>(seq_id);
     const PhiloxWords w = philox4x32_10(static_cast<uint32_t>(pos), static_cast<uint32_t>(sid),
-                                        static_cast<uint32_t>(sid >> 32), 0u,
+                                        static_cast<uint32_t>(sid >> 32), stream,
                                         static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
-    *u_acc = word_to_unit(w.w[0]);
-    *u_smp = word_to_unit(w.w[1]);
+    *u0 = word_to_unit(w.w[0]);
+    *u1 = word_to_unit(w.w[1]);
+}
+
+// (u_acc, u_smp) for the token decided at absolute position `pos` of sequence `seq_id`
+// (stream 0). Tree verification draws the acceptance uniform of a node's i-th
+// candidate, i >= 2, from word 0 of stream i (stream 1 belongs to draft sampling).
+__host__ __device__ __forceinline__ void verify_uniforms(uint64_t seed, int64_t seq_id, int64_t pos,
+                                                         double* u_acc, double* u_smp) {
+    stream_uniforms(seed, seq_id, pos, 0u, u_acc, u_smp);
 }
 
 }  // namespace specverify

@@ -1,0 +1,190 @@
+"""Pins for the tree-verification oracle (CPU only).
+
+* A chain-shaped tree (one child per node) is the ordinary chain: the walk
+  reproduces the chain oracle's outputs decision for decision, and the tree mask
+  reproduces the causal verify attention.
+* A star (every draft a child of the root) sees only the cache, the root and
+  itself; attention is checked against a dense masked softmax built from scratch.
+* Over the 2^24 grid of one candidate's uniform, with the earlier candidates
+  rejected, the accept count equals ceil(r(x)/q(x) 2^24) for the residual r left by
+  those rejections, and the final draw's counts equal the residual's interval
+  widths: the walk uses the right uniform and the right residual at every step.
+* Monte Carlo, multi-round with the commit: generating tokens by repeated tree
+  rounds (branching 2, depth 2, children drawn i.i.d. from the draft) gives the
+  target Markov chain's joint law (chi-squared, fixed seeds): the walk is lossless.
+"""
+
+import math
+
+import numpy as np
+from scipy import stats
+
+from oracle import attention as oatt
+from oracle import commit as ocommit
+from oracle import reject as orej
+from oracle import tree as otree
+from oracle.philox import verify_uniforms
+from workloads import PRESETS, draft_from_logits, make_attention_inputs, make_reject_inputs
+
+GRID = 1 << 24
+
+
+def test_chain_shaped_tree_is_the_chain():
+    inp = make_reject_inputs(PRESETS["tiny"], B=6)
+    B, k = inp["B"], inp["k"]
+    parents = np.tile(np.arange(k, dtype=np.int32), (B, 1))          # node n's parent is n - 1
+    draft_rows = np.concatenate([inp["draft_logits"], inp["draft_logits"][:, :1]], axis=1)   # leaf row unused
+    for seed in range(40):
+        t = otree.verify_batch_tree(inp["target_logits"], draft_rows, inp["draft_tokens"], parents, inp["seq_ids"],
+                                    inp["seq_lens"], 1.0, seed)
+        c = orej.verify_batch(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["seq_ids"],
+                              inp["seq_lens"], k, 1.0, seed)
+        for key in ("out_tokens", "num_accepted", "out_probs", "accept_probs"):
+            np.testing.assert_array_equal(t[key], c[key], err_msg=key)
+        for b in range(B):
+            a = int(t["num_accepted"][b])
+            assert list(t["accepted_nodes"][b, :a]) == list(range(1, a + 1))
+
+
+def test_chain_shaped_tree_attention_is_causal_verify_attention():
+    a = make_attention_inputs(PRESETS["tiny"], B=3)
+    k = a["k"]
+    parents = np.tile(np.arange(k, dtype=np.int32), (3, 1))
+    t = otree.verify_attention_tree(a["q"], a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], parents,
+                                    a["Hq"], a["Hkv"], a["block_size"], a["sm_scale"])
+    c = oatt.verify_attention(a["q"], a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], k, a["Hq"],
+                              a["Hkv"], a["block_size"], a["sm_scale"])
+    np.testing.assert_allclose(t, c, rtol=0, atol=1e-14)
+
+
+def test_star_tree_attention_against_a_dense_masked_softmax():
+    a = make_attention_inputs(PRESETS["tiny"], B=2)
+    k, Hq, Hkv, D, bs = a["k"], a["Hq"], a["Hkv"], a["D"], a["block_size"]
+    parents = np.zeros((2, k), dtype=np.int32)                        # every draft hangs off the root
+    t = otree.verify_attention_tree(a["q"], a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], parents,
+                                    Hq, Hkv, bs, a["sm_scale"])
+    G = Hq // Hkv
+    for b in range(2):
+        L = int(a["seq_lens"][b])
+        n_keys = L + k + 1
+        for h in range(Hq):
+            g = h // G
+            # dense K, V from the block table, key by key
+            K = np.array([oatt.bf16_to_f64(a["k_cache"][a["block_table"][b, s // bs], g, s % bs]) for s in range(n_keys)])
+            Vv = np.array([oatt.bf16_to_f64(a["v_cache"][a["block_table"][b, s // bs], g, :, s % bs])
+                           for s in range(n_keys)])
+            for n in range(k + 1):
+                mask = np.zeros(n_keys, bool)
+                mask[:L + 1] = True                                   # cache and root
+                mask[L + n] = True                                    # itself
+                s = a["sm_scale"] * (K @ oatt.bf16_to_f64(a["q"][b, n, h]))
+                s[~mask] = -np.inf
+                w = np.exp(s - s.max())
+                want = (w / w.sum()) @ Vv
+                np.testing.assert_allclose(t[b, n, h], want, rtol=0, atol=1e-12)
+
+
+def _first_grid_point(pred):
+    lo, hi = 0, GRID
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if pred(mid):
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+def test_multi_candidate_step_over_the_uniform_grid():
+    rng = np.random.default_rng(3)
+    V = 6
+    p = orej.softmax_t(rng.standard_normal(V) * 1.5, 1.0)
+    q = orej.softmax_t(rng.standard_normal(V) * 1.5, 1.0)
+    # residuals after rejecting candidates, written out independently of the walk
+    r1 = np.maximum(0.0, p - q); r1 /= math.fsum(r1)
+    r2 = np.maximum(0.0, r1 - q); r2 /= math.fsum(r2)
+    # every candidate can be rejected (ratio < 1); candidate 3 still has residual mass
+    x1 = int(np.argmin(p / q))
+    x2 = int(np.argmin(r1 / q))
+    ok3 = np.where((r2 > 0) & (r2 / q < 1), r2 / q, -1.0)
+    x3 = int(np.argmax(ok3))
+    tokens = [x1, x2, x3]
+    assert p[x1] / q[x1] < 1 and r1[x2] / q[x2] < 1 and 0 < r2[x3] < q[x3]
+    r3 = np.maximum(0.0, r2 - q); r3 /= math.fsum(r3)
+    parents = [0, 0, 0]                                              # three candidates at the root
+    leaf = orej.softmax_t(np.zeros(V), 1.0)
+    p_of = lambda v: p if v == 0 else leaf
+    q_of = lambda v: q
+    REJ = 1.0 - 2.0 ** -24                                           # rejects unless the ratio is >= 1
+    for i, r in ((1, p), (2, r1), (3, r2)):
+        x = tokens[i - 1]
+        want = min(GRID, math.ceil(r[x] / q[x] * GRID))
+
+        def rejects(m, i=i):      # candidate i is node i
+            def uni(P, stream):
+                return (m / GRID if stream == (0 if i == 1 else i) else REJ, 0.0)
+            return otree.walk(p_of, q_of, tokens, parents, 10, uni).nodes[:1] != [i]
+        assert _first_grid_point(rejects) == want, (i, want)
+    # all three rejected: the final draw over the grid of u_smp has the widths of r3
+    C = np.cumsum(r3)
+
+    def draw(m):
+        return otree.walk(p_of, q_of, tokens, parents, 10, lambda P, s: (REJ, m / GRID)).tokens[0]
+    edges = [_first_grid_point(lambda m, y=y: draw(m) > y) for y in range(V)]
+    widths = np.diff([0] + edges)
+    want = np.diff(np.concatenate([[0], np.minimum([math.ceil(C[y] / C[-1] * GRID) for y in range(V)], GRID)]))
+    np.testing.assert_array_equal(widths, want)
+    assert np.all(widths[r3 == 0] == 0)
+
+
+def _tree_round(A, Bm, last, rng, t=2, depth=2):
+    """A draft tree of branching t and the given depth, children drawn i.i.d. from the draft
+    chain Bm at their parent's token; returns parents, tokens, target rows, draft rows."""
+    parents, toks, node_tok = [], [], [last]
+    frontier = [0]
+    for _ in range(depth):
+        nxt = []
+        for v in frontier:
+            for _ in range(t):
+                tok = int(draft_from_logits(rng, Bm[node_tok[v]][None], 1.0)[0])
+                parents.append(v)
+                toks.append(tok)
+                node_tok.append(tok)
+                nxt.append(len(node_tok) - 1)
+        frontier = nxt
+    tl = np.array([A[x] for x in node_tok], np.float32)
+    dl = np.array([Bm[x] for x in node_tok], np.float32)
+    return np.array(parents, np.int32), np.array(toks, np.int32), tl, dl
+
+
+def test_monte_carlo_lossless_tree_rounds_with_commit():
+    rng = np.random.default_rng(12)
+    V, n_tok, n = 3, 3, 20_000
+    A = (rng.standard_normal((V, V)) * 1.2).astype(np.float32)
+    Bm = (A + rng.standard_normal((V, V)) * 1.0).astype(np.float32)
+    P = np.array([orej.softmax_t(A[i], 1.0) for i in range(V)])
+    x0 = 2
+    counts = np.zeros((V,) * n_tok)
+    used = set()
+    for s in range(n):
+        seq, L = [x0], 10
+        while len(seq) - 1 < n_tok:
+            par, toks, tl, dl = _tree_round(A, Bm, seq[-1], rng)
+            out = otree.verify_batch_tree(tl[None], dl[None], toks[None], par[None], np.array([s]), np.array([L]),
+                                          1.0, 4321)
+            a = int(out["num_accepted"][0])
+            if s < 100:
+                for j in range(a + 1):
+                    assert (s, L + 1 + j) not in used
+                    used.add((s, L + 1 + j))
+            seq.extend(int(x) for x in out["out_tokens"][0, :a + 1])
+            L = int(ocommit.commit_lengths([L], [a], 10**9)[0][0])
+        counts[tuple(seq[1:n_tok + 1])] += 1
+    want = np.zeros_like(counts)
+    for idx in np.ndindex(*counts.shape):
+        pr, prev = 1.0, x0
+        for tkn in idx:
+            pr *= P[prev, tkn]
+            prev = tkn
+        want[idx] = pr
+    assert stats.chisquare(counts.ravel(), n * want.ravel()).pvalue > 1e-4

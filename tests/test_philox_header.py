@@ -1,6 +1,7 @@
 """The library's Philox header (compiled for the host) and the oracle's Philox are
 two independent implementations of the SC'11 definition; they must agree bit for
-bit on the verify keying (seed, sequence id, position). CPU only."""
+bit on the verify keying (seed, sequence id, position, stream: 0 for the chain, 2 ..
+for the later candidates of a tree node). CPU only."""
 
 import os
 import shutil
@@ -35,12 +36,14 @@ def test_header_matches_oracle(exe):
     seeds[:3] = [0, 2**64 - 1, 0x5EED0001]
     sids[:3] = [0, -1, 2**40 + 17]
     pos[:3] = [0, 2**31 - 2, 262147]
-    text = "\n".join(f"{int(s)} {int(i)} {int(p)}" for s, i, p in zip(seeds, sids, pos)) + "\n"
+    streams = np.where(rng.random(n) < 0.5, 0, rng.integers(2, 16, size=n))
+    text = "\n".join(f"{int(s)} {int(i)} {int(p)} {int(st)}" for s, i, p, st in zip(seeds, sids, pos, streams)) + "\n"
     lines = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
     for t in range(n):
         got = [int(float(x)) for x in lines[t].split()]
         sid = int(sids[t]) & (2**64 - 1)
         sd = int(seeds[t])
-        w = philox.philox4x32_10((int(pos[t]), sid & 0xFFFFFFFF, sid >> 32, 0), (sd & 0xFFFFFFFF, sd >> 32))
-        ua, us = philox.verify_uniforms(sd, int(sids[t]), int(pos[t]))
+        st = int(streams[t])
+        w = philox.philox4x32_10((int(pos[t]), sid & 0xFFFFFFFF, sid >> 32, st), (sd & 0xFFFFFFFF, sd >> 32))
+        ua, us = philox.verify_uniforms(sd, int(sids[t]), int(pos[t]), st)
         assert got == [*w, int(ua * 2**24), int(us * 2**24)], t
