@@ -20,6 +20,8 @@ the L2 or the 256 MiB MALL (the flush is outside the timed calls).
 Other modes:
   --variant plain              k = 0 on the same workload: plain decoding
   --variant ragged             per-sequence draft lengths k_b ~ U{0..7}
+  --variant tree [--tree T,D]  a full T-ary draft tree of depth D (default 2,2: six
+                               nodes) through the tree attention and the tree walk
   --cpu-baseline-only          time the oracle (run in a single-threaded child)
   --copy-calibration           also run an elementwise kernel of known traffic
                                (negation of 512 MiB fp32: 512 MiB read, 512 MiB
@@ -368,6 +370,131 @@ def gpu_bench_ragged(args, p, dev) -> dict:
     )
 
 
+def tree_shape(spec: str) -> tuple[int, int]:
+    t, d = (int(x) for x in spec.split(","))
+    return t, d
+
+
+def gpu_bench_tree(args, p, dev) -> dict:
+    """The 8B step over a full t-ary draft tree of depth d (the same tree for every sequence)."""
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_14_amd as sv
+    from workloads import make_tree_attention_inputs, make_tree_reject_inputs, tree_parents
+
+    t_br, depth = tree_shape(args.tree)
+    parents = tree_parents(t_br, depth)
+    N = int(parents.shape[0])
+    print(f"[bench] generating {args.workload} tree inputs (t = {t_br}, depth = {depth}, N = {N})",
+          file=sys.stderr, flush=True)
+    a = make_tree_attention_inputs(p, N)
+    r = make_tree_reject_inputs(p, parents)
+    assert np.array_equal(a["seq_lens"], r["seq_lens"])
+    bf16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    B = p.B
+    q, kc, vc, bt = bf16(a["q"]), bf16(a["k_cache"]), bf16(a["v_cache"]), t(a["block_table"])
+    del a["k_cache"], a["v_cache"]
+    par = t(r["parents"])
+    seq_lens0 = t(a["seq_lens"])
+    seq_lens = seq_lens0.clone()
+    tl, dl, dt, sid = t(r["target_logits"]), t(r["draft_logits"]), t(r["draft_tokens"]), t(r["seq_ids"])
+    del r["target_logits"], r["draft_logits"]
+    attn_out = torch.empty_like(q)
+    out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    out_probs = torch.empty((B, N + 1), dtype=torch.float32, device=dev)
+    acc_probs = torch.empty((B, N), dtype=torch.float32, device=dev)
+    acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    num_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    overflow = torch.empty(B, dtype=torch.int32, device=dev)
+    cap = a["max_blocks"] * p.block_size
+    msl = a["max_seq_len"]
+    attn_ws = torch.zeros(max(256, sv.verify_attn_workspace_size(B, N, p.Hq, p.Hkv, p.D, msl)),
+                          dtype=torch.uint8, device=dev)
+    rej_ws = torch.zeros(sv.reject_sample_tree_workspace_size(B, N, p.V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        seq_lens.copy_(seq_lens0)
+        if events is not None:
+            events[0].record(stream)
+        sv.verify_attn_tree(q, kc, vc, bt, seq_lens, par, attn_out, msl, None, attn_ws, stream)
+        if events is not None:
+            events[1].record(stream)
+        sv.reject_sample_tree(tl, dl, dt, par, sid, seq_lens, p.temperature, r["seed"], out_tokens, num_acc,
+                              acc_nodes, out_probs, acc_probs, rej_ws, stream)
+        if events is not None:
+            events[2].record(stream)
+        sv.commit_lengths(seq_lens, num_acc, N, cap, overflow, stream)
+        if events is not None:
+            events[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    acc_ref = num_acc.cpu().numpy().copy()
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    acc = num_acc.cpu().numpy()
+    nodes = acc_nodes.cpu().numpy()
+    if not np.array_equal(acc, acc_ref):
+        raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
+    mean = lambda v: sum(v) / len(v)
+    attn_s = mean([e[0].elapsed_time(e[1]) for e in evs.values()]) / 1e3
+    rej_s = mean([e[1].elapsed_time(e[2]) for e in evs.values()]) / 1e3
+    com_s = mean([e[2].elapsed_time(e[3]) for e in evs.values()]) / 1e3
+    a_bytes, _, _ = algorithmic_bytes(dataclasses.replace(p, k=N), a["seq_lens"], acc)
+    r_bytes = tree_reject_bytes(p, parents, acc, nodes)
+    tokens = int(np.sum(acc + 1))
+    step_s = wall / args.steps
+    attn_gbs, rej_gbs = a_bytes / attn_s / 1e9, r_bytes / rej_s / 1e9
+    return dict(
+        metric=METRIC, value=tokens / step_s, unit="verified tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=step_s * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=(f"{args.workload} with a draft tree: B={B}, full {t_br}-ary tree of depth {depth} "
+                              f"(N={N} draft nodes), Hq={p.Hq}, Hkv={p.Hkv}, D={p.D}, contexts {p.ctx}, "
+                              f"block_size={p.block_size}, V={p.V}, T={p.temperature}, "
+                              "one attention layer + tree walk + commit"),
+                    global_batch=B, k=f"tree {t_br}x{depth}", parallelism="none (1 GPU)"),
+        roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
+                      traffic=None, kernel="spec_verify_attn_tree (attn_streamk_kernel + attn_merge_kernel)",
+                      algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_s * 1e6),
+        verified_tokens_per_step=tokens,
+        mean_emitted_per_sequence=tokens / B,
+        kernels=dict(verify_attn=dict(avg_us=attn_s * 1e6, bytes=a_bytes, gbs=attn_gbs,
+                                      frac_of_peak=attn_gbs / HBM_PEAK_GBS),
+                     reject_sample=dict(avg_us=rej_s * 1e6, bytes=r_bytes, gbs=rej_gbs,
+                                        frac_of_peak=rej_gbs / HBM_PEAK_GBS),
+                     commit_lengths=dict(avg_us=com_s * 1e6)),
+        cold_cache=cold_cache_calls(step, dev, args.cold_steps),
+    )
+
+
+def tree_reject_bytes(preset, parents, num_accepted, accepted_nodes) -> int:
+    """Bytes the tree walk must read: the target row of every node on the walked path, and the
+    draft row of those that have children (their candidates are tested against it), plus the
+    token, parent, length and output arrays."""
+    import numpy as np
+    par = np.asarray(parents)
+    N, V, B = int(par.shape[-1]), preset.V, preset.B
+    has_kids = np.zeros(N + 1, dtype=bool)
+    has_kids[par] = True
+    rows = 0
+    for b in range(B):
+        path = [0] + [int(x) for x in accepted_nodes[b, :int(num_accepted[b])]]
+        rows += sum(2 if has_kids[v] else 1 for v in path)
+    return int(rows * V * 4 + B * N * 4 * 2 + B * (8 + 4) + B * (N + 1) * 8 + B * N * 8 + B * 4)
+
+
 def gpu_bench(args) -> dict:
     import numpy as np
     import torch
@@ -383,6 +510,8 @@ def gpu_bench(args) -> dict:
         p = dataclasses.replace(p, k=0)
     if args.variant == "ragged":
         return gpu_bench_ragged(args, p, dev)
+    if args.variant == "tree":
+        return gpu_bench_tree(args, p, dev)
     print(f"[bench] generating {args.workload} inputs (k = {p.k})", file=sys.stderr, flush=True)
     inp = make_inputs(args.workload, preset=p)
 
@@ -517,7 +646,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="8b")
-    ap.add_argument("--variant", choices=["uniform", "plain", "ragged"], default="uniform")
+    ap.add_argument("--variant", choices=["uniform", "plain", "ragged", "tree"], default="uniform")
+    ap.add_argument("--tree", default="2,2", metavar="T,D",
+                    help="tree variant: branching factor and depth of the full draft tree")
     ap.add_argument("--cold-steps", type=int, default=30,
                     help="steps timed per call after a cache-evicting write (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -216,6 +216,70 @@ spec_status spec_reject_sample_ragged(const float* target_logits, const float* d
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Tree verification  [RESP] (GAP 1: speculation with a branching factor t; the
+ * drafts form a tree that one target pass checks). The pages give neither the
+ * mask nor the acceptance rule; the ones below are multi-candidate speculative
+ * sampling (SpecInfer, Miao et al. 2024), which keeps the output distribution
+ * equal to the target's when each node's children were drawn independently from
+ * the draft distribution at that node.
+ *
+ * Tree of one sequence: node 0 is the last committed token (position L_b), nodes
+ * 1 .. N (N = nodes) are drafts; parents[b][n-1] in [0, n) is node n's parent, and
+ * node n sits at position L_b + depth(n). The children of a node, in index order,
+ * are its candidates; at most 4 per node.
+ *
+ * spec_verify_attn_tree: as spec_verify_attn with k = N (q, out [B][N+1][Hq][D];
+ * the caller has appended the KV rows of nodes 0 .. N at cache slots
+ * L_b .. L_b + N), except that node n attends the committed keys 0 .. L_b - 1 and
+ * the slots L_b + m of its ancestors m and itself (the tree mask). Workspace:
+ * spec_verify_attn_workspace_size(B, N, ...). 1 <= N <= 15.
+ *
+ * spec_reject_sample_tree: the walk. At node v (from the root) with children
+ * c_1 .. c_m: r = p_v; for i = 1 .. m accept c_i's token x iff u_i < r(x)/q_v(x)
+ * (q_v(x) = 0: +inf if r(x) > 0, else 0), u_1 = word 0 of Philox(P, seq, stream 0)
+ * and u_i = word 0 of stream i for i >= 2, P = L_b + depth(v) + 1; an accepted
+ * child continues the walk; after a rejection r = max(0, r - q_v) normalised (left
+ * unchanged if it sums to zero). If every child is rejected, the token at P is drawn
+ * from r with u_smp (word 1 of stream 0) and the walk stops; at a leaf, a bonus
+ * token is drawn from p_v with u_smp. A chain-shaped tree reproduces
+ * spec_reject_sample.
+ *
+ *  target_logits fp32 [B][N+1][V]  row n: target logits at node n
+ *  draft_logits  fp32 [B][N+1][V]  row v: draft logits at node v (the distribution
+ *                                  v's children were drawn from; rows of leaves unused)
+ *  draft_tokens  int32 [B][N]      token of node n at [n-1] (each < V)
+ *  parents       int32 [B][N]
+ *  out_tokens    int32 [B][N+1]    the accepted path's tokens, then the drawn token,
+ *                                  then -1
+ *  num_accepted  int32 [B]         a_b = depth of the last accepted node
+ *  accepted_nodes int32 [B][N] or NULL: the accepted nodes in path order, then -1
+ *                (their KV rows are the ones to keep at L_b+1 .. L_b+a_b before
+ *                the commit L' = L + a + 1; moving them is the caller's)
+ *  out_probs     fp32 [B][N+1] or NULL: p at the deciding node of each emitted token
+ *  accept_probs  fp32 [B][N]   or NULL: min(1, r(x)/q(x)) at each tested node, -1 else
+ *
+ * Shapes: 1 <= B <= 65535; 1 <= N <= 15; V as for spec_reject_sample. The parents
+ * are a device-side precondition (a node with more than 4 children, or a parent
+ * index out of range, ends that sequence with num_accepted = -1). Workspace:
+ * spec_reject_sample_tree_workspace_size(B, N, V).
+ * ---------------------------------------------------------------------- */
+spec_status spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* parents,
+                                  void* out, int32_t B, int32_t nodes, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t block_size, int32_t max_blocks, int32_t num_blocks,
+                                  int32_t max_seq_len, float sm_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+spec_status spec_reject_sample_tree_workspace_size(int32_t B, int32_t nodes, int32_t V, size_t* bytes_out);
+
+spec_status spec_reject_sample_tree(const float* target_logits, const float* draft_logits,
+                                    const int32_t* draft_tokens, const int32_t* parents, const int64_t* seq_ids,
+                                    const int32_t* seq_lens, int32_t B, int32_t nodes, int32_t V,
+                                    float temperature, uint64_t seed, int32_t* out_tokens, int32_t* num_accepted,
+                                    int32_t* accepted_nodes, float* out_probs, float* accept_probs,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Commit  [ACC] (accepted length per step), [RESP] (KV cache extended in place).
  *
  * seq_lens[b] <- seq_lens[b] + num_accepted[b] + 1, unless that exceeds

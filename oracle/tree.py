@@ -100,13 +100,14 @@ class TreeResult:
     out_probs: list         # p_v(token) at the node each token was decided at
     accept_probs: dict      # node -> min(1, r(x)/q(x)) for every tested node
     decisions: list
+    decision_nodes: list    # the tested node of each acceptance decision (-1 for a draw)
 
 
 def walk(p_of, q_of, tokens, parents, L: int, uni) -> TreeResult:
     """The walk of T3. p_of(v) / q_of(v): target / draft distributions at node v;
     tokens[n-1]: token of node n; uni(P, stream) -> (word-0 unit, word-1 unit) (T4)."""
     v, depth = 0, 0
-    out, nodes, probs, acc_probs, dec = [], [], [], {}, []
+    out, nodes, probs, acc_probs, dec, dnodes = [], [], [], {}, [], []
     while True:
         P = L + depth + 1
         p = p_of(v)
@@ -114,9 +115,10 @@ def walk(p_of, q_of, tokens, parents, L: int, uni) -> TreeResult:
         if not ch:
             y, margin = inverse_cdf(p, uni(P, 0)[1])
             dec.append(Decision("sample", depth, y, margin))
+            dnodes.append(-1)
             out.append(y)
             probs.append(float(p[y]))
-            return TreeResult(out, depth, nodes, probs, acc_probs, dec)
+            return TreeResult(out, depth, nodes, probs, acc_probs, dec, dnodes)
         q = q_of(v)
         r = p
         moved = False
@@ -128,6 +130,7 @@ def walk(p_of, q_of, tokens, parents, L: int, uni) -> TreeResult:
             acc_probs[c] = min(1.0, ratio)
             accepted = u < ratio
             dec.append(Decision("accept", depth, int(accepted), math.inf if math.isinf(ratio) else abs(u - ratio)))
+            dnodes.append(c)
             if accepted:
                 out.append(x)
                 probs.append(float(p[x]))
@@ -140,9 +143,10 @@ def walk(p_of, q_of, tokens, parents, L: int, uni) -> TreeResult:
         if not moved:
             y, margin = inverse_cdf(r, uni(P, 0)[1])
             dec.append(Decision("sample", depth, y, margin))
+            dnodes.append(-1)
             out.append(y)
             probs.append(float(p[y]))
-            return TreeResult(out, depth, nodes, probs, acc_probs, dec)
+            return TreeResult(out, depth, nodes, probs, acc_probs, dec, dnodes)
 
 
 def verify_batch_tree(target_logits, draft_logits, draft_tokens, parents, seq_ids, seq_lens,

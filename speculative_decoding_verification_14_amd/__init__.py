@@ -17,7 +17,8 @@ import threading
 
 __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", "reject_sample",
            "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
-           "reject_sample_ragged", "LIB_PATH", "SYMBOLS"]
+           "reject_sample_ragged", "verify_attn_tree", "reject_sample_tree", "reject_sample_tree_workspace_size",
+           "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
 
@@ -37,6 +38,10 @@ SYMBOLS = {
     "spec_verify_attn_ragged": (_c_int32, [_vp] * 7 + [_c_int32] * 9 + [ctypes.c_float, _vp, _c_size, _vp]),
     "spec_reject_sample_ragged": (_c_int32, [_vp] * 6 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
                                   + [_vp] * 5 + [_c_size, _vp]),
+    "spec_verify_attn_tree": (_c_int32, [_vp] * 7 + [_c_int32] * 9 + [ctypes.c_float, _vp, _c_size, _vp]),
+    "spec_reject_sample_tree_workspace_size": (_c_int32, [_c_int32] * 3 + [ctypes.POINTER(_c_size)]),
+    "spec_reject_sample_tree": (_c_int32, [_vp] * 6 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
+                                + [_vp] * 6 + [_c_size, _vp]),
 }
 
 
@@ -202,6 +207,66 @@ def reject_sample_ragged(target_logits, draft_logits, draft_tokens, cu_drafts, s
                                          _opt(accept_probs, torch.float32, "accept_probs"),
                                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                          _stream_handle(stream)), "spec_reject_sample_ragged")
+    return out_tokens, num_accepted
+
+
+def verify_attn_tree(q, k_cache, v_cache, block_table, seq_lens, parents, out, max_seq_len: int,
+                     sm_scale: float | None = None, workspace=None, stream=None):
+    """spec_verify_attn_tree. q/out bf16 [B][N+1][Hq][D] (node n's row; the cache holds the KV of
+    nodes 0 .. N at slots L_b .. L_b + N); parents int32 [B][N] on the device."""
+    import torch
+    B, N1, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    lib = library()
+    need = verify_attn_workspace_size(B, N1 - 1, Hq, Hkv, D, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = _workspace("attn", q.device, need)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.spec_verify_attn_tree(_need(q, torch.bfloat16, "q"), _need(k_cache, torch.bfloat16, "k_cache"),
+                                     _need(v_cache, torch.bfloat16, "v_cache"),
+                                     _need(block_table, torch.int32, "block_table"),
+                                     _need(seq_lens, torch.int32, "seq_lens"), _need(parents, torch.int32, "parents"),
+                                     _need(out, torch.bfloat16, "out"),
+                                     B, N1 - 1, Hq, Hkv, D, bs, max_blocks, NB, int(max_seq_len), scale,
+                                     wptr, wbytes, _stream_handle(stream)), "spec_verify_attn_tree")
+    return out
+
+
+def reject_sample_tree_workspace_size(B, nodes, V) -> int:
+    n = _c_size(0)
+    _check(library().spec_reject_sample_tree_workspace_size(B, nodes, V, ctypes.byref(n)),
+           "spec_reject_sample_tree_workspace_size")
+    return n.value
+
+
+def reject_sample_tree(target_logits, draft_logits, draft_tokens, parents, seq_ids, seq_lens, temperature: float,
+                       seed: int, out_tokens, num_accepted, accepted_nodes=None, out_probs=None, accept_probs=None,
+                       workspace=None, stream=None):
+    """spec_reject_sample_tree. target / draft fp32 [B][N+1][V] (one row per node); draft_tokens,
+    parents int32 [B][N]; out_tokens int32 [B][N+1]; accepted_nodes int32 [B][N]; out_probs fp32
+    [B][N+1]; accept_probs fp32 [B][N]."""
+    import torch
+    B, N1, V = target_logits.shape
+    lib = library()
+    need = reject_sample_tree_workspace_size(B, N1 - 1, V)
+    if workspace is None:
+        workspace = _workspace("reject_tree", target_logits.device, need)
+    _check(lib.spec_reject_sample_tree(_need(target_logits, torch.float32, "target_logits"),
+                                       _need(draft_logits, torch.float32, "draft_logits"),
+                                       _need(draft_tokens, torch.int32, "draft_tokens"),
+                                       _need(parents, torch.int32, "parents"),
+                                       _need(seq_ids, torch.int64, "seq_ids"), _need(seq_lens, torch.int32, "seq_lens"),
+                                       B, N1 - 1, V, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                       _need(out_tokens, torch.int32, "out_tokens"),
+                                       _need(num_accepted, torch.int32, "num_accepted"),
+                                       _opt(accepted_nodes, torch.int32, "accepted_nodes"),
+                                       _opt(out_probs, torch.float32, "out_probs"),
+                                       _opt(accept_probs, torch.float32, "accept_probs"),
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream)), "spec_reject_sample_tree")
     return out_tokens, num_accepted
 
 

@@ -59,7 +59,8 @@ spec_status from_hip(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR
 namespace {
 
 spec_status verify_attn_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                             const int32_t* seq_lens, const int32_t* cu_drafts, void* out, int32_t B, int32_t k,
+                             const int32_t* seq_lens, const int32_t* cu_drafts, const int32_t* parents, void* out,
+                             int32_t B, int32_t k,
                              int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
                              int32_t num_blocks, int32_t max_seq_len, float sm_scale, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -75,7 +76,7 @@ spec_status verify_attn_impl(const void* q, const void* k_cache, const void* v_c
     if ((s = check_device()) != SPEC_OK) return s;
     AttnLaunch p;
     p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
-    p.block_table = block_table; p.seq_lens = seq_lens; p.cu_drafts = cu_drafts; p.out = out;
+    p.block_table = block_table; p.seq_lens = seq_lens; p.cu_drafts = cu_drafts; p.parents = parents; p.out = out;
     p.B = B; p.k = k; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
     p.block_size = block_size; p.max_blocks = max_blocks; p.num_blocks = num_blocks;
     p.max_seq_len = max_seq_len; p.sm_scale = sm_scale;
@@ -99,7 +100,7 @@ spec_status reject_impl(const float* target_logits, const float* draft_logits, c
     if (s != SPEC_OK) return s;
     RejectLaunch p;
     p.target_logits = target_logits; p.draft_logits = draft_logits; p.draft_tokens = draft_tokens;
-    p.seq_ids = seq_ids; p.seq_lens = seq_lens; p.cu_drafts = cu_drafts;
+    p.seq_ids = seq_ids; p.seq_lens = seq_lens; p.cu_drafts = cu_drafts; p.parents = nullptr; p.out_nodes = nullptr;
     p.B = B; p.k = k; p.V = V; p.temperature = temperature; p.seed = seed;
     p.out_tokens = out_tokens; p.num_accepted = num_accepted;
     p.out_probs = out_probs; p.accept_probs = accept_probs;
@@ -143,8 +144,9 @@ spec_status spec_verify_attn(const void* q, const void* k_cache, const void* v_c
                              int32_t block_size, int32_t max_blocks, int32_t num_blocks,
                              int32_t max_seq_len, float sm_scale,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, nullptr, out, B, k, Hq, Hkv, D, block_size,
-                            max_blocks, num_blocks, max_seq_len, sm_scale, workspace, workspace_bytes, stream);
+    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, nullptr, nullptr, out, B, k, Hq, Hkv, D,
+                            block_size, max_blocks, num_blocks, max_seq_len, sm_scale, workspace, workspace_bytes,
+                            stream);
 }
 
 spec_status spec_verify_attn_ragged(const void* q, const void* k_cache, const void* v_cache,
@@ -154,7 +156,20 @@ spec_status spec_verify_attn_ragged(const void* q, const void* k_cache, const vo
                                     int32_t max_seq_len, float sm_scale,
                                     void* workspace, size_t workspace_bytes, void* stream) {
     if (!cu_drafts) return SPEC_ERR_NULL_POINTER;
-    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, cu_drafts, out, B, max_k, Hq, Hkv, D,
+    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, cu_drafts, nullptr, out, B, max_k, Hq, Hkv,
+                            D, block_size, max_blocks, num_blocks, max_seq_len, sm_scale, workspace, workspace_bytes,
+                            stream);
+}
+
+spec_status spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* parents,
+                                  void* out, int32_t B, int32_t nodes, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t block_size, int32_t max_blocks, int32_t num_blocks,
+                                  int32_t max_seq_len, float sm_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!parents) return SPEC_ERR_NULL_POINTER;
+    if (nodes < 1) return SPEC_ERR_BAD_SHAPE;
+    return verify_attn_impl(q, k_cache, v_cache, block_table, seq_lens, nullptr, parents, out, B, nodes, Hq, Hkv, D,
                             block_size, max_blocks, num_blocks, max_seq_len, sm_scale, workspace, workspace_bytes,
                             stream);
 }
@@ -188,6 +203,38 @@ spec_status spec_reject_sample_ragged(const float* target_logits, const float* d
     return reject_impl(target_logits, draft_logits, draft_tokens, cu_drafts, seq_ids, seq_lens, B, max_k, V,
                        temperature, seed, out_tokens, num_accepted, out_probs, accept_probs, workspace,
                        workspace_bytes, stream);
+}
+
+spec_status spec_reject_sample_tree_workspace_size(int32_t B, int32_t nodes, int32_t V, size_t* bytes_out) {
+    if (!bytes_out) return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || B > 65535 || nodes < 1 || nodes > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
+    *bytes_out = reject_tree_workspace_bytes(B, nodes, V);
+    return SPEC_OK;
+}
+
+spec_status spec_reject_sample_tree(const float* target_logits, const float* draft_logits,
+                                    const int32_t* draft_tokens, const int32_t* parents, const int64_t* seq_ids,
+                                    const int32_t* seq_lens, int32_t B, int32_t nodes, int32_t V,
+                                    float temperature, uint64_t seed, int32_t* out_tokens, int32_t* num_accepted,
+                                    int32_t* accepted_nodes, float* out_probs, float* accept_probs,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 1 || B > 65535 || nodes < 1 || nodes > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
+    if (!target_logits || !draft_logits || !draft_tokens || !parents || !seq_ids || !seq_lens || !out_tokens ||
+        !num_accepted || !workspace)
+        return SPEC_ERR_NULL_POINTER;
+    if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
+    if (workspace_bytes < reject_tree_workspace_bytes(B, nodes, V)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    RejectLaunch p;
+    p.target_logits = target_logits; p.draft_logits = draft_logits; p.draft_tokens = draft_tokens;
+    p.seq_ids = seq_ids; p.seq_lens = seq_lens; p.cu_drafts = nullptr; p.parents = parents;
+    p.out_nodes = accepted_nodes;
+    p.B = B; p.k = nodes; p.V = V; p.temperature = temperature; p.seed = seed;
+    p.out_tokens = out_tokens; p.num_accepted = num_accepted;
+    p.out_probs = out_probs; p.accept_probs = accept_probs;
+    p.workspace = workspace;
+    return from_hip(launch_reject_tree(p, static_cast<hipStream_t>(stream)));
 }
 
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,

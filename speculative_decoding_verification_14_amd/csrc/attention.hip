@@ -29,6 +29,10 @@
 //    segment in workgroup order (deterministic).
 //  * Inside a piece the four waves take interleaved 32-key blocks; at the end the
 //    waves' (max, sum, O) are combined through LDS.
+//  * Tree verification ("ReSpec: Towards Optimizing Speculative Decoding in
+//    Reinforcement Learning Systems", GAP 1: speculation with a branching factor)
+//    replaces the causal mask inside the draft by the tree mask: node n's row sees
+//    the committed keys and the slots L + m of its ancestors m (and itself).
 //  * Ragged draft lengths (k_b per sequence, rows packed by an offsets array) use
 //    the same kernels: a sequence contributes (k_b+1) x G rows, ceil of that / 32
 //    row groups per KV head, and L_b + k_b + 1 keys to the flat work order, so
@@ -56,6 +60,7 @@ struct AttnArgs {
     const int32_t* bt;
     const int32_t* seq_lens;
     const int32_t* cu;   // [B+1] draft-count offsets, or null: every sequence has k drafts
+    const int32_t* parents;   // tree: [B][k] parent of node n at [n-1], or null (causal chain)
     uint16_t* out;
     float* part_o;     // [kMaxP][2][32 rows][D]
     float* part_ml;    // [kMaxP][2][32 rows][2]
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(kAT) void attn_plan_kernel(const int32_t* seq_lens,
     build_prefix(seq_lens, cu, B, k, G, Hkv, prefix, s_wave);
 }
 
-template <int D, int NT>
+template <int D, int NT, bool kTree>
 __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
     constexpr int DS = D / 32;   // k-steps of S^T = K Q^T
     constexpr int DJ = D / 16;   // 16-dim blocks of O^T
@@ -221,9 +226,29 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
         const int c0 = it0 * kIterKeys;
         const int c1 = min(N, it1 * kIterKeys);
 
+        // Tree: ancestor-or-self masks of the nodes (bit m: slot L + m is visible),
+        // built from the parents with uniform loads; the chain sees every slot <= L + i.
+        unsigned anc_all[16];
+        if (kTree) {
+            anc_all[0] = 1u;
+#pragma unroll
+            for (int n = 1; n < 16; ++n) {
+                unsigned m = 1u << n;
+                if (n <= sh.kb) {
+                    int par = a.parents[size_t(b) * a.k + n - 1];
+                    par = par < 0 ? 0 : (par >= n ? n - 1 : par);   // a broken tree stays in range
+#pragma unroll
+                    for (int j = 0; j < n; ++j)
+                        if (j == par) m |= anc_all[j];
+                }
+                anc_all[n] = m;
+            }
+        }
+
         // Q^T operands and the last visible key of this lane's query row in each tile.
         bf16x8 qop[NT][DS];
         int lim[NT];
+        unsigned anc[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int r = rg * 32 + n * 16 + l16;
@@ -234,10 +259,17 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(load16(qp + 32 * ds));
                 lim[n] = L + i;
+                anc[n] = ~0u;
+                if (kTree) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (j == i) anc[n] = anc_all[j];
+                }
             } else {
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds) qop[n][ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
                 lim[n] = N - 1;   // padding rows: harmless finite result, never stored
+                anc[n] = ~0u;
             }
         }
 
@@ -310,7 +342,17 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
                             const int key = t0 + 8 * lg + i;
-                            if (key >= s1 || key > lim[n]) sv[i] = -INFINITY;
+                            bool hide;
+                            if constexpr (kTree) {
+                                // draft slot L + m is visible iff bit m of the ancestor mask is set; the
+                                // bits stop at the node itself, which covers the causal limit, and every
+                                // key < s1 lies below L + 16. Branch-free, with an in-range shift.
+                                const unsigned rel = static_cast<unsigned>(key - L);
+                                hide = (key >= s1) | ((rel < 32u) & (((anc[n] >> (rel & 31u)) & 1u) == 0u));
+                            } else {
+                                hide = key >= s1 || key > lim[n];
+                            }
+                            if (hide) sv[i] = -INFINITY;
                         }
                     }
                     float bmax = sv[0];
@@ -474,9 +516,9 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
 }
 
 // Persistent-grid size per (device, kernel instantiation): CUs x resident workgroups.
-int g_grid_memo[64][4];
+int g_grid_memo[64][8];
 
-template <int D, int NT>
+template <int D, int NT, bool kTree>
 int persistent_grid(int slot) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -487,7 +529,7 @@ int persistent_grid(int slot) {
     if (memo > 0) return memo;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_streamk_kernel<D, NT>, kAT, 0) != hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_streamk_kernel<D, NT, kTree>, kAT, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 256;
     }
@@ -524,6 +566,7 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     a.bt = p.block_table;
     a.seq_lens = p.seq_lens;
     a.cu = p.cu_drafts;
+    a.parents = p.parents;
     a.out = static_cast<uint16_t*>(p.out);
     char* ws = static_cast<char*>(p.workspace);
     a.prefix = reinterpret_cast<int32_t*>(ws);
@@ -550,23 +593,21 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
         if (e != hipSuccess) return e;
     }
     const dim3 block(kAT);
+    const bool tree = p.parents != nullptr;
+    const int slot = (p.D == 128 ? 0 : 4) + (geo.tiles == 1 ? 0 : 2) + (tree ? 1 : 0);
+#define SPEC_ATTN_LAUNCH(DD, NN, TT)                                                               \
+    do {                                                                                           \
+        a.P = persistent_grid<DD, NN, TT>(slot);                                                   \
+        hipLaunchKernelGGL((attn_streamk_kernel<DD, NN, TT>), dim3(a.P), block, 0, stream, a);     \
+    } while (0)
     if (p.D == 128) {
-        if (geo.tiles == 1) {
-            a.P = persistent_grid<128, 1>(0);
-            hipLaunchKernelGGL((attn_streamk_kernel<128, 1>), dim3(a.P), block, 0, stream, a);
-        } else {
-            a.P = persistent_grid<128, 2>(1);
-            hipLaunchKernelGGL((attn_streamk_kernel<128, 2>), dim3(a.P), block, 0, stream, a);
-        }
+        if (geo.tiles == 1) { if (tree) SPEC_ATTN_LAUNCH(128, 1, true); else SPEC_ATTN_LAUNCH(128, 1, false); }
+        else { if (tree) SPEC_ATTN_LAUNCH(128, 2, true); else SPEC_ATTN_LAUNCH(128, 2, false); }
     } else {
-        if (geo.tiles == 1) {
-            a.P = persistent_grid<64, 1>(2);
-            hipLaunchKernelGGL((attn_streamk_kernel<64, 1>), dim3(a.P), block, 0, stream, a);
-        } else {
-            a.P = persistent_grid<64, 2>(3);
-            hipLaunchKernelGGL((attn_streamk_kernel<64, 2>), dim3(a.P), block, 0, stream, a);
-        }
+        if (geo.tiles == 1) { if (tree) SPEC_ATTN_LAUNCH(64, 1, true); else SPEC_ATTN_LAUNCH(64, 1, false); }
+        else { if (tree) SPEC_ATTN_LAUNCH(64, 2, true); else SPEC_ATTN_LAUNCH(64, 2, false); }
     }
+#undef SPEC_ATTN_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid(a.U, p.B);

@@ -14,6 +14,7 @@ struct AttnLaunch {
     const int32_t* block_table;
     const int32_t* seq_lens;
     const int32_t* cu_drafts;   // [B+1] draft-count offsets (ragged k), or NULL: k drafts each
+    const int32_t* parents;     // tree: [B][k] parent of node n at [n-1] (tree mask), or NULL
     void* out;
     int B, k, Hq, Hkv, D, block_size, max_blocks, num_blocks, max_seq_len;   // k: the largest k_b
     float sm_scale;
@@ -39,7 +40,9 @@ struct RejectLaunch {
     const int64_t* seq_ids;
     const int32_t* seq_lens;
     const int32_t* cu_drafts;   // [B+1] draft-count offsets (ragged k), or NULL: k drafts each
-    int B, k, V;                // k: the largest k_b
+    const int32_t* parents;     // tree: [B][k] parent of node n at [n-1] (k = nodes), else NULL
+    int32_t* out_nodes;         // tree: [B][k] accepted nodes, or NULL
+    int B, k, V;                // k: the largest k_b (tree: the number of draft nodes)
     float temperature;
     uint64_t seed;
     int32_t* out_tokens;
@@ -52,6 +55,9 @@ struct RejectLaunch {
 size_t reject_workspace_bytes(int B, int k, int V);
 int reject_max_vocab();   // largest V the reject kernel accepts
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream);
+size_t reject_tree_workspace_bytes(int B, int nodes, int V);
+int reject_tree_max_branch();   // children per tree node the walk supports
+hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream);
 
 hipError_t launch_commit(int32_t* seq_lens, const int32_t* num_accepted, int B, int capacity,
                          int32_t* overflow_flags, hipStream_t stream);

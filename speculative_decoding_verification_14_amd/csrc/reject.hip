@@ -54,6 +54,8 @@ constexpr int kSampSlots = 8;              // A, B, P, Q (hi, lo each); bonus ro
 constexpr int kUnitWaves = 8;              // unit wavefronts per workgroup
 constexpr int kRT = kUnitWaves * kWave;    // 512 threads
 constexpr int kMaxQ = 32;                  // workgroups per sequence: U <= 256, i.e. V <= 2^20
+constexpr int kMaxBranch = 4;              // tree: children per node
+constexpr int kTreeEx = 24;                // tree: exchanges per sequence (levels, passes, the draw)
 constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this probability share use fp64
 constexpr unsigned kSpinLimit = 1u << 20;
 
@@ -75,6 +77,9 @@ struct RejectArgs {
     unsigned* ctl;                     // epoch of the last finished call, finished-wave count, error flag
     unsigned long long* stat_slots;    // [B][k+1][kStatSlots][Q]: workgroup statistics per level
     unsigned long long* samp_slots;    // [B][kSampSlots][Q]: workgroup sampling sums
+    const int32_t* parents;            // tree: [B][k] parent of node n at [n-1]; null for a chain
+    int32_t* out_nodes;                // tree: [B][k] accepted node indices, or null
+    unsigned long long* tree_slots;    // tree: [B][kTreeEx][kSampSlots][Q], one block per exchange
     int B, k, V, U, Q, groups;
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
@@ -613,51 +618,22 @@ __device__ __forceinline__ int find_crossing(double w, double carry, double t, d
     return l;
 }
 
-// Draw from the weights of this unit (residual of row `row`; p_row when `use_p` or
-// for the bonus row), given the running sum `run` before this unit and the
-// target t. Only the wavefront owning the crossing unit calls this; the lane
-// holding the drawn token writes it, its probability and the padding of the
-// sequence's outputs.
-template <bool kVec4>
-__device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, int row, bool two_rows,
-                                           const float* prow, const float* qrow, const SampleCtx& c,
-                                           const LoadSums& ls, bool use_p, bool exact, double run, double t,
-                                           double invZp, double invZq, double Zp_true, double wscale,
-                                           double M_ref) {
-    // wscale maps this unit's weights onto the scale of run and t (1, except for
-    // the bonus row, whose unit weights are relative to the unit's own maximum);
-    // M_ref is the row maximum the emitted probability is taken against.
+// Inverse CDF inside the crossing unit, given the running sum `run` before the
+// unit and the target t. lv(i, j0) returns the sum of the sampling weights of
+// load i over lanes j0 .. j0+15 (from the LDS slab, or recomputed); wf(vp, vq, w)
+// the weights of four logits, on the same scale as run and t. Returns true on the
+// one lane that holds the drawn token, with its id in y and its target logit in zy.
+template <bool kVec4, typename LV, typename WF>
+__device__ __forceinline__ bool scan_unit(const RejectArgs& a, const SeqCtx& s, const float* prow,
+                                          const float* qrow, bool two_rows, bool exact, double run, double t,
+                                          LV&& lv, WF&& wf, int& y, float& zy) {
     const int lane = lane_id();
     const int base = s.u * kUnit + lane * 4;
-    const bool residual = two_rows && !use_p;
     // Load level (each load of a wavefront is 256 consecutive tokens): load i's
     // total T_i is summed by the four lanes 4i..4i+3, sixteen per-lane sums each.
-    double Ti;
-    {
-        const int i = lane >> 2, j0 = (lane & 3) * (kWave / 4);
-        double v = 0.0;
-        if (!use_p) {
-#pragma unroll
-            for (int j = 0; j < kWave / 4; ++j) {
-                const double2 g = ls[i][j0 + j];
-                v += residual ? g.x * invZp - g.y * invZq : g.x;
-            }
-        } else {                 // zero residual (rare): p-weights of this load, recomputed
-#pragma unroll 1
-            for (int j = 0; j < kWave / 4; ++j) {
-                const int x = s.u * kUnit + i * (kWave * 4) + (j0 + j) * 4;
-                double w[4];
-                load_weights(two_rows, false, load4<kVec4>(row_rsrc(prow, a.V), a.V, x),
-                             two_rows ? load4<kVec4>(row_rsrc(qrow, a.V), a.V, x)
-                             : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, c, invZp, invZq, w);
-                v += (w[0] + w[1]) + (w[2] + w[3]);
-            }
-        }
-        v *= wscale;
-        v += __shfl_xor(v, 1, kWave);
-        v += __shfl_xor(v, 2, kWave);
-        Ti = v;
-    }
+    double Ti = lv(lane >> 2, (lane & 3) * (kWave / 4));
+    Ti += __shfl_xor(Ti, 1, kWave);
+    Ti += __shfl_xor(Ti, 2, kWave);
     const bool head = (lane & 3) == 3;   // one lane per load carries its total
     const double incl = dpp_wave_incl_scan(head ? Ti : 0.0);
     const unsigned long long pos_i = __ballot(head && Ti > 0.0);
@@ -676,9 +652,7 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     double w[4];
     const f4 vp = load4<kVec4>(row_rsrc(prow, a.V), a.V, base + istar * (kWave * 4));
     const f4 vq = two_rows ? load4<kVec4>(row_rsrc(qrow, a.V), a.V, base + istar * (kWave * 4)) : vp;
-    load_weights(two_rows, residual, vp, vq, c, invZp, invZq, w);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] *= wscale;
+    wf(vp, vq, w);
     const double lsum = (w[0] + w[1]) + (w[2] + w[3]);
     const double lincl = dpp_wave_incl_scan(lsum);
     const double lexcl = dpp_wave_shr1(lincl);
@@ -704,15 +678,20 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
         estar = elast;
     }
     estar = __shfl(estar, lstar, kWave);
-    if (lane != lstar) return;
+    if (lane != lstar) return false;
     if (estar < 0) estar = 0;
-    int y = s.u * kUnit + istar * (kWave * 4) + lstar * 4 + estar;
-    float zy = estar == 0 ? vp.x : (estar == 1 ? vp.y : (estar == 2 ? vp.z : vp.w));
+    y = s.u * kUnit + istar * (kWave * 4) + lstar * 4 + estar;
+    zy = estar == 0 ? vp.x : (estar == 1 ? vp.y : (estar == 2 ? vp.z : vp.w));
     if (y >= a.V) {        // only reachable when every weight is zero
         y = a.V - 1;
         zy = prow[y];
     }
-    const double py = exp_nonpos_f64((static_cast<double>(zy) - M_ref) * c.invT64) / Zp_true;
+    return true;
+}
+
+// The chain's outputs after the draw of token y (probability py) at index `row`:
+// the token, its probability, and the padding of the sequence's outputs.
+__device__ __forceinline__ void emit_chain(const RejectArgs& a, const SeqCtx& s, int row, int y, double py) {
     const int k = s.kb;
     const size_t ob = s.tb;
     a.out_tokens[ob + row] = y;
@@ -724,6 +703,53 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     if (a.accept_probs)
         for (int i = row + 1; i < k; ++i) a.accept_probs[s.db + i] = -1.0f;
     a.num_accepted[s.b] = row;
+}
+
+// Draw from the weights of this unit (residual of row `row`; p_row when `use_p` or
+// for the bonus row), given the running sum `run` before this unit and the
+// target t. Only the wavefront owning the crossing unit calls this; the lane
+// holding the drawn token writes it, its probability and the padding of the
+// sequence's outputs.
+template <bool kVec4>
+__device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, int row, bool two_rows,
+                                           const float* prow, const float* qrow, const SampleCtx& c,
+                                           const LoadSums& ls, bool use_p, bool exact, double run, double t,
+                                           double invZp, double invZq, double Zp_true, double wscale,
+                                           double M_ref) {
+    // wscale maps this unit's weights onto the scale of run and t (1, except for
+    // the bonus row, whose unit weights are relative to the unit's own maximum);
+    // M_ref is the row maximum the emitted probability is taken against.
+    const bool residual = two_rows && !use_p;
+    auto lv = [&](int i, int j0) -> double {
+        double v = 0.0;
+        if (!use_p) {
+#pragma unroll
+            for (int j = 0; j < kWave / 4; ++j) {
+                const double2 g = ls[i][j0 + j];
+                v += residual ? g.x * invZp - g.y * invZq : g.x;
+            }
+        } else {                 // zero residual (rare): p-weights of this load, recomputed
+#pragma unroll 1
+            for (int j = 0; j < kWave / 4; ++j) {
+                const int x = s.u * kUnit + i * (kWave * 4) + (j0 + j) * 4;
+                double w[4];
+                load_weights(two_rows, false, load4<kVec4>(row_rsrc(prow, a.V), a.V, x),
+                             two_rows ? load4<kVec4>(row_rsrc(qrow, a.V), a.V, x)
+                             : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, c, invZp, invZq, w);
+                v += (w[0] + w[1]) + (w[2] + w[3]);
+            }
+        }
+        return v * wscale;
+    };
+    auto wf = [&](const f4& vp, const f4& vq, double (&w)[4]) {
+        load_weights(two_rows, residual, vp, vq, c, invZp, invZq, w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] *= wscale;
+    };
+    int y;
+    float zy;
+    if (!scan_unit<kVec4>(a, s, prow, qrow, two_rows, exact, run, t, lv, wf, y, zy)) return;
+    emit_chain(a, s, row, y, exp_nonpos_f64((static_cast<double>(zy) - M_ref) * c.invT64) / Zp_true);
 }
 
 // Reads wave 0's sampling decision and runs the final scan in the owning
@@ -826,11 +852,25 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
                       1.0, c.Mp64);
 }
 
-// Acceptance test of draft j from the combined statistics and the draft token's
-// two logits (loaded while the group was exchanging statistics); workgroup 0
-// writes the outputs of the test.
-__device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, int j, const RowStats& st,
-                                            const TokenLogits& tl) {
+// One acceptance test: the rows it reads, the candidate, where its uniform comes
+// from and where its outputs go (a chain level, or the first child of a tree node).
+struct LevelRef {
+    const float* prow;
+    const float* qrow;
+    size_t tok_idx;               // the candidate is draft_tokens[tok_idx]
+    int pos;                      // decided position L + 1 + pos
+    unsigned stream;              // Philox stream of the acceptance uniform
+    unsigned long long* slots;    // this exchange's slots
+    size_t acc_idx, out_idx;      // accept_probs index; out_tokens / out_probs index
+    long long node_idx;           // out_nodes index (tree), -1: none
+    int node;
+};
+
+// Acceptance test of one candidate from the combined statistics and its two
+// logits (loaded while the group was exchanging statistics); workgroup 0 writes
+// the outputs of the test.
+__device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, const LevelRef& r,
+                                            const RowStats& st, const TokenLogits& tl) {
     double ep = 0.0, eq = 0.0;   // p and q of the token times Z_p and Z_q
     if (tl.ok) {
         ep = exp_nonpos_f64((static_cast<double>(tl.zp) - st.Mp) * a.invT64);
@@ -842,10 +882,11 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
     if (s.q == 0 && lane_id() == 0) {
         const double p_d = ep / st.Zp, q_d = eq / st.Zq;
         const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
-        if (a.accept_probs) a.accept_probs[s.db + j] = static_cast<float>(fmin(1.0, ratio));
+        if (a.accept_probs) a.accept_probs[r.acc_idx] = static_cast<float>(fmin(1.0, ratio));
         if (accepted) {
-            a.out_tokens[s.tb + j] = tl.tok;
-            if (a.out_probs) a.out_probs[s.tb + j] = static_cast<float>(p_d);
+            a.out_tokens[r.out_idx] = tl.tok;
+            if (a.out_probs) a.out_probs[r.out_idx] = static_cast<float>(p_d);
+            if (r.node_idx >= 0 && a.out_nodes) a.out_nodes[r.node_idx] = r.node;
         }
     }
     return accepted;
@@ -857,11 +898,11 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
 // workgroup reaches the same decision from the same bits. Returns the result flags
 // (kResAccepted, kResError) and the row's statistics in `st`.
 template <bool kVec4>
-__device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
-                                               f4 (&xq)[kVecs], RowStats& st, Shared& sh,
+__device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx& s, const LevelRef& r,
+                                               f4 (&xp)[kVecs], f4 (&xq)[kVecs], RowStats& st, Shared& sh,
                                                bool& counted) {
-    const float* prow = s.prow_base + size_t(row) * a.V;
-    const float* qrow = s.qrow_base + size_t(row) * a.V;
+    const float* prow = r.prow;
+    const float* qrow = r.qrow;
     load_unit<kVec4, true>(row_rsrc(prow, a.V), row_rsrc(qrow, a.V), a.V, s.u, xp, xq);
     // wave 0 takes the acceptance test: the draft token and its two logits are read
     // behind the unit's loads, through the scalar cache (uniform addresses into
@@ -872,7 +913,7 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
     tok.ok = false;
     float ztp = 0.0f, ztq = 0.0f;
     if (s.wave == 0) {
-        tok.tok = load_uniform(a.draft_tokens, s.db + row);
+        tok.tok = load_uniform(a.draft_tokens, r.tok_idx);
         tok.ok = tok.tok >= 0 && tok.tok < a.V;
         if (tok.ok) {
             ztp = load_uniform(prow, tok.tok);
@@ -906,14 +947,13 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
         double Zp_w, Zq_w;
         combine_pair(mpw, zpw, a.invT64, Mp_w, Zp_w);
         combine_pair(mqw, zqw, a.invT64, Mq_w, Zq_w);
-        const size_t level = size_t(s.b) * (a.k + 1) + row;
-        unsigned long long* slots = a.stat_slots + level * a.Q * kStatSlots;
+        unsigned long long* slots = r.slots;
         const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_w), __builtin_bit_cast(unsigned, Mq_w),
                                           hi32(Zp_w), lo32(Zp_w), hi32(Zq_w), lo32(Zq_w)};
         publish(slots + s.q, pay, s.epoch, a.Q);
         TokenLogits tl = tok;
         double u_smp;
-        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &tl.u_acc, &u_smp);
+        stream_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + r.pos, r.stream, &tl.u_acc, &u_smp);
         unsigned v[kStatSlots];
         unsigned flags = 0;
         if (gather<kStatSlots>(slots, a.Q, s.epoch, v)) {
@@ -925,7 +965,7 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
                          a.invT64, st.Mp, st.Zp);
             combine_pair(have ? __builtin_bit_cast(float, v[1]) : -INFINITY, have ? join64(v[4], v[5]) : 0.0,
                          a.invT64, st.Mq, st.Zq);
-            if (accept_test(a, s, row, st, tl)) flags |= kResAccepted;
+            if (accept_test(a, s, r, st, tl)) flags |= kResAccepted;
         } else {
             count_group(a, s, counted);
             st.Mp = st.Mq = 0.0f;
@@ -942,16 +982,33 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
     return static_cast<unsigned>(uniform(static_cast<int>(sh.res.flags)));
 }
 
+// Level `row` of the chain (rows p_row and q_row, draft row, position L + 1 + row).
+template <bool kVec4>
+__device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
+                                               f4 (&xq)[kVecs], RowStats& st, Shared& sh, bool& counted) {
+    LevelRef r;
+    r.prow = s.prow_base + size_t(row) * a.V;
+    r.qrow = s.qrow_base + size_t(row) * a.V;
+    r.tok_idx = s.db + row;
+    r.pos = row;
+    r.stream = 0u;
+    r.slots = a.stat_slots + (size_t(s.b) * (a.k + 1) + row) * a.Q * kStatSlots;
+    r.acc_idx = s.db + row;
+    r.out_idx = s.tb + row;
+    r.node_idx = -1;
+    r.node = 0;
+    return level_core<kVec4>(a, s, r, xp, xq, st, sh, counted);
+}
+
 // The bonus row p_k after k acceptances, with one exchange: each wavefront weighs
 // its unit against the unit's own maximum M_u (heavy logits judged with the
 // unit's own normaliser, a superset of the row's heavy set); wave 0 rescales its
 // units to the workgroup maximum and publishes (sum, maximum); the gathered pairs
 // are rescaled to the row maximum M, which also gives the row's Z.
-template <bool kVec4>
-__device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
-                                          Shared& sh, bool& counted) {
-    const int row = s.kb;
-    const float* prow = s.prow_base + size_t(row) * a.V;
+template <bool kVec4, typename E>
+__device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s, const float* prow, int pos,
+                                           unsigned long long* slots, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
+                                           Shared& sh, bool& counted, E&& emit) {
     const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, a.V);
     load_unit<kVec4, false>(rp, rp, a.V, s.u, xp, xq);
     float m = -INFINITY;
@@ -985,11 +1042,10 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
         }
         const double Mw = dpp_wave_max(static_cast<float>(Mv));
         const double Ww = dpp_wave_sum((Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - Mw) * a.invT64) : 0.0);
-        unsigned long long* slots = a.samp_slots + size_t(s.b) * a.Q * kSampSlots;
         const unsigned pay[4] = {hi32(Ww), lo32(Ww), hi32(Mw), lo32(Mw)};
         publish(slots + s.q, pay, s.epoch, a.Q);
         double u_acc, u_smp;
-        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
+        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[4];
         const bool ok = gather<4>(slots, a.Q, s.epoch, v);
         count_group(a, s, counted);
@@ -1024,8 +1080,427 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
     double run, t, Z, M;
     if (!read_samp(a, s, sh, use_p, exact, run, t, Z, M)) return;
     const double wscale = exp_nonpos_f64((Mu64 - M) * a.invT64);
-    final_scan<kVec4>(a, s, row, false, prow, prow, c, sh.ls[s.wave], false, exact, run, t, 1.0 / Z, 1.0, Z, wscale,
-                      M);
+    const LoadSums& ls = sh.ls[s.wave];
+    auto lv = [&](int i, int j0) -> double {
+        double v = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWave / 4; ++j) v += ls[i][j0 + j].x;
+        return v * wscale;
+    };
+    auto wf = [&](const f4& vp, const f4& vq, double (&w)[4]) {
+        load_weights(false, false, vp, vq, c, 1.0 / Z, 1.0, w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] *= wscale;
+    };
+    int y;
+    float zy;
+    if (!scan_unit<kVec4>(a, s, prow, prow, false, exact, run, t, lv, wf, y, zy)) return;
+    emit(y, exp_nonpos_f64((static_cast<double>(zy) - M) * c.invT64) / Z);
+}
+
+// The bonus row p_k after k acceptances.
+template <bool kVec4>
+__device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
+                                          Shared& sh, bool& counted) {
+    const int row = s.kb;
+    bonus_core<kVec4>(a, s, s.prow_base + size_t(row) * a.V, row,
+                      a.samp_slots + size_t(s.b) * a.Q * kSampSlots, xp, xq, sh, counted,
+                      [&](int y, double py) { emit_chain(a, s, row, y, py); });
+}
+
+
+// ---------------------------------------------------------------- tree verification
+//
+// "ReSpec: Towards Optimizing Speculative Decoding in Reinforcement Learning
+// Systems" (talk notes), GAP 1: speculation with a branching factor, the drafts
+// forming a tree that one target pass checks. The walk is multi-candidate
+// speculative sampling (SpecInfer, Miao et al. 2024): at node v the children are
+// tested in index order against a running residual r (r = p_v first, then
+// r = max(0, r - q_v) normalised after each rejection, unchanged if that sums to
+// zero); an accepted child continues the walk, a node whose children are all
+// rejected ends it with a draw from r, and a leaf ends it with a bonus draw from
+// p_v. The first child is an ordinary level of the chain (same uniform, same
+// statistics); candidate i >= 2 takes word 0 of Philox stream i.
+
+// The rounds of one node after its first child was rejected, with the exact
+// normalisers of its two rows.
+struct TreeRounds {
+    double iZp, iZq;
+    double iW[kMaxBranch];   // 1 / W_j, W_j the sum of round j's residual
+    unsigned keep;           // bit j: round j summed to zero and left r unchanged
+    int n;                   // rounds taken
+};
+
+// r after the rounds taken, for one logit with unnormalised weights a (p) and b (q).
+__device__ __forceinline__ double tree_r(const TreeRounds& R, double a, double b) {
+    double r = a * R.iZp;
+    const double qb = b * R.iZq;
+#pragma unroll
+    for (int j = 0; j < kMaxBranch; ++j) {
+        if (j < R.n) {
+            const double u = fmax(0.0, r - qb);
+            r = ((R.keep >> j) & 1u) ? r : u * R.iW[j];
+        }
+    }
+    return r;
+}
+
+__device__ __forceinline__ void tree_push(TreeRounds& R, double W) {
+    const bool zero = !(W > 0.0);
+#pragma unroll
+    for (int j = 0; j < kMaxBranch; ++j)
+        if (j == R.n) R.iW[j] = zero ? 0.0 : 1.0 / W;
+    R.keep |= (zero ? 1u : 0u) << R.n;
+    ++R.n;
+}
+
+// One pass over the unit in registers (rows p_v, q_v): f(a, b) -> (w1, w2) for every
+// logit, with a = e^{(z_p - M_p)/T}, b = e^{(z_q - M_q)/T} (fp64 for heavy logits,
+// compensated fp32 otherwise, as for the chain's residual); the per-load w1 sums go
+// to the wavefront's LDS slab. Returns the wavefront's (sum w1, sum w2).
+template <bool kVec4, typename F>
+__device__ __forceinline__ double2 tree_unit_pass(const f4 (&xp)[kVecs], const f4 (&xq)[kVecs], const SampleCtx& c,
+                                                  const float* prow, const float* qrow, int base, LoadSums& ls,
+                                                  F&& f) {
+    const int lane = lane_id();
+    HeavyBits hb = heavy_bits(true, xp, xq, c);
+    HeavyRound hr;
+    heavy_fetch(true, prow, qrow, base, hb, hr);
+    double S1 = 0.0, S2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+        float la[4], lb[4];
+        bool in_s[4], h[4];
+        light_weights(true, xp[i], xq[i], c, la, lb, in_s, h);   // heavy logits come out as 0
+        double l1 = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double2 w = f(static_cast<double>(la[e]), static_cast<double>(lb[e]));
+            l1 += w.x;
+            S2 += w.y;
+        }
+        S1 += l1;
+        ls[i][lane] = make_double2(l1, 0.0);
+    }
+    auto add = [&](int i, double va, double vb, bool) {
+        const double2 w = f(va, vb);
+        S1 += w.x;
+        S2 += w.y;
+        ls[i][lane].x += w.x;
+    };
+    heavy_weigh(true, c, hr, add);
+    while (__any((hb.lo | hb.hi) != 0u)) {
+        heavy_fetch(true, prow, qrow, base, hb, hr);
+        heavy_weigh(true, c, hr, add);
+    }
+    return make_double2(dpp_wave_sum(S1), dpp_wave_sum(S2));
+}
+
+enum : int { kDrawn = 0, kDrawZero = 1, kDrawError = 2 };
+
+// One pass and one exchange: the group's totals (T1, T2) of f's two weights, in
+// every wavefront; with `draw`, also the draw from the w1 weights with u_smp at
+// position L + 1 + pos (emit(y, p_v(y)) runs on the lane holding the token), or
+// kDrawZero, without drawing, if they sum to zero.
+template <bool kVec4, typename F, typename E>
+__device__ __forceinline__ int tree_round(const RejectArgs& a, const SeqCtx& s, const f4 (&xp)[kVecs],
+                                          const f4 (&xq)[kVecs], const SampleCtx& c, double iZp, const float* prow,
+                                          const float* qrow, unsigned long long* slots, int pos, Shared& sh,
+                                          bool draw, F&& f, E&& emit, double& T1, double& T2) {
+    const int lane = lane_id();
+    const double2 ws = tree_unit_pass<kVec4>(xp, xq, c, prow, qrow, s.u * kUnit + lane * 4, sh.ls[s.wave], f);
+    if (lane == 0) sh.usum[s.wave] = make_double4(ws.x, ws.y, 0.0, 0.0);
+    __syncthreads();
+    if (s.wave == 0) {
+        double u1 = 0.0, u2 = 0.0;
+        if (lane < kUnitWaves) {
+            const double4 v = sh.usum[lane];
+            u1 = v.x;
+            u2 = v.y;
+        }
+        const double w1 = dpp_wave_sum(u1), w2 = dpp_wave_sum(u2);
+        const unsigned pay[4] = {hi32(w1), lo32(w1), hi32(w2), lo32(w2)};
+        publish(slots + s.q, pay, s.epoch, a.Q);
+        double u_acc, u_smp;
+        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
+        unsigned v[4];
+        const bool ok = gather<4>(slots, a.Q, s.epoch, v);
+        const double Wg = join64(v[0], v[1]);      // lane l < Q: workgroup l's sums (zero in the others)
+        const double t1 = dpp_wave_sum(Wg), t2 = dpp_wave_sum(join64(v[2], v[3]));
+        const double t = u_smp * t1;
+        double run = 0.0;
+        bool exact = false;
+        int owner = -1;
+        unsigned flags = ok ? 0u : kSampError;
+        if (draw) {
+            if (!(t1 > 0.0)) {
+                flags |= kSampUseP;                   // nothing to draw from
+            } else {
+                const int qstar = find_crossing(Wg, 0.0, t, run, exact);
+                if (qstar == s.q) {
+                    bool exact_u;
+                    owner = find_crossing(u1, run, t, run, exact_u);
+                    exact = exact && exact_u;
+                }
+            }
+        }
+        if (lane == 0) {
+            sh.samp.owner = owner;
+            sh.samp.flags = flags | (exact ? kSampExact : 0u);
+            sh.samp.run = run;
+            sh.samp.t = t;
+            sh.samp.Z1 = t1;
+            sh.samp.Z2 = t2;
+        }
+    }
+    __syncthreads();
+    const unsigned flags = static_cast<unsigned>(uniform(static_cast<int>(sh.samp.flags)));
+    T1 = uniform(sh.samp.Z1);
+    T2 = uniform(sh.samp.Z2);
+    if (flags & kSampError) return kDrawError;
+    if (!draw) return kDrawn;
+    if (flags & kSampUseP) return kDrawZero;
+    if (uniform(sh.samp.owner) != s.wave) return kDrawn;
+    const double run = uniform(sh.samp.run), t = uniform(sh.samp.t);
+    const LoadSums& ls = sh.ls[s.wave];
+    auto lv = [&](int i, int j0) -> double {
+        double v = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWave / 4; ++j) v += ls[i][j0 + j].x;
+        return v;
+    };
+    auto wf = [&](const f4& vp, const f4& vq, double (&w)[4]) {
+        float la[4], lb[4];
+        bool in_s[4], h[4];
+        light_weights(true, vp, vq, c, la, lb, in_s, h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double va = h[e] ? exp_nonpos_f64((static_cast<double>(vp[e]) - c.Mp64) * c.invT64) : la[e];
+            const double vb = h[e] ? exp_nonpos_f64((static_cast<double>(vq[e]) - c.Mq64) * c.invT64) : lb[e];
+            w[e] = f(va, vb).x;
+        }
+    };
+    int y;
+    float zy;
+    if (scan_unit<kVec4>(a, s, prow, qrow, true, (flags & kSampExact) != 0u, run, t, lv, wf, y, zy))
+        emit(y, exp_nonpos_f64((static_cast<double>(zy) - c.Mp64) * c.invT64) * iZp);
+    return kDrawn;
+}
+
+// The test of a node's i-th child (i >= 2) against the residual the rounds leave:
+// accept iff u < r(x) / q(x), u = word 0 of stream i. Every workgroup takes it from
+// the same bits; workgroup 0 writes its outputs. Returns the decision.
+__device__ __forceinline__ bool tree_candidate(const RejectArgs& a, const SeqCtx& s, const SampleCtx& c,
+                                               const TreeRounds& R, const float* prow, const float* qrow, int node,
+                                               int i, int depth, Shared& sh) {
+    if (s.wave == 0) {
+        const int N = a.k;
+        const size_t nb = size_t(s.b) * N;
+        const int x = load_uniform(a.draft_tokens, nb + node - 1);
+        const bool ok = x >= 0 && x < a.V;
+        double av = 0.0, bv = 0.0;   // out-of-range ids (a broken precondition) are rejected
+        if (ok) {
+            av = exp_nonpos_f64((static_cast<double>(load_uniform(prow, x)) - c.Mp64) * c.invT64);
+            bv = exp_nonpos_f64((static_cast<double>(load_uniform(qrow, x)) - c.Mq64) * c.invT64);
+        }
+        const double rx = tree_r(R, av, bv), qx = bv * R.iZq;
+        double u0, u1;
+        stream_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + depth, static_cast<uint32_t>(i), &u0, &u1);
+        const bool accepted = u0 * qx < rx;   // q = 0: accepted iff r > 0, as a ratio of +inf
+        if (s.q == 0 && lane_id() == 0) {
+            const double ratio = (qx > 0.0) ? rx / qx : (rx > 0.0 ? INFINITY : 0.0);
+            if (a.accept_probs) a.accept_probs[nb + node - 1] = static_cast<float>(fmin(1.0, ratio));
+            if (accepted) {
+                const size_t ob = size_t(s.b) * (N + 1);
+                a.out_tokens[ob + depth] = x;
+                if (a.out_probs) a.out_probs[ob + depth] = static_cast<float>(av * R.iZp);
+                if (a.out_nodes) a.out_nodes[nb + depth] = node;
+            }
+        }
+        if (lane_id() == 0) sh.res.flags = accepted ? kResAccepted : 0u;
+    }
+    __syncthreads();
+    return (static_cast<unsigned>(uniform(static_cast<int>(sh.res.flags))) & kResAccepted) != 0u;
+}
+
+// The tree's outputs after the final draw of token y (probability py) at index
+// `depth`: the token, the padding, the untested nodes and the accepted length.
+__device__ __forceinline__ void emit_tree(const RejectArgs& a, const SeqCtx& s, int depth, unsigned tested, int y,
+                                          double py) {
+    const int N = a.k;
+    const size_t ob = size_t(s.b) * (N + 1), nb = size_t(s.b) * N;
+    a.out_tokens[ob + depth] = y;
+    if (a.out_probs) a.out_probs[ob + depth] = static_cast<float>(py);
+    for (int i = depth + 1; i <= N; ++i) {
+        a.out_tokens[ob + i] = -1;
+        if (a.out_probs) a.out_probs[ob + i] = 0.0f;
+    }
+    if (a.out_nodes)
+        for (int i = depth; i < N; ++i) a.out_nodes[nb + i] = -1;
+    if (a.accept_probs)
+        for (int n = 1; n <= N; ++n)
+            if (!((tested >> n) & 1u)) a.accept_probs[nb + n - 1] = -1.0f;
+    a.num_accepted[s.b] = depth;
+}
+
+// SampleCtx of a node's rows from its chain statistics (as for the chain's residual).
+__device__ __forceinline__ SampleCtx residual_ctx(const RejectArgs& a, const RowStats& st) {
+    SampleCtx c;
+    c.Mp = st.Mp;
+    c.Mq = st.Mq;
+    c.invT = a.invT;
+    c.Mp64 = st.Mp;
+    c.Mq64 = st.Mq;
+    c.invT64 = a.invT64;
+    c.tp = heavy_threshold(st.Mp, st.Zp, a.T);
+    c.tq = heavy_threshold(st.Mq, st.Zq, a.T);
+    c.dn = ln_approx(st.Zp) - ln_approx(st.Zq);
+    return c;
+}
+
+// The walk of one sequence's tree (nodes 0 .. N, rows [N+1][V] of target and draft).
+template <bool kVec4>
+__device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
+                                          Shared& sh, bool& counted) {
+    const int N = a.k;
+    const size_t b = s.b;
+    const float* tbase = a.target + b * (N + 1) * a.V;
+    const float* dbase = a.draft + b * (N + 1) * a.V;
+    unsigned long long* slots0 = a.tree_slots + b * kTreeEx * kSampSlots * a.Q;
+    auto slot = [&](int e) { return slots0 + size_t(e) * kSampSlots * a.Q; };
+    int ex = 0, v = 0, depth = 0;
+    unsigned tested = 0u;
+    for (;;) {
+        // children of v in index order, four bits each (scalar loads of the parents)
+        unsigned chp = 0u;
+        int m = 0;
+        for (int n = v + 1; n <= N; ++n) {
+            if (load_uniform(a.parents, b * N + n - 1) == v) {
+                if (m < kMaxBranch) chp |= static_cast<unsigned>(n) << (4 * m);
+                ++m;
+            }
+        }
+        if (m > kMaxBranch || ex + 4 + m > kTreeEx) {   // outside the documented shapes
+            flag_error(a, s);
+            return;
+        }
+        const float* prow = tbase + size_t(v) * a.V;
+        auto emit = [&](int y, double py) { emit_tree(a, s, depth, tested, y, py); };
+        if (m == 0) {   // a leaf: the bonus draw from p_v
+            bonus_core<kVec4>(a, s, prow, depth, slot(ex++), xp, xq, sh, counted, emit);
+            return;
+        }
+        const float* qrow = dbase + size_t(v) * a.V;
+        const int c1 = static_cast<int>(chp & 15u);
+        LevelRef r;
+        r.prow = prow;
+        r.qrow = qrow;
+        r.tok_idx = b * N + c1 - 1;
+        r.pos = depth;
+        r.stream = 0u;
+        r.slots = slot(ex++);
+        r.acc_idx = b * N + c1 - 1;
+        r.out_idx = b * (N + 1) + depth;
+        r.node_idx = static_cast<long long>(b * N + depth);
+        r.node = c1;
+        RowStats st;
+        const unsigned res = level_core<kVec4>(a, s, r, xp, xq, st, sh, counted);
+        tested |= 1u << c1;
+        if (res & kResError) {
+            flag_error(a, s);
+            return;
+        }
+        if (res & kResAccepted) {
+            v = c1;
+            ++depth;
+            continue;
+        }
+        // The first child was rejected. Phase 0 takes the exact normalisers; phase
+        // i = 1 .. m-1 the residual left by i rejections, then tests child i+1; phase
+        // m draws from the residual after all m rejections, phase m+1 (only if that
+        // residual sums to zero) from the residual before it. One pass per phase,
+        // at one call site, so the unit in registers is walked by a single copy of
+        // the pass.
+        const SampleCtx c = residual_ctx(a, st);
+        TreeRounds R;
+        R.iZp = 0.0;
+        R.iZq = 0.0;
+#pragma unroll
+        for (int j = 0; j < kMaxBranch; ++j) R.iW[j] = 0.0;
+        R.keep = 0u;
+        R.n = 0;
+        bool moved = false;
+        for (int phase = 0;; ++phase) {
+            const bool draw = phase >= m;
+            const int fsel = phase == 0 ? 0 : (phase <= m ? 1 : 2);   // (a, b) | max(0, r - q) | r
+            auto f = [&](double av, double bv) {
+                const double r = tree_r(R, av, bv);
+                const double u = fmax(0.0, r - bv * R.iZq);
+                return make_double2(fsel == 0 ? av : (fsel == 1 ? u : r), fsel == 0 ? bv : 0.0);
+            };
+            double T1, T2;
+            const int d = tree_round<kVec4>(a, s, xp, xq, c, R.iZp, prow, qrow, slot(ex++), depth, sh, draw, f,
+                                            emit, T1, T2);
+            if (d == kDrawError || (d == kDrawZero && phase > m)) {
+                flag_error(a, s);
+                return;
+            }
+            if (draw) {
+                if (d == kDrawZero) continue;   // to phase m + 1
+                return;
+            }
+            if (phase == 0) {
+                R.iZp = 1.0 / T1;
+                R.iZq = 1.0 / T2;
+                continue;
+            }
+            tree_push(R, T1);
+            const int ci = static_cast<int>((chp >> (4 * phase)) & 15u);
+            tested |= 1u << ci;
+            if (tree_candidate(a, s, c, R, prow, qrow, ci, phase + 1, depth, sh)) {
+                v = ci;
+                ++depth;
+                moved = true;
+                break;
+            }
+        }
+        if (moved) continue;
+        return;
+    }
+}
+
+template <bool kVec4>
+__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_tree_kernel(RejectArgs a) {
+    const int w = blockIdx.x;
+    int group, q;
+    if (a.groups % 8 == 0) {
+        const int l = w / 8;
+        group = (w % 8) + 8 * (l / a.Q);
+        q = l % a.Q;
+    } else {
+        group = w / a.Q;
+        q = w % a.Q;
+    }
+    SeqCtx s;
+    s.q = q;
+    s.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    s.u = q * kUnitWaves + s.wave;
+    {
+        const unsigned last = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.epoch = (last + 1u == 0u) ? 1u : last + 1u;
+    }
+    bool counted = q != 0;
+    __shared__ Shared sh;
+    f4 xp[kVecs], xq[kVecs];
+    for (int b = group; b < a.B; b += a.groups) {
+        s.b = b;
+        s.kb = a.k;
+        s.tb = size_t(b) * (a.k + 1);
+        s.db = size_t(b) * a.k;
+        s.sid = load_uniform(a.seq_ids, b);
+        s.L = load_uniform(a.seq_lens, b);
+        tree_walk<kVec4>(a, s, xp, xq, sh, counted);
+    }
 }
 
 template <bool kVec4>
@@ -1088,7 +1563,7 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <bool kVec4>
+template <bool kVec4, bool kTree>
 hipError_t co_resident(int dev, int* wgs) {
     static int memo[64];
     if (dev >= 0 && dev < 64 && memo[dev] > 0) {
@@ -1096,7 +1571,9 @@ hipError_t co_resident(int dev, int* wgs) {
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4>, kRT, 0);
+    hipError_t e = kTree
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_tree_kernel<kVec4>, kRT, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4>, kRT, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -1105,13 +1582,13 @@ hipError_t co_resident(int dev, int* wgs) {
     return hipSuccess;
 }
 
-template <bool kVec4>
+template <bool kVec4, bool kTree>
 hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     int wgs = 0;
-    e = co_resident<kVec4>(dev, &wgs);
+    e = co_resident<kVec4, kTree>(dev, &wgs);
     if (e != hipSuccess) return e;
     int groups = min(a.B, wgs / a.Q);
     if (groups < 1) return hipErrorInvalidConfiguration;
@@ -1122,7 +1599,8 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     // cooperative launch would guarantee it, at ~13 us of extra launch latency
     // per call on this stack; should residency ever be partial, the waits are
     // bounded and the affected sequences report an error instead of hanging.)
-    hipLaunchKernelGGL((reject_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
+    if (kTree) hipLaunchKernelGGL((reject_tree_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
+    else hipLaunchKernelGGL((reject_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1156,13 +1634,56 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.ctl = reinterpret_cast<unsigned*>(ws + lay.ctl);
     a.stat_slots = reinterpret_cast<unsigned long long*>(ws + lay.stat);
     a.samp_slots = reinterpret_cast<unsigned long long*>(ws + lay.samp);
+    a.parents = nullptr;
+    a.out_nodes = nullptr;
+    a.tree_slots = nullptr;
     a.B = p.B; a.k = p.k; a.V = p.V; a.U = U; a.Q = Q; a.groups = 0;
     a.invT = 1.0f / p.temperature;
     a.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(p.temperature));
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.T = p.temperature;
     a.seed = p.seed;
-    return (p.V % 4) == 0 ? launch_variant<true>(a, stream) : launch_variant<false>(a, stream);
+    return (p.V % 4) == 0 ? launch_variant<true, false>(a, stream) : launch_variant<false, false>(a, stream);
+}
+
+size_t reject_tree_workspace_bytes(int B, int nodes, int V) {
+    const int U = (V + kUnit - 1) / kUnit;
+    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
+    (void)nodes;
+    return align256(4 * sizeof(unsigned)) + sizeof(unsigned long long) * size_t(B) * kTreeEx * kSampSlots * Q;
+}
+
+int reject_tree_max_branch() { return kMaxBranch; }
+
+hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
+    const int U = (p.V + kUnit - 1) / kUnit;
+    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
+    if (Q > kMaxQ) return hipErrorInvalidValue;
+    char* ws = static_cast<char*>(p.workspace);
+    RejectArgs a;
+    a.target = p.target_logits;
+    a.draft = p.draft_logits;
+    a.draft_tokens = p.draft_tokens;
+    a.seq_ids = p.seq_ids;
+    a.seq_lens = p.seq_lens;
+    a.cu = nullptr;
+    a.out_tokens = p.out_tokens;
+    a.num_accepted = p.num_accepted;
+    a.out_probs = p.out_probs;
+    a.accept_probs = p.accept_probs;
+    a.ctl = reinterpret_cast<unsigned*>(ws);
+    a.stat_slots = nullptr;
+    a.samp_slots = nullptr;
+    a.parents = p.parents;
+    a.out_nodes = p.out_nodes;
+    a.tree_slots = reinterpret_cast<unsigned long long*>(ws + align256(4 * sizeof(unsigned)));
+    a.B = p.B; a.k = p.k; a.V = p.V; a.U = U; a.Q = Q; a.groups = 0;
+    a.invT = 1.0f / p.temperature;
+    a.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(p.temperature));
+    a.invT64 = 1.0 / static_cast<double>(p.temperature);
+    a.T = p.temperature;
+    a.seed = p.seed;
+    return (p.V % 4) == 0 ? launch_variant<true, true>(a, stream) : launch_variant<false, true>(a, stream);
 }
 
 }  // namespace specverify
