@@ -37,9 +37,15 @@ T4  Uniforms.  The children of the node at depth d are decided at position
     draft generator); the final sample or bonus uses word 1 of stream 0 (the
     chain's u_smp). So a chain-shaped tree reproduces the chain's decisions.
 T5  Outputs.  Emitted tokens (the accepted path, then the sampled token), a =
-    depth of the last accepted node, the accepted node indices (so the caller can
-    move their KV rows to L+1 .. L+a before the commit L' = L + a + 1), p_v of
-    every emitted token at its node, and min(1, r(x)/q(x)) of every tested node.
+    depth of the last accepted node, the accepted node indices, p_v of every
+    emitted token at its node, and min(1, r(x)/q(x)) of every tested node.
+T6  Commit.  The committed prefix after the step is the root and the accepted
+    path, so the KV rows of the accepted nodes n_1 .. n_a (path order) move to
+    slots L+1 .. L+a (slot L+j takes what slot L+n_j held before the move; the
+    root stays at L), then L' = L + a + 1 as for the chain. A commit that would
+    pass the capacity is refused (the chain's rule) and then nothing moves;
+    a <= 0 moves nothing. Slots past L+a keep their old rows: they lie beyond
+    L' and the next step's append overwrites them.
 """
 
 from __future__ import annotations
@@ -50,6 +56,7 @@ import math
 import numpy as np
 
 from .attention import attend, bf16_to_f64, gather_sequence_kv
+from .commit import commit_lengths
 from .philox import verify_uniforms
 from .reject import Decision, inverse_cdf, softmax_t
 
@@ -189,3 +196,26 @@ def verify_batch_tree(target_logits, draft_logits, draft_tokens, parents, seq_id
         results.append(res)
     return dict(out_tokens=out_tokens, num_accepted=num_accepted, accepted_nodes=accepted_nodes,
                 out_probs=out_probs, accept_probs=accept_probs, results=results)
+
+
+def commit_tree(k_cache, v_cache, block_table, seq_lens, accepted_nodes, num_accepted, capacity_tokens: int):
+    """T6 on the paged caches (K [pages][Hkv][bs][D], V [pages][Hkv][D][bs]). Every row is read
+    from the caches as they were before the call and written into copies, so the order of the
+    moves cannot matter. Returns (k_cache', v_cache', new lengths, overflow flags)."""
+    kc, vc = k_cache.copy(), v_cache.copy()
+    new_L, overflow = commit_lengths(seq_lens, num_accepted, capacity_tokens)
+    bs = k_cache.shape[2]
+
+    def where(b, s):
+        return int(block_table[b, s // bs]), s % bs
+
+    for b in range(len(seq_lens)):
+        L, a = int(seq_lens[b]), int(num_accepted[b])
+        if overflow[b] or a <= 0:
+            continue
+        for j in range(1, a + 1):
+            ps, os_ = where(b, L + int(accepted_nodes[b, j - 1]))
+            pd, od = where(b, L + j)
+            kc[pd, :, od, :] = k_cache[ps, :, os_, :]
+            vc[pd, :, :, od] = v_cache[ps, :, :, os_]
+    return kc, vc, new_L, overflow

@@ -12,6 +12,11 @@
 * Monte Carlo, multi-round with the commit: generating tokens by repeated tree
   rounds (branching 2, depth 2, children drawn i.i.d. from the draft) gives the
   target Markov chain's joint law (chi-squared, fixed seeds): the walk is lossless.
+* The tree commit: after moving the accepted path, plain causal attention over
+  the cache at depth j of the path gives exactly what the tree mask gave that
+  node before the move (the mask's definition, not the move's code); a
+  chain-shaped path moves nothing; only the slots L+1 .. L+a change, and an
+  overflowing commit changes nothing.
 """
 
 import math
@@ -24,7 +29,8 @@ from oracle import commit as ocommit
 from oracle import reject as orej
 from oracle import tree as otree
 from oracle.philox import verify_uniforms
-from workloads import PRESETS, draft_from_logits, make_attention_inputs, make_reject_inputs
+from workloads import (PRESETS, draft_from_logits, make_attention_inputs, make_reject_inputs,
+                       make_tree_attention_inputs, random_parents, random_paths)
 
 GRID = 1 << 24
 
@@ -188,3 +194,79 @@ def test_monte_carlo_lossless_tree_rounds_with_commit():
             prev = tkn
         want[idx] = pr
     assert stats.chisquare(counts.ravel(), n * want.ravel()).pvalue > 1e-4
+
+
+def _tree_commit_case(seed: int, N: int = 9):
+    p = PRESETS["tiny"]
+    a = make_tree_attention_inputs(p, N, seed=seed)
+    rng = np.random.Generator(np.random.PCG64(8100 + seed))
+    parents = np.stack([random_parents(rng, N) for _ in range(p.B)])
+    nodes, depth = random_paths(rng, parents, stop=0.2)
+    return p, a, parents, nodes, depth
+
+
+def test_tree_commit_then_causal_attention_equals_the_tree_mask():
+    for seed in range(3):
+        p, a, parents, nodes, depth = _tree_commit_case(seed)
+        L = a["seq_lens"]
+        cap = a["max_blocks"] * p.block_size
+        kc, vc, newL, over = otree.commit_tree(a["k_cache"], a["v_cache"], a["block_table"], L, nodes, depth, cap)
+        assert not over.any()
+        np.testing.assert_array_equal(newL, L + depth + 1)
+        tree = otree.verify_attention_tree(a["q"], a["k_cache"], a["v_cache"], a["block_table"], L, parents,
+                                           p.Hq, p.Hkv, p.block_size, a["sm_scale"])
+        G = p.Hq // p.Hkv
+        for b in range(p.B):
+            path = [0] + [int(x) for x in nodes[b, :depth[b]]]
+            for g in range(p.Hkv):
+                K, Vv = oatt.gather_sequence_kv(kc, vc, a["block_table"], b, g, int(L[b]) + len(path),
+                                                p.block_size)
+                for j, n in enumerate(path):
+                    vis = int(L[b]) + j + 1          # causal: keys 0 .. L + j
+                    for h in range(g * G, (g + 1) * G):
+                        got = oatt.attend(oatt.bf16_to_f64(a["q"][b, n, h]), K[:vis], Vv[:vis], a["sm_scale"])
+                        np.testing.assert_array_equal(got, tree[b, n, h])
+
+
+def test_tree_commit_chain_path_moves_nothing():
+    p = PRESETS["tiny"]
+    N = 6
+    a = make_tree_attention_inputs(p, N, seed=1)
+    depth = np.array([0, 2, 6, 4], dtype=np.int32)[: p.B]
+    nodes = np.full((p.B, N), -1, dtype=np.int32)
+    for b in range(p.B):
+        nodes[b, :depth[b]] = np.arange(1, depth[b] + 1)
+    kc, vc, newL, over = otree.commit_tree(a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], nodes, depth,
+                                           10 ** 6)
+    np.testing.assert_array_equal(kc, a["k_cache"])
+    np.testing.assert_array_equal(vc, a["v_cache"])
+    np.testing.assert_array_equal(newL, a["seq_lens"] + depth + 1)
+
+
+def test_tree_commit_touches_only_the_new_prefix_and_refuses_overflow():
+    p, a, parents, nodes, depth = _tree_commit_case(5)
+    L = a["seq_lens"].astype(np.int64)
+    cap = int(L[1] + depth[1])                  # sequence 1 would pass the capacity by one token
+    kc, vc, newL, over = otree.commit_tree(a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], nodes, depth,
+                                           cap)
+    bs = p.block_size
+    allowed = set()
+    for b in range(p.B):
+        if over[b]:
+            assert newL[b] == L[b]
+            continue
+        for j in range(1, int(depth[b]) + 1):
+            allowed.add((int(a["block_table"][b, (L[b] + j) // bs]), int((L[b] + j) % bs)))
+    assert over[1] == 1
+    changed_k = {(int(pg), int(o)) for pg, _, o in zip(*np.nonzero((kc != a["k_cache"]).any(axis=3)))}
+    changed_v = {(int(pg), int(o)) for pg, _, o in zip(*np.nonzero((vc != a["v_cache"]).any(axis=2)))}
+    assert changed_k <= allowed and changed_v <= allowed
+    # every moved slot holds the old row of its node
+    for b in range(p.B):
+        if over[b]:
+            continue
+        for j in range(1, int(depth[b]) + 1):
+            sp, so = int(a["block_table"][b, (L[b] + nodes[b, j - 1]) // bs]), int((L[b] + nodes[b, j - 1]) % bs)
+            dp, do = int(a["block_table"][b, (L[b] + j) // bs]), int((L[b] + j) % bs)
+            np.testing.assert_array_equal(kc[dp, :, do, :], a["k_cache"][sp, :, so, :])
+            np.testing.assert_array_equal(vc[dp, :, :, do], a["v_cache"][sp, :, :, so])

@@ -10,4 +10,4 @@ from .gen import PRESETS, Preset, make_attention_inputs, make_reject_inputs, mak
 from .gen import bf16_bits, verify_seed, draft_from_logits  # noqa: F401
 from .ragged import (make_ragged_attention_inputs, make_ragged_reject_inputs, pack_reject_inputs,  # noqa: F401
                      ragged_draft_lengths, offsets)
-from .tree import make_tree_attention_inputs, make_tree_reject_inputs, random_parents, tree_parents  # noqa: F401
+from .tree import make_tree_attention_inputs, make_tree_reject_inputs, random_parents, random_paths, tree_parents  # noqa: F401

@@ -42,6 +42,27 @@ def random_parents(rng: np.random.Generator, N: int, max_children: int = 4) -> n
     return np.array(parents, dtype=np.int32)
 
 
+def random_paths(rng: np.random.Generator, parents: np.ndarray, stop: float = 0.25) -> tuple:
+    """A random root-to-node path in each sequence's tree: from the root, stop with probability
+    `stop` (or at a leaf), else step to a uniformly chosen child. Returns (accepted_nodes [B][N],
+    path order then -1; depth [B]) for parents [B][N]."""
+    par = np.asarray(parents)
+    B, N = par.shape
+    nodes = np.full((B, N), -1, dtype=np.int32)
+    depth = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        v, d = 0, 0
+        while True:
+            kids = [n for n in range(1, N + 1) if int(par[b, n - 1]) == v]
+            if not kids or rng.random() < stop:
+                break
+            v = int(rng.choice(kids))
+            nodes[b, d] = v
+            d += 1
+        depth[b] = d
+    return nodes, depth
+
+
 def make_tree_reject_inputs(preset: Preset, parents: np.ndarray, seed: int | None = None, B: int | None = None) -> dict:
     """target [B][N+1][V], draft [B][N+1][V], tokens [B][N] drawn from q at each parent,
     parents [B][N] (the same tree for every sequence if a 1-d array is given)."""
