@@ -376,7 +376,10 @@ def tree_shape(spec: str) -> tuple[int, int]:
 
 
 def gpu_bench_tree(args, p, dev) -> dict:
-    """The 8B step over a full t-ary draft tree of depth d (the same tree for every sequence)."""
+    """The 8B step over a full t-ary draft tree of depth d (the same tree for every sequence):
+    tree attention, the tree walk, and the tree commit (the accepted path's KV rows move to
+    L+1 .. L+a, then the lengths). The lengths are restored before every step; the moved rows
+    only change attention outputs, which the walk does not read, so every step does the same work."""
     import numpy as np
     import torch
     import speculative_decoding_verification_14_amd as sv
@@ -425,7 +428,7 @@ def gpu_bench_tree(args, p, dev) -> dict:
                               acc_nodes, out_probs, acc_probs, rej_ws, stream)
         if events is not None:
             events[2].record(stream)
-        sv.commit_lengths(seq_lens, num_acc, N, cap, overflow, stream)
+        sv.commit_tree(kc, vc, bt, seq_lens, acc_nodes, num_acc, cap, overflow, stream)
         if events is not None:
             events[3].record(stream)
 
@@ -463,7 +466,7 @@ def gpu_bench_tree(args, p, dev) -> dict:
         config=dict(workload=(f"{args.workload} with a draft tree: B={B}, full {t_br}-ary tree of depth {depth} "
                               f"(N={N} draft nodes), Hq={p.Hq}, Hkv={p.Hkv}, D={p.D}, contexts {p.ctx}, "
                               f"block_size={p.block_size}, V={p.V}, T={p.temperature}, "
-                              "one attention layer + tree walk + commit"),
+                              "one attention layer + tree walk + tree commit"),
                     global_batch=B, k=f"tree {t_br}x{depth}", parallelism="none (1 GPU)"),
         roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
                       traffic=None, kernel="spec_verify_attn_tree (attn_streamk_kernel + attn_merge_kernel)",
@@ -474,7 +477,7 @@ def gpu_bench_tree(args, p, dev) -> dict:
                                       frac_of_peak=attn_gbs / HBM_PEAK_GBS),
                      reject_sample=dict(avg_us=rej_s * 1e6, bytes=r_bytes, gbs=rej_gbs,
                                         frac_of_peak=rej_gbs / HBM_PEAK_GBS),
-                     commit_lengths=dict(avg_us=com_s * 1e6)),
+                     commit_tree=dict(avg_us=com_s * 1e6)),
         cold_cache=cold_cache_calls(step, dev, args.cold_steps),
     )
 

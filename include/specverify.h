@@ -253,8 +253,8 @@ spec_status spec_reject_sample_ragged(const float* target_logits, const float* d
  *                                  then -1
  *  num_accepted  int32 [B]         a_b = depth of the last accepted node
  *  accepted_nodes int32 [B][N] or NULL: the accepted nodes in path order, then -1
- *                (their KV rows are the ones to keep at L_b+1 .. L_b+a_b before
- *                the commit L' = L + a + 1; moving them is the caller's)
+ *                (their KV rows are the ones to keep at L_b+1 .. L_b+a_b;
+ *                spec_commit_tree moves them and commits L' = L + a + 1)
  *  out_probs     fp32 [B][N+1] or NULL: p at the deciding node of each emitted token
  *  accept_probs  fp32 [B][N]   or NULL: min(1, r(x)/q(x)) at each tested node, -1 else
  *
@@ -291,6 +291,36 @@ spec_status spec_reject_sample_tree(const float* target_logits, const float* dra
  * ---------------------------------------------------------------------- */
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
                                 int32_t capacity_tokens, int32_t* overflow_flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Tree commit  [RESP] (GAP 1: a tree of drafts checked in one pass; "Adaptive
+ * Server": the KV cache is extended in place). After spec_reject_sample_tree the
+ * committed prefix is the root and the accepted path n_1 .. n_a, whose KV rows sit
+ * at slots L_b + n_j. For every sequence whose commit fits, slot L_b + j takes the
+ * K and V rows (all KV heads) that slot L_b + n_j held before the call, j = 1 .. a
+ * (the root stays at L_b), then seq_lens[b] += a + 1 as in spec_commit_lengths. A
+ * commit past capacity_tokens moves nothing (overflow_flags[b] = 1); a_b <= 0
+ * moves nothing. Slots past L_b + a_b keep their old rows (they lie beyond the new
+ * length). Two launches on `stream`: the move, then the length commit.
+ *
+ *  k_cache / v_cache  bf16 paged caches, as for spec_verify_attn (in/out)
+ *  block_table        int32 [B][max_blocks]; slots L_b .. L_b + nodes must map to
+ *                     pages that no other sequence's slots L .. L + nodes use
+ *  seq_lens           int32 [B] in/out (the lengths the tree step ran at)
+ *  accepted_nodes     int32 [B][nodes]: the accepted nodes in path order (as written
+ *                     by spec_reject_sample_tree); entry j-1 must lie in [j, nodes]
+ *  num_accepted       int32 [B]: a_b (-1, an error of the walk, moves nothing)
+ *  overflow_flags     int32 [B] or NULL
+ *
+ * Shapes: 1 <= B <= 65535; 1 <= nodes <= 15; 1 <= Hkv <= 65535; D in {64, 128};
+ * block_size a power of two in [16, 64]. A node index or page id out of range
+ * leaves that sequence's cache untouched (a device-side precondition: the length
+ * commit still runs).
+ * ---------------------------------------------------------------------- */
+spec_status spec_commit_tree(void* k_cache, void* v_cache, const int32_t* block_table, int32_t* seq_lens,
+                             const int32_t* accepted_nodes, const int32_t* num_accepted, int32_t B,
+                             int32_t nodes, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
+                             int32_t num_blocks, int32_t capacity_tokens, int32_t* overflow_flags, void* stream);
 
 #ifdef __cplusplus
 }

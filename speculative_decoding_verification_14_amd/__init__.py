@@ -18,6 +18,7 @@ import threading
 __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", "reject_sample",
            "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
            "reject_sample_ragged", "verify_attn_tree", "reject_sample_tree", "reject_sample_tree_workspace_size",
+           "commit_tree",
            "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -42,6 +43,7 @@ SYMBOLS = {
     "spec_reject_sample_tree_workspace_size": (_c_int32, [_c_int32] * 3 + [ctypes.POINTER(_c_size)]),
     "spec_reject_sample_tree": (_c_int32, [_vp] * 6 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
                                 + [_vp] * 6 + [_c_size, _vp]),
+    "spec_commit_tree": (_c_int32, [_vp] * 6 + [_c_int32] * 8 + [_vp, _vp]),
 }
 
 
@@ -308,6 +310,25 @@ def commit_lengths(seq_lens, num_accepted, k: int, capacity_tokens: int, overflo
                                          _need(num_accepted, torch.int32, "num_accepted"), B, int(k),
                                          int(capacity_tokens), _opt(overflow_flags, torch.int32, "overflow_flags"),
                                          _stream_handle(stream)), "spec_commit_lengths")
+    return seq_lens
+
+
+def commit_tree(k_cache, v_cache, block_table, seq_lens, accepted_nodes, num_accepted, capacity_tokens: int,
+                overflow_flags=None, stream=None):
+    """spec_commit_tree: move the accepted path's KV rows to L+1 .. L+a, then seq_lens[b] += a + 1
+    unless past capacity_tokens. accepted_nodes int32 [B][N] as written by reject_sample_tree."""
+    import torch
+    B, N = accepted_nodes.shape
+    NB, Hkv, bs, D = k_cache.shape
+    _check(library().spec_commit_tree(_need(k_cache, torch.bfloat16, "k_cache"),
+                                      _need(v_cache, torch.bfloat16, "v_cache"),
+                                      _need(block_table, torch.int32, "block_table"),
+                                      _need(seq_lens, torch.int32, "seq_lens"),
+                                      _need(accepted_nodes, torch.int32, "accepted_nodes"),
+                                      _need(num_accepted, torch.int32, "num_accepted"), B, N, Hkv, D, bs,
+                                      block_table.shape[1], NB, int(capacity_tokens),
+                                      _opt(overflow_flags, torch.int32, "overflow_flags"), _stream_handle(stream)),
+           "spec_commit_tree")
     return seq_lens
 
 

@@ -247,4 +247,24 @@ spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, 
                                   static_cast<hipStream_t>(stream)));
 }
 
+spec_status spec_commit_tree(void* k_cache, void* v_cache, const int32_t* block_table, int32_t* seq_lens,
+                             const int32_t* accepted_nodes, const int32_t* num_accepted, int32_t B,
+                             int32_t nodes, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
+                             int32_t num_blocks, int32_t capacity_tokens, int32_t* overflow_flags, void* stream) {
+    if (!k_cache || !v_cache || !block_table || !seq_lens || !accepted_nodes || !num_accepted)
+        return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || B > 65535 || nodes < 1 || nodes > 15 || Hkv < 1 || Hkv > 65535) return SPEC_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return SPEC_ERR_BAD_SHAPE;
+    if (!is_pow2_in(block_size, 16, 64) || max_blocks < 1 || num_blocks < 1 || capacity_tokens < 1)
+        return SPEC_ERR_BAD_SHAPE;
+    const spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    TreeCommitLaunch p;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.block_table = block_table; p.seq_lens = seq_lens;
+    p.accepted_nodes = accepted_nodes; p.num_accepted = num_accepted; p.overflow_flags = overflow_flags;
+    p.B = B; p.nodes = nodes; p.Hkv = Hkv; p.D = D; p.block_size = block_size; p.max_blocks = max_blocks;
+    p.num_blocks = num_blocks; p.capacity = capacity_tokens;
+    return from_hip(launch_tree_commit(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

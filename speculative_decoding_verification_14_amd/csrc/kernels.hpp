@@ -62,4 +62,18 @@ hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream);
 hipError_t launch_commit(int32_t* seq_lens, const int32_t* num_accepted, int B, int capacity,
                          int32_t* overflow_flags, hipStream_t stream);
 
+struct TreeCommitLaunch {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_table;
+    int32_t* seq_lens;
+    const int32_t* accepted_nodes;   // [B][nodes]
+    const int32_t* num_accepted;
+    int32_t* overflow_flags;
+    int B, nodes, Hkv, D, block_size, max_blocks, num_blocks, capacity;
+};
+
+// Moves the accepted path's KV rows to L+1 .. L+a, then commits the lengths.
+hipError_t launch_tree_commit(const TreeCommitLaunch& p, hipStream_t stream);
+
 }  // namespace specverify

@@ -93,6 +93,22 @@ def test_commit_validation(lib):
     assert lib.spec_commit_lengths(FAKE, FAKE, 4, 16, 100, NULL, NULL) == 2
 
 
+def _tree_commit_args(**over):
+    a = dict(kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, nodes=FAKE, acc=FAKE, B=4, N=6, Hkv=2, D=64, bs=16, mb=8, nb=32,
+             cap=128, over=NULL, stream=NULL)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(nodes=NULL), 1), (dict(kc=NULL), 1), (dict(acc=NULL), 1),
+    (dict(B=0), 2), (dict(N=0), 2), (dict(N=16), 2), (dict(Hkv=0), 2), (dict(D=96), 2), (dict(bs=8), 2),
+    (dict(bs=24), 2), (dict(mb=0), 2), (dict(nb=0), 2), (dict(cap=0), 2),
+])
+def test_tree_commit_validation(lib, over, code):
+    assert lib.spec_commit_tree(*_tree_commit_args(**over)) == code
+
+
 def test_workspace_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.spec_reject_sample_workspace_size(64, 3, 128256, ctypes.byref(n)) == 0
@@ -117,3 +133,4 @@ def test_no_device_is_reported_not_crashed(lib):
     assert lib.spec_verify_attn(*_attn_args()) == 5
     assert lib.spec_reject_sample(*_rej_args()) == 5
     assert lib.spec_commit_lengths(FAKE, FAKE, 4, 3, 100, NULL, NULL) == 5
+    assert lib.spec_commit_tree(*_tree_commit_args()) == 5
