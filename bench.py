@@ -22,6 +22,8 @@ Other modes:
   --variant ragged             per-sequence draft lengths k_b ~ U{0..7}
   --variant tree [--tree T,D]  a full T-ary draft tree of depth D (default 2,2: six
                                nodes) through the tree attention and the tree walk
+  --variant fused              RoPE + KV append, attention, the LM head (H = 4096),
+                               rejection sampling on its logits, and the commit
   --cpu-baseline-only          time the oracle (run in a single-threaded child)
   --copy-calibration           also run an elementwise kernel of known traffic
                                (negation of 512 MiB fp32: 512 MiB read, 512 MiB
@@ -370,6 +372,129 @@ def gpu_bench_ragged(args, p, dev) -> dict:
     )
 
 
+def gpu_bench_fused(args, p, dev) -> dict:
+    """The whole verify pass of one attention layer plus the output head on the 8B shape: RoPE and
+    KV append of the k+1 new rows, verify attention, the LM head (hidden [B(k+1)][4096] x W
+    [128256][4096]^T), rejection sampling on those logits, and the commit. The draft logits are the
+    LM head's logits plus the 8B recipe's draft noise, and the draft tokens are sampled from them,
+    so acceptance behaves as in the three-call step."""
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_14_amd as sv
+    from workloads import (ROPE_THETA, draft_from_logits, make_attention_inputs, make_lm_head_inputs,
+                           make_new_rows, verify_seed)
+
+    B, k, H = p.B, p.k, 4096
+    R = B * (k + 1)
+    theta = ROPE_THETA.get(args.workload, 500000.0)
+    print(f"[bench] generating {args.workload} inputs for the fused pass (R = {R}, H = {H}, V = {p.V})",
+          file=sys.stderr, flush=True)
+    a = make_attention_inputs(p)
+    rows = make_new_rows(p, k, seed=p.index)
+    lm = make_lm_head_inputs(R, H, p.V, seed=p.index)
+    bf16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q, kn, vn = bf16(rows["q"]), bf16(rows["k_new"]), bf16(rows["v_new"])
+    kc, vc, bt = bf16(a["k_cache"]), bf16(a["v_cache"]), t(a["block_table"])
+    del a["k_cache"], a["v_cache"]
+    hidden, weight = bf16(lm["hidden"]), bf16(lm["weight"])
+    del lm
+    tl = torch.empty((B, k + 1, p.V), dtype=torch.float32, device=dev)
+    sv.lm_head(hidden, weight, tl)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(1000 + p.index))
+    target = tl.cpu().numpy()
+    draft = np.ascontiguousarray(target[:, :k] + rng.standard_normal((B, k, p.V), dtype=np.float32)
+                                 * np.float32(p.draft_sigma))
+    tokens = draft_from_logits(rng, draft, p.temperature).astype(np.int32)
+    dl, dt = t(draft), t(tokens)
+    sid = t((np.arange(B, dtype=np.int64) * 7919 + 1_000_003 * (p.index + 1)).astype(np.int64))
+    seq_lens0 = t(a["seq_lens"])
+    seq_lens = seq_lens0.clone()
+    attn_out = torch.empty_like(q)
+    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    num_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out_probs = torch.empty((B, k + 1), dtype=torch.float32, device=dev)
+    acc_probs = torch.empty((B, k), dtype=torch.float32, device=dev)
+    overflow = torch.empty(B, dtype=torch.int32, device=dev)
+    cap = a["max_blocks"] * p.block_size
+    msl = a["max_seq_len"]
+    attn_ws = torch.zeros(max(256, sv.verify_attn_workspace_size(B, k, p.Hq, p.Hkv, p.D, msl)),
+                          dtype=torch.uint8, device=dev)
+    rej_ws = torch.zeros(sv.reject_sample_workspace_size(B, k, p.V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    seed = verify_seed(p)
+
+    def step(events=None):
+        rec = (lambda i: events[i].record(stream)) if events is not None else (lambda i: None)
+        seq_lens.copy_(seq_lens0)
+        rec(0)
+        sv.rope_append(q, kn, vn, kc, vc, bt, seq_lens, theta, None, stream)   # q turns again each step
+        rec(1)
+        sv.verify_attn(q, kc, vc, bt, seq_lens, attn_out, msl, None, attn_ws, stream)
+        rec(2)
+        sv.lm_head(hidden, weight, tl, stream)
+        rec(3)
+        sv.reject_sample(tl, dl, dt, sid, seq_lens, p.temperature, seed, out_tokens, num_acc, out_probs, acc_probs,
+                         rej_ws, stream)
+        rec(4)
+        sv.commit_lengths(seq_lens, num_acc, k, cap, overflow, stream)
+        rec(5)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    acc_ref = num_acc.cpu().numpy().copy()
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(6)] for i in sampled}
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    acc = num_acc.cpu().numpy()
+    if not np.array_equal(acc, acc_ref):
+        raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
+    mean = lambda v: sum(v) / len(v)
+    call_s = [mean([e[j].elapsed_time(e[j + 1]) for e in evs.values()]) / 1e3 for j in range(5)]
+    a_bytes, r_bytes, _ = algorithmic_bytes(p, a["seq_lens"], acc)
+    lm_bytes = p.V * H * 2 + R * H * 2 + R * p.V * 4
+    lm_flops = 2.0 * R * H * p.V
+    rope_bytes = B * (k + 1) * (p.Hq * 2 + p.Hkv * 3) * p.D * 2
+    tokens = int(np.sum(acc + 1))
+    step_s = wall / args.steps
+    gbs = lambda by, sec: by / sec / 1e9
+    lm_gbs, lm_tf = gbs(lm_bytes, call_s[2]), lm_flops / call_s[2] / 1e12
+    return dict(
+        metric=METRIC, value=tokens / step_s, unit="verified tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=step_s * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=(f"{args.workload} fused pass: B={B}, k={k}, Hq={p.Hq}, Hkv={p.Hkv}, D={p.D}, "
+                              f"contexts {p.ctx}, block_size={p.block_size}, H={H}, V={p.V}, T={p.temperature}, "
+                              f"RoPE theta={theta:g}; RoPE + KV append, one attention layer, LM head, rejection "
+                              "sampling, commit"),
+                    global_batch=B, k=k, parallelism="none (1 GPU)"),
+        roofline=dict(bound="hbm", achieved=lm_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=lm_gbs / HBM_PEAK_GBS,
+                      traffic=None, kernel="spec_lm_head (lm_head_kernel)", algorithmic_bytes_per_call=lm_bytes,
+                      avg_call_us=call_s[2] * 1e6,
+                      mfma=dict(achieved=lm_tf, peak=2500.0, unit="TFLOP/s", frac=lm_tf / 2500.0)),
+        verified_tokens_per_step=tokens,
+        mean_emitted_per_sequence=tokens / B,
+        kernels=dict(
+            rope_append=dict(avg_us=call_s[0] * 1e6, bytes=rope_bytes, gbs=gbs(rope_bytes, call_s[0])),
+            verify_attn=dict(avg_us=call_s[1] * 1e6, bytes=a_bytes, gbs=gbs(a_bytes, call_s[1]),
+                             frac_of_peak=gbs(a_bytes, call_s[1]) / HBM_PEAK_GBS),
+            lm_head=dict(avg_us=call_s[2] * 1e6, bytes=lm_bytes, gbs=lm_gbs, frac_of_peak=lm_gbs / HBM_PEAK_GBS,
+                         tflops=lm_tf, frac_of_mfma_peak=lm_tf / 2500.0),
+            reject_sample=dict(avg_us=call_s[3] * 1e6, bytes=r_bytes, gbs=gbs(r_bytes, call_s[3]),
+                               frac_of_peak=gbs(r_bytes, call_s[3]) / HBM_PEAK_GBS),
+            commit_lengths=dict(avg_us=call_s[4] * 1e6)),
+    )
+
+
 def tree_shape(spec: str) -> tuple[int, int]:
     t, d = (int(x) for x in spec.split(","))
     return t, d
@@ -515,6 +640,8 @@ def gpu_bench(args) -> dict:
         return gpu_bench_ragged(args, p, dev)
     if args.variant == "tree":
         return gpu_bench_tree(args, p, dev)
+    if args.variant == "fused":
+        return gpu_bench_fused(args, p, dev)
     print(f"[bench] generating {args.workload} inputs (k = {p.k})", file=sys.stderr, flush=True)
     inp = make_inputs(args.workload, preset=p)
 
@@ -649,7 +776,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="8b")
-    ap.add_argument("--variant", choices=["uniform", "plain", "ragged", "tree"], default="uniform")
+    ap.add_argument("--variant", choices=["uniform", "plain", "ragged", "tree", "fused"], default="uniform")
     ap.add_argument("--tree", default="2,2", metavar="T,D",
                     help="tree variant: branching factor and depth of the full draft tree")
     ap.add_argument("--cold-steps", type=int, default=30,

@@ -322,6 +322,47 @@ spec_status spec_commit_tree(void* k_cache, void* v_cache, const int32_t* block_
                              int32_t nodes, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
                              int32_t num_blocks, int32_t capacity_tokens, int32_t* overflow_flags, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Upstream of the verify step  [ACC] (section 2: the target checks all k drafts in
+ * one forward pass, whose output distribution the sampler reads); [RESP] ("Adaptive
+ * Server": the KV cache is extended in place). The pages name no position encoding
+ * or output head; the readings here are rotate-half RoPE and a plain LM head.
+ *
+ * spec_rope_append: for the k+1 new rows of every sequence (row 0 the last committed
+ * token, rows 1..k the drafts; for a tree, row n is node n), rotate q (in place) and
+ * k_new by RoPE at position P = L_b + i (tree: L_b + depth(n)), then write the
+ * rotated K and the given V into cache slot L_b + i (tree: L_b + n). For each pair
+ * j in [0, D/2) the elements (x_j, x_{j+D/2}) turn by the angle P * theta^(-2j/D);
+ * the rotation is computed in float64 and rounded once to bfloat16 (nearest even).
+ *
+ *  q       bf16 [B][k+1][Hq][D] in/out    k_new, v_new  bf16 [B][k+1][Hkv][D]
+ *  k_cache, v_cache, block_table   as for spec_verify_attn (the cache is written)
+ *  seq_lens int32 [B] (L_b, before the step)
+ *  parents  int32 [B][k] (a tree, positions by depth) or NULL (a chain)
+ *  rope_theta > 1 (500000 for the 8B shape, 1000000 for the Qwen shapes)
+ * Shapes: 1 <= B <= 65535; 0 <= k <= 15 (k >= 1 with parents); Hq a multiple of
+ * Hkv; D in {64, 128}; block_size a power of two in [16, 64]. A row whose slot lies
+ * outside the block table, or on a page id out of range, is rotated but not
+ * appended (a device-side precondition). One launch.
+ *
+ * spec_lm_head: logits[r][v] = sum_h hidden[r][h] * weight[v][h], bf16 operands with
+ * float32 accumulation (each bf16 product is exact in float32; the sum is within
+ * H * 2^-24 / (1 - H * 2^-24) of sum_h |hidden[r][h] weight[v][h]|), no bias. The
+ * rows are the verify rows in spec_reject_sample's order, so `logits` is its
+ * target_logits as written.
+ *
+ *  hidden  bf16 [R][H]   weight  bf16 [V][H]   logits  fp32 [R][V] (written)
+ * Shapes: 1 <= R <= 65535 * 256; V >= 1; H a positive multiple of 128; V * H <= 2^40.
+ * One launch.
+ * ---------------------------------------------------------------------- */
+spec_status spec_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, const int32_t* parents,
+                             int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                             int32_t max_blocks, int32_t num_blocks, double rope_theta, void* stream);
+
+spec_status spec_lm_head(const void* hidden, const void* weight, float* logits, int32_t R, int32_t H, int32_t V,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

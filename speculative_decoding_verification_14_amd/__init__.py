@@ -18,7 +18,7 @@ import threading
 __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", "reject_sample",
            "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
            "reject_sample_ragged", "verify_attn_tree", "reject_sample_tree", "reject_sample_tree_workspace_size",
-           "commit_tree",
+           "commit_tree", "rope_append", "lm_head",
            "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -44,6 +44,8 @@ SYMBOLS = {
     "spec_reject_sample_tree": (_c_int32, [_vp] * 6 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
                                 + [_vp] * 6 + [_c_size, _vp]),
     "spec_commit_tree": (_c_int32, [_vp] * 6 + [_c_int32] * 8 + [_vp, _vp]),
+    "spec_rope_append": (_c_int32, [_vp] * 8 + [_c_int32] * 8 + [ctypes.c_double, _vp]),
+    "spec_lm_head": (_c_int32, [_vp] * 3 + [_c_int32] * 3 + [_vp]),
 }
 
 
@@ -330,6 +332,38 @@ def commit_tree(k_cache, v_cache, block_table, seq_lens, accepted_nodes, num_acc
                                       _opt(overflow_flags, torch.int32, "overflow_flags"), _stream_handle(stream)),
            "spec_commit_tree")
     return seq_lens
+
+
+def rope_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, rope_theta: float, parents=None,
+                stream=None):
+    """spec_rope_append: rotate q (in place) and k_new by RoPE at each row's position, then write the
+    rotated K and v_new into cache slots L_b + i. q bf16 [B][k+1][Hq][D]; k_new / v_new bf16
+    [B][k+1][Hkv][D]; parents int32 [B][k] for a tree (positions by depth), else None."""
+    import torch
+    B, K1, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    _check(library().spec_rope_append(_need(q, torch.bfloat16, "q"), _need(k_new, torch.bfloat16, "k_new"),
+                                      _need(v_new, torch.bfloat16, "v_new"),
+                                      _need(k_cache, torch.bfloat16, "k_cache"),
+                                      _need(v_cache, torch.bfloat16, "v_cache"),
+                                      _need(block_table, torch.int32, "block_table"),
+                                      _need(seq_lens, torch.int32, "seq_lens"), _opt(parents, torch.int32, "parents"),
+                                      B, K1 - 1, Hq, Hkv, D, bs, block_table.shape[1], NB, float(rope_theta),
+                                      _stream_handle(stream)), "spec_rope_append")
+    return q
+
+
+def lm_head(hidden, weight, logits, stream=None):
+    """spec_lm_head: logits fp32 [R][V] = hidden bf16 [R][H] x weight bf16 [V][H]^T."""
+    import torch
+    R, H = hidden.shape
+    V = weight.shape[0]
+    if weight.shape[1] != H or logits.numel() != R * V or logits.shape[-1] != V:
+        raise ValueError("lm_head: hidden [R][H], weight [V][H] and logits [..][V] with R * V elements")
+    _check(library().spec_lm_head(_need(hidden, torch.bfloat16, "hidden"), _need(weight, torch.bfloat16, "weight"),
+                                  _need(logits, torch.float32, "logits"), R, H, V, _stream_handle(stream)),
+           "spec_lm_head")
+    return logits
 
 
 def verify_step(q, k_cache, v_cache, block_table, seq_lens, attn_out, max_seq_len, target_logits, draft_logits,

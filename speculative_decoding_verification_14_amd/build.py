@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "attention.hip", "reject.hip", "commit.hip"]
+SOURCES = ["api.hip", "attention.hip", "reject.hip", "commit.hip", "upstream.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.

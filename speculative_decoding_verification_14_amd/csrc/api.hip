@@ -267,4 +267,37 @@ spec_status spec_commit_tree(void* k_cache, void* v_cache, const int32_t* block_
     return from_hip(launch_tree_commit(p, static_cast<hipStream_t>(stream)));
 }
 
+spec_status spec_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, const int32_t* parents,
+                             int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                             int32_t max_blocks, int32_t num_blocks, double rope_theta, void* stream) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens) return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || B > 65535 || k < 0 || k > 15 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return SPEC_ERR_BAD_SHAPE;
+    if (parents && k < 1) return SPEC_ERR_BAD_SHAPE;
+    if (D != 64 && D != 128) return SPEC_ERR_BAD_SHAPE;
+    if (!is_pow2_in(block_size, 16, 64) || max_blocks < 1 || num_blocks < 1) return SPEC_ERR_BAD_SHAPE;
+    if (!(std::isfinite(rope_theta) && rope_theta > 1.0)) return SPEC_ERR_BAD_VALUE;
+    const spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    RopeLaunch p;
+    p.q = q; p.k_new = k_new; p.v_new = v_new; p.k_cache = k_cache; p.v_cache = v_cache;
+    p.block_table = block_table; p.seq_lens = seq_lens; p.parents = parents;
+    p.B = B; p.k = k; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.block_size = block_size; p.max_blocks = max_blocks;
+    p.num_blocks = num_blocks; p.theta = rope_theta;
+    return from_hip(launch_rope_append(p, static_cast<hipStream_t>(stream)));
+}
+
+spec_status spec_lm_head(const void* hidden, const void* weight, float* logits, int32_t R, int32_t H, int32_t V,
+                         void* stream) {
+    if (!hidden || !weight || !logits) return SPEC_ERR_NULL_POINTER;
+    if (R < 1 || R > 65535 * 256 || V < 1 || H < lm_head_k_multiple() || H % lm_head_k_multiple() != 0)
+        return SPEC_ERR_BAD_SHAPE;
+    if (static_cast<long long>(V) * H > (1LL << 40)) return SPEC_ERR_BAD_SHAPE;
+    const spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    LmHeadLaunch p;
+    p.hidden = hidden; p.weight = weight; p.logits = logits; p.R = R; p.H = H; p.V = V;
+    return from_hip(launch_lm_head(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -76,4 +76,29 @@ struct TreeCommitLaunch {
 // Moves the accepted path's KV rows to L+1 .. L+a, then commits the lengths.
 hipError_t launch_tree_commit(const TreeCommitLaunch& p, hipStream_t stream);
 
+struct RopeLaunch {
+    void* q;                    // [B][k+1][Hq][D] bf16, rotated in place
+    const void* k_new;          // [B][k+1][Hkv][D] bf16
+    const void* v_new;          // [B][k+1][Hkv][D] bf16
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* parents;     // tree: [B][k], or NULL
+    int B, k, Hq, Hkv, D, block_size, max_blocks, num_blocks;
+    double theta;
+};
+
+hipError_t launch_rope_append(const RopeLaunch& p, hipStream_t stream);
+
+struct LmHeadLaunch {
+    const void* hidden;   // [R][H] bf16
+    const void* weight;   // [V][H] bf16
+    float* logits;        // [R][V]
+    int R, H, V;
+};
+
+int lm_head_k_multiple();   // H must be a multiple of this
+hipError_t launch_lm_head(const LmHeadLaunch& p, hipStream_t stream);
+
 }  // namespace specverify

@@ -109,6 +109,31 @@ def test_tree_commit_validation(lib, over, code):
     assert lib.spec_commit_tree(*_tree_commit_args(**over)) == code
 
 
+def _rope_args(**over):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, par=NULL, B=4, k=3, Hq=8, Hkv=2, D=64,
+             bs=16, mb=8, nb=32, theta=500000.0, stream=NULL)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=NULL), 1), (dict(vc=NULL), 1), (dict(sl=NULL), 1),
+    (dict(B=0), 2), (dict(k=16), 2), (dict(k=-1), 2), (dict(k=0, par=FAKE), 2), (dict(Hq=7), 2), (dict(D=80), 2),
+    (dict(bs=128), 2), (dict(nb=0), 2), (dict(theta=1.0), 3), (dict(theta=float("nan")), 3),
+])
+def test_rope_append_validation(lib, over, code):
+    assert lib.spec_rope_append(*_rope_args(**over)) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, FAKE, FAKE, 4, 256, 100), 1), ((FAKE, FAKE, NULL, 4, 256, 100), 1),
+    ((FAKE, FAKE, FAKE, 0, 256, 100), 2), ((FAKE, FAKE, FAKE, 4, 64, 100), 2), ((FAKE, FAKE, FAKE, 4, 320, 100), 2),
+    ((FAKE, FAKE, FAKE, 4, 256, 0), 2), ((FAKE, FAKE, FAKE, 4, 1 << 24, 1 << 17), 2),
+])
+def test_lm_head_validation(lib, args, code):
+    assert lib.spec_lm_head(*args, NULL) == code
+
+
 def test_workspace_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.spec_reject_sample_workspace_size(64, 3, 128256, ctypes.byref(n)) == 0
@@ -134,3 +159,5 @@ def test_no_device_is_reported_not_crashed(lib):
     assert lib.spec_reject_sample(*_rej_args()) == 5
     assert lib.spec_commit_lengths(FAKE, FAKE, 4, 3, 100, NULL, NULL) == 5
     assert lib.spec_commit_tree(*_tree_commit_args()) == 5
+    assert lib.spec_rope_append(*_rope_args()) == 5
+    assert lib.spec_lm_head(FAKE, FAKE, FAKE, 4, 256, 100, NULL) == 5
