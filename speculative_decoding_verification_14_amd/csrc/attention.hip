@@ -34,9 +34,12 @@
 //    replaces the causal mask inside the draft by the tree mask: node n's row sees
 //    the committed keys and the slots L + m of its ancestors m (and itself).
 //  * Ragged draft lengths (k_b per sequence, rows packed by an offsets array) use
-//    the same kernels: a sequence contributes (k_b+1) x G rows, ceil of that / 32
-//    row groups per KV head, and L_b + k_b + 1 keys to the flat work order, so
+//    the same kernels: a sequence contributes (k_b+1) x G rows, ceil of that / the
+//    row-group size per KV head, and L_b + k_b + 1 keys to the flat work order, so
 //    short drafts cost no padding work.
+//  * Row groups hold 16, 32 or 64 query rows (one, two or four MFMA tiles, chosen
+//    from the largest (k+1) x G of the call), so up to 64 rows per KV head read the
+//    KV once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,10 +65,11 @@ struct AttnArgs {
     const int32_t* cu;   // [B+1] draft-count offsets, or null: every sequence has k drafts
     const int32_t* parents;   // tree: [B][k] parent of node n at [n-1], or null (causal chain)
     uint16_t* out;
-    float* part_o;     // [kMaxP][2][32 rows][D]
-    float* part_ml;    // [kMaxP][2][32 rows][2]
+    float* part_o;     // [kMaxP][2][rg_rows][D]
+    float* part_ml;    // [kMaxP][2][rg_rows][2]
     int32_t* prefix;   // [B+1] exclusive prefix of work (iterations x row groups x KV heads) per sequence
     int B, k, Hq, Hkv, G, rows, row_groups, U, max_blocks, bs_log2, P;   // rows, row_groups, U: at k
+    int rg_rows;       // query rows per row group: 16 x the tiles of the launched kernel
     float scale_log2;
 };
 
@@ -76,7 +80,7 @@ struct SeqShape {
     int kb, row0, rows, row_groups;
 };
 
-__device__ __forceinline__ SeqShape seq_shape(const int32_t* cu, int b, int k, int G) {
+__device__ __forceinline__ SeqShape seq_shape(const int32_t* cu, int b, int k, int G, int rg_rows) {
     SeqShape s;
     if (cu) {
         const int c0 = cu[b], c1 = cu[b + 1];
@@ -87,7 +91,7 @@ __device__ __forceinline__ SeqShape seq_shape(const int32_t* cu, int b, int k, i
         s.row0 = b * (k + 1);
     }
     s.rows = (s.kb + 1) * G;
-    s.row_groups = (s.rows + 31) / 32;
+    s.row_groups = (s.rows + rg_rows - 1) / rg_rows;
     return s;
 }
 
@@ -122,8 +126,9 @@ __device__ __forceinline__ int iters_of(int seq_len, int k) {
 }
 
 // Flat work of sequence b: 128-key iterations x row groups x KV heads.
-__device__ __forceinline__ int work_of(const int32_t* seq_lens, const int32_t* cu, int b, int k, int G, int Hkv) {
-    const SeqShape sh = seq_shape(cu, b, k, G);
+__device__ __forceinline__ int work_of(const int32_t* seq_lens, const int32_t* cu, int b, int k, int G, int Hkv,
+                                       int rg_rows) {
+    const SeqShape sh = seq_shape(cu, b, k, G, rg_rows);
     return iters_of(seq_lens[b], sh.kb) * sh.row_groups * Hkv;
 }
 
@@ -141,13 +146,13 @@ __device__ __forceinline__ int range_owner(long long x, long long total, int P) 
 
 // Exclusive prefix of work per sequence, built by one 256-thread workgroup into
 // `dst` (LDS or global); dst[B] is the total.
-__device__ void build_prefix(const int32_t* seq_lens, const int32_t* cu, int B, int k, int G, int Hkv,
+__device__ void build_prefix(const int32_t* seq_lens, const int32_t* cu, int B, int k, int G, int Hkv, int rg_rows,
                              int32_t* dst, int* s_wave) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     int carry = 0;
     for (int base = 0; base < B; base += kAT) {
         const int b = base + tid;
-        int v = (b < B) ? work_of(seq_lens, cu, b, k, G, Hkv) : 0;
+        int v = (b < B) ? work_of(seq_lens, cu, b, k, G, Hkv, rg_rows) : 0;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
             const int y = __shfl_up(v, o, kWave);
@@ -168,15 +173,16 @@ __device__ void build_prefix(const int32_t* seq_lens, const int32_t* cu, int B, 
 }
 
 __global__ __launch_bounds__(kAT) void attn_plan_kernel(const int32_t* seq_lens, const int32_t* cu, int B, int k,
-                                                        int G, int Hkv, int32_t* prefix) {
+                                                        int G, int Hkv, int rg_rows, int32_t* prefix) {
     __shared__ int s_wave[kAWaves];
-    build_prefix(seq_lens, cu, B, k, G, Hkv, prefix, s_wave);
+    build_prefix(seq_lens, cu, B, k, G, Hkv, rg_rows, prefix, s_wave);
 }
 
 template <int D, int NT, bool kTree>
 __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
     constexpr int DS = D / 32;   // k-steps of S^T = K Q^T
     constexpr int DJ = D / 16;   // 16-dim blocks of O^T
+    constexpr int kRG = 16 * NT; // query rows per row group
     __shared__ int s_bt[kBtEntries];
     __shared__ int32_t s_prefix[kLdsPrefix + 1];
     __shared__ int s_wave[kAWaves];
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 
     const int32_t* prefix = a.prefix;
     if (a.B <= kLdsPrefix) {
-        build_prefix(a.seq_lens, a.cu, a.B, a.k, a.G, a.Hkv, s_prefix, s_wave);
+        build_prefix(a.seq_lens, a.cu, a.B, a.k, a.G, a.Hkv, kRG, s_prefix, s_wave);
         if (w == 0)
             for (int i = tid; i <= a.B; i += kAT) a.prefix[i] = s_prefix[i];
         prefix = s_prefix;
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
         if (prefix[mid] <= r0) lo = mid; else hi = mid - 1;
     }
     int b = lo;
-    SeqShape sh = seq_shape(a.cu, b, a.k, a.G);
+    SeqShape sh = seq_shape(a.cu, b, a.k, a.G, kRG);
     int U_b = sh.row_groups * a.Hkv;
     int iters_b = (prefix[b + 1] - prefix[b]) / U_b;
     const long long off = r0 - prefix[b];
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
         unsigned anc[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            const int r = rg * 32 + n * 16 + l16;
+            const int r = rg * kRG + n * 16 + l16;
             if (r < sh.rows) {
                 const int i = r / a.G;
                 const int h = g * a.G + r % a.G;
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                     for (int v = 0; v < kAWaves; ++v) x += s_o[v][r][d0 + dd];
                     acc[dd] = x;
                 }
-                const int row = rg * 32 + n * 16 + r;
+                const int row = rg * kRG + n * 16 + r;
                 if (whole) {
                     if (row < sh.rows) {
                         const int i = row / a.G;
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                         for (int dd = 0; dd < D / 16; ++dd) op[dd] = f32_to_bf16_bits(acc[dd] * inv);
                     }
                 } else {
-                    const size_t prow = slot * 32 + n * 16 + r;
+                    const size_t prow = slot * kRG + n * 16 + r;
                     float* po = a.part_o + prow * D + d0;
 #pragma unroll
                     for (int dd = 0; dd < D / 16; ++dd) po[dd] = acc[dd];
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                 if (++b >= a.B) break;
             } while (prefix[b + 1] == prefix[b]);
             if (b >= a.B) break;
-            sh = seq_shape(a.cu, b, a.k, a.G);
+            sh = seq_shape(a.cu, b, a.k, a.G, kRG);
             U_b = sh.row_groups * a.Hkv;
             iters_b = (prefix[b + 1] - prefix[b]) / U_b;
         }
@@ -470,7 +476,8 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) {
     const int u = blockIdx.x, b = blockIdx.y;
-    const SeqShape sh = seq_shape(a.cu, b, a.k, a.G);
+    const int rgr = 16 * tiles;
+    const SeqShape sh = seq_shape(a.cu, b, a.k, a.G, rgr);
     const int U_b = sh.row_groups * a.Hkv;
     if (u >= U_b) return;
     const long long total = a.prefix[a.B];
@@ -486,11 +493,11 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
     for (int n = 0; n < tiles; ++n) {
         const int r = tid / 16;
         const int d0 = (tid % 16) * (D / 16);
-        const int row = rg * 32 + n * 16 + r;
+        const int row = rg * rgr + n * 16 + r;
         if (row >= sh.rows) continue;
         float M = -INFINITY;
         for (int ww = w0; ww <= w1; ++ww) {
-            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * 32 + n * 16 + r;
+            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * rgr + n * 16 + r;
             M = fmaxf(M, a.part_ml[prow * 2]);
         }
         float lsum = 0.0f;
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
 #pragma unroll
         for (int dd = 0; dd < D / 16; ++dd) acc[dd] = 0.0f;
         for (int ww = w0; ww <= w1; ++ww) {
-            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * 32 + n * 16 + r;
+            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * rgr + n * 16 + r;
             const float ms = a.part_ml[prow * 2];
             const float wt = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
             lsum += wt * a.part_ml[prow * 2 + 1];
@@ -516,7 +523,7 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
 }
 
 // Persistent-grid size per (device, kernel instantiation): CUs x resident workgroups.
-int g_grid_memo[64][8];
+int g_grid_memo[64][16];
 
 template <int D, int NT, bool kTree>
 int persistent_grid(int slot) {
@@ -548,12 +555,12 @@ AttnGeometry attn_geometry(int B, int k, int Hq, int Hkv, int D, int max_seq_len
     AttnGeometry g;
     const int G = Hq / Hkv;
     g.rows = (k + 1) * G;
-    g.tiles = g.rows <= 16 ? 1 : 2;
-    g.row_groups = (g.rows + 31) / 32;
+    g.tiles = g.rows <= 16 ? 1 : (g.rows <= 32 ? 2 : 4);
+    g.row_groups = (g.rows + 16 * g.tiles - 1) / (16 * g.tiles);
     g.chunk = kIterKeys;
     g.splits = (max_seq_len + kIterKeys - 1) / kIterKeys;
     const size_t prefix_bytes = align256(sizeof(int32_t) * (size_t(B) + 1));
-    const size_t part = size_t(kMaxP) * 2 * 32;
+    const size_t part = size_t(kMaxP) * 2 * 16 * g.tiles;
     g.workspace = prefix_bytes + part * size_t(D) * sizeof(float) + part * 2 * sizeof(float);
     return g;
 }
@@ -571,7 +578,7 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     char* ws = static_cast<char*>(p.workspace);
     a.prefix = reinterpret_cast<int32_t*>(ws);
     a.part_o = reinterpret_cast<float*>(ws + align256(sizeof(int32_t) * (size_t(p.B) + 1)));
-    a.part_ml = a.part_o + size_t(kMaxP) * 2 * 32 * p.D;
+    a.part_ml = a.part_o + size_t(kMaxP) * 2 * 16 * geo.tiles * p.D;
     a.B = p.B;
     a.k = p.k;
     a.Hq = p.Hq;
@@ -579,6 +586,7 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     a.G = p.Hq / p.Hkv;
     a.rows = geo.rows;
     a.row_groups = geo.row_groups;
+    a.rg_rows = 16 * geo.tiles;
     a.U = p.Hkv * geo.row_groups;
     a.max_blocks = p.max_blocks;
     int lg = 0;
@@ -588,13 +596,13 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
 
     if (p.B > kLdsPrefix) {
         hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAT), 0, stream, p.seq_lens, p.cu_drafts, p.B, p.k, a.G,
-                           p.Hkv, a.prefix);
+                           p.Hkv, a.rg_rows, a.prefix);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 block(kAT);
     const bool tree = p.parents != nullptr;
-    const int slot = (p.D == 128 ? 0 : 4) + (geo.tiles == 1 ? 0 : 2) + (tree ? 1 : 0);
+    const int slot = (p.D == 128 ? 0 : 6) + (geo.tiles == 1 ? 0 : (geo.tiles == 2 ? 2 : 4)) + (tree ? 1 : 0);
 #define SPEC_ATTN_LAUNCH(DD, NN, TT)                                                               \
     do {                                                                                           \
         a.P = persistent_grid<DD, NN, TT>(slot);                                                   \
@@ -602,10 +610,12 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
     } while (0)
     if (p.D == 128) {
         if (geo.tiles == 1) { if (tree) SPEC_ATTN_LAUNCH(128, 1, true); else SPEC_ATTN_LAUNCH(128, 1, false); }
-        else { if (tree) SPEC_ATTN_LAUNCH(128, 2, true); else SPEC_ATTN_LAUNCH(128, 2, false); }
+        else if (geo.tiles == 2) { if (tree) SPEC_ATTN_LAUNCH(128, 2, true); else SPEC_ATTN_LAUNCH(128, 2, false); }
+        else { if (tree) SPEC_ATTN_LAUNCH(128, 4, true); else SPEC_ATTN_LAUNCH(128, 4, false); }
     } else {
         if (geo.tiles == 1) { if (tree) SPEC_ATTN_LAUNCH(64, 1, true); else SPEC_ATTN_LAUNCH(64, 1, false); }
-        else { if (tree) SPEC_ATTN_LAUNCH(64, 2, true); else SPEC_ATTN_LAUNCH(64, 2, false); }
+        else if (geo.tiles == 2) { if (tree) SPEC_ATTN_LAUNCH(64, 2, true); else SPEC_ATTN_LAUNCH(64, 2, false); }
+        else { if (tree) SPEC_ATTN_LAUNCH(64, 4, true); else SPEC_ATTN_LAUNCH(64, 4, false); }
     }
 #undef SPEC_ATTN_LAUNCH
     hipError_t e = hipGetLastError();
