@@ -6,7 +6,10 @@ last place where the exact value sits on a rounding boundary: none expected),
 for chains and trees, both head sizes, every page size, positions up to 262K,
 and composed with spec_verify_attn. spec_lm_head: every logit within the fp32
 summation bound of the exact sum, on ragged shapes (R not a multiple of 16 or
-256, V not a multiple of 16 or 256) and the 8B shape (sampled columns).
+256, V not a multiple of 16 or 256) and the 8B shape (sampled columns). The
+whole pass composed on the device (RoPE + append, attention, LM head, the
+sampler on the LM head's logits as written, the commit), each stage against the
+oracle run on what that stage received.
 """
 
 import dataclasses
@@ -15,10 +18,12 @@ import numpy as np
 import pytest
 
 from oracle import attention as oatt
+from oracle import commit as ocommit
+from oracle import reject as orej
 from oracle import upstream as oup
-from tests.parity import ATTN_TOL, bf16_dev, dev, say
-from workloads import (PRESETS, ROPE_THETA, make_attention_inputs, make_lm_head_inputs, make_new_rows,
-                       random_parents, tree_parents)
+from tests.parity import ATTN_TOL, Tally, bf16_dev, compare_reject, dev, say
+from workloads import (PRESETS, ROPE_THETA, draft_from_logits, make_attention_inputs, make_lm_head_inputs,
+                       make_new_rows, random_parents, tree_parents)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +152,61 @@ def test_lm_head_8b_shape_sampled_columns(device):
     err = np.abs(got[:, cols] - want)
     say(f"[lm head] 8b: {cols.size} columns, max err {err.max():.2e}, max err / bound {(err / bound).max():.3f}")
     assert np.all(err <= bound)
+
+
+def test_fused_pass_on_the_device(device):
+    import torch
+    import speculative_decoding_verification_14_amd as sv
+    k, H, V, T = 3, 512, 3001, 1.0
+    p = dataclasses.replace(PRESETS["tiny"], D=128, Hq=8, Hkv=2, B=6, k=k, ctx=("uniform", 1, 600))
+    B, R = p.B, p.B * (k + 1)
+    a = make_attention_inputs(p, seed=31)
+    rows = make_new_rows(p, k, seed=31)
+    lm = make_lm_head_inputs(R, H, V, seed=31)
+    theta = 500000.0
+    # device pass: RoPE + append, attention, LM head
+    q = bf16_dev(rows["q"], device)
+    kc, vc = bf16_dev(a["k_cache"], device), bf16_dev(a["v_cache"], device)
+    bt, sl = dev(a["block_table"], device), dev(a["seq_lens"], device)
+    sv.rope_append(q, bf16_dev(rows["k_new"], device), bf16_dev(rows["v_new"], device), kc, vc, bt, sl, theta)
+    attn = torch.empty_like(q)
+    sv.verify_attn(q, kc, vc, bt, sl, attn, a["max_seq_len"], a["sm_scale"])
+    logits = torch.empty((B, k + 1, V), dtype=torch.float32, device=device)
+    sv.lm_head(bf16_dev(lm["hidden"], device), bf16_dev(lm["weight"], device), logits)
+    torch.cuda.synchronize()
+    target = logits.cpu().numpy()
+    # drafts drawn from the LM head's logits plus noise, as a drafter close to the target would
+    rng = np.random.Generator(np.random.PCG64(4242))
+    draft = np.ascontiguousarray(target[:, :k] + rng.standard_normal((B, k, V), dtype=np.float32))
+    tokens = draft_from_logits(rng, draft, T).astype(np.int32)
+    seq_ids = (np.arange(B, dtype=np.int64) * 7919 + 17).astype(np.int64)
+    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+    num_acc = torch.empty(B, dtype=torch.int32, device=device)
+    out_probs = torch.empty((B, k + 1), dtype=torch.float32, device=device)
+    acc_probs = torch.empty((B, k), dtype=torch.float32, device=device)
+    tally = Tally()
+    wq, wk, wv = oup.rope_append(rows["q"], rows["k_new"], rows["v_new"], a["k_cache"], a["v_cache"],
+                                 a["block_table"], a["seq_lens"], theta)
+    want_attn = oatt.verify_attention(wq, wk, wv, a["block_table"], a["seq_lens"], k, p.Hq, p.Hkv, p.block_size,
+                                      a["sm_scale"])
+    attn_err = np.abs(attn.float().cpu().numpy().astype(np.float64) - want_attn).max()
+    want_logits = oup.lm_head(lm["hidden"], lm["weight"]).reshape(B, k + 1, V)
+    bound = oup.lm_head_error_bound(lm["hidden"], lm["weight"]).reshape(B, k + 1, V)
+    assert attn_err <= ATTN_TOL
+    assert np.all(np.abs(target.astype(np.float64) - want_logits) <= bound)
+    cap = a["max_blocks"] * p.block_size
+    for seed in range(40):
+        sl.copy_(torch.from_numpy(a["seq_lens"]))
+        sv.reject_sample(logits, dev(draft, device), dev(tokens, device), dev(seq_ids, device), sl, T, seed,
+                         out_tokens, num_acc, out_probs, acc_probs)
+        sv.commit_lengths(sl, num_acc, k, cap)
+        torch.cuda.synchronize()
+        got = dict(out_tokens=out_tokens.cpu().numpy(), num_accepted=num_acc.cpu().numpy(),
+                   out_probs=out_probs.cpu().numpy().astype(np.float64),
+                   accept_probs=acc_probs.cpu().numpy().astype(np.float64))
+        want = orej.verify_batch(target, draft, tokens, seq_ids, a["seq_lens"], k, T, seed)
+        compare_reject(got, want, tally, k)
+        new_len, _ = ocommit.commit_lengths(a["seq_lens"], got["num_accepted"], cap)
+        np.testing.assert_array_equal(sl.cpu().numpy(), new_len)
+    say(f"[fused pass] attention err {attn_err:.2e}; sampler {tally.summary()}")
+    assert tally.ok(), tally.summary()
