@@ -57,13 +57,16 @@ HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 10
 METRIC = "verified tokens/s + HBM GB/s (% of peak) for spec verify, 8B shape, k=3"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_counters.txt")
+LM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "lm_head_8b_counters.txt")
 KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/attention.hip",
                   "speculative_decoding_verification_14_amd/csrc/common.hpp"]
+LM_KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/upstream.hip",
+                     "speculative_decoding_verification_14_amd/csrc/common.hpp"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -88,17 +91,19 @@ def algorithmic_bytes(preset, seq_lens, num_accepted, draft_lens=None):
     return attn, reject, commit
 
 
-def stored_traffic():
-    """HBM bytes per verify-attention call from committed rocprofv3 counter runs, if still valid."""
-    if not os.path.exists(COUNTERS_FILE):
+def stored_traffic(path=None, sources=None):
+    """HBM bytes per call of the dominant kernel from committed rocprofv3 counter runs, if still
+    valid (the file records a hash of the kernel's sources)."""
+    path = COUNTERS_FILE if path is None else path
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 key, _, v = line.partition(":")
                 vals[key.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return int(float(vals["hbm_bytes_per_call"]))
@@ -224,10 +229,11 @@ def _counter_means(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
-def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, write_cmd: str) -> None:
+def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, write_cmd: str,
+                   kind: str = "attn") -> None:
     """Per-call HBM bytes of the verify attention (and, for reference, the reject
-    kernel) from FETCH_SIZE / WRITE_SIZE runs, each scaled by what the same counter
-    reads for the calibration kernel of known traffic."""
+    kernel), or with kind "lm" of the LM head, from FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by what the same counter reads for the calibration kernel of known traffic."""
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
     calib = lambda d: [v for k, v in d.items() if "neg" in k.lower()]
@@ -236,25 +242,49 @@ def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, wri
         raise RuntimeError("calibration kernel not found in the counter runs (run them with --copy-calibration)")
     f_scale = CALIB_BYTES / (max(cf) * 1024.0)   # counters are in KiB per dispatch
     w_scale = CALIB_BYTES / (max(cw) * 1024.0)
-    attn = sorted(k for k in set(fetch) | set(write) if k.startswith("attn_"))
-    rej = sorted(k for k in set(fetch) | set(write) if k.startswith("reject_"))
     per_call = lambda ks: sum(fetch.get(k, 0.0) * 1024.0 * f_scale + write.get(k, 0.0) * 1024.0 * w_scale for k in ks)
-    lines = ["# rocprofv3 hardware counters, 8b workload (B=64, k=3, V=128256), one call of each kernel per step",
-             f"# fetch command: {fetch_cmd}", f"# write command: {write_cmd}",
-             "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by the factor that maps the",
-             "# calibration kernel (fp32 negation: 512 MiB read, 512 MiB written) onto its known traffic.",
-             f"kernel_source_sha256_16: {kernel_source_hash()}",
-             f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}"]
-    for k in attn + rej:
-        lines.append(f"{k}: FETCH_SIZE {fetch.get(k, 0.0):.1f} KiB, WRITE_SIZE {write.get(k, 0.0):.1f} KiB per dispatch")
-    lines.append(f"hbm_bytes_per_call: {per_call(attn):.0f}")
-    lines.append(f"reject_hbm_bytes_per_call: {per_call(rej):.0f}")
+    head = ["# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by the factor that maps the",
+            "# calibration kernel (fp32 negation: 512 MiB read, 512 MiB written) onto its known traffic."]
+    if kind == "lm":
+        lm = sorted(k for k in set(fetch) | set(write) if k.startswith("lm_head"))
+        lines = ["# rocprofv3 hardware counters, LM head of the 8b fused pass (R=256, H=4096, V=128256)",
+                 f"# fetch command: {fetch_cmd}", f"# write command: {write_cmd}", *head,
+                 f"kernel_source_sha256_16: {kernel_source_hash(LM_KERNEL_SOURCES)}",
+                 f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}"]
+        for k in lm:
+            lines.append(f"{k}: FETCH_SIZE {fetch.get(k, 0.0):.1f} KiB, WRITE_SIZE {write.get(k, 0.0):.1f} KiB "
+                         "per dispatch")
+        lines.append(f"hbm_bytes_per_call: {per_call(lm):.0f}")
+    else:
+        attn = sorted(k for k in set(fetch) | set(write) if k.startswith("attn_"))
+        rej = sorted(k for k in set(fetch) | set(write) if k.startswith("reject_"))
+        lines = ["# rocprofv3 hardware counters, 8b workload (B=64, k=3, V=128256), one call of each kernel per step",
+                 f"# fetch command: {fetch_cmd}", f"# write command: {write_cmd}", *head,
+                 f"kernel_source_sha256_16: {kernel_source_hash()}",
+                 f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}"]
+        for k in attn + rej:
+            lines.append(f"{k}: FETCH_SIZE {fetch.get(k, 0.0):.1f} KiB, WRITE_SIZE {write.get(k, 0.0):.1f} KiB "
+                         "per dispatch")
+        lines.append(f"hbm_bytes_per_call: {per_call(attn):.0f}")
+        lines.append(f"reject_hbm_bytes_per_call: {per_call(rej):.0f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
 # ----------------------------------------------------------------------------- GPU benchmark
+
+def copy_calibration(dev) -> dict:
+    """An elementwise kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 27   # 128 Mi fp32 = 512 MiB read + 512 MiB written by one elementwise kernel
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return dict(kernel="elementwise neg (fp32)", bytes_read=4 * n, bytes_written=4 * n, calls=3)
+
 
 def cold_cache_calls(step, dev, n: int) -> dict | None:
     """Per-call HIP-event times over n steps, each preceded by a 512 MiB write that
@@ -468,6 +498,8 @@ def gpu_bench_fused(args, p, dev) -> dict:
     step_s = wall / args.steps
     gbs = lambda by, sec: by / sec / 1e9
     lm_gbs, lm_tf = gbs(lm_bytes, call_s[2]), lm_flops / call_s[2] / 1e12
+    if args.copy_calibration:
+        copy_calibration(dev)
     return dict(
         metric=METRIC, value=tokens / step_s, unit="verified tokens/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=step_s * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
@@ -478,7 +510,8 @@ def gpu_bench_fused(args, p, dev) -> dict:
                               "sampling, commit"),
                     global_batch=B, k=k, parallelism="none (1 GPU)"),
         roofline=dict(bound="hbm", achieved=lm_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=lm_gbs / HBM_PEAK_GBS,
-                      traffic=None, kernel="spec_lm_head (lm_head_kernel)", algorithmic_bytes_per_call=lm_bytes,
+                      traffic=stored_traffic(LM_COUNTERS_FILE, LM_KERNEL_SOURCES),
+                      kernel="spec_lm_head (lm_head_kernel)", algorithmic_bytes_per_call=lm_bytes,
                       avg_call_us=call_s[2] * 1e6,
                       mfma=dict(achieved=lm_tf, peak=2500.0, unit="TFLOP/s", frac=lm_tf / 2500.0)),
         verified_tokens_per_step=tokens,
@@ -713,15 +746,7 @@ def gpu_bench(args) -> dict:
         raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
     cold = cold_cache_calls(step, dev, args.cold_steps)
 
-    copy_info = None
-    if args.copy_calibration:
-        n = 1 << 27   # 128 Mi fp32 = 512 MiB read + 512 MiB written by one elementwise kernel
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        copy_info = dict(kernel="elementwise neg (fp32)", bytes_read=4 * n, bytes_written=4 * n, calls=3)
+    copy_info = copy_calibration(dev) if args.copy_calibration else None
 
     tokens = int(np.sum(acc + 1))
     a_bytes, r_bytes, c_bytes = algorithmic_bytes(p, np.asarray(seq_lens0.cpu()), acc)
@@ -788,6 +813,7 @@ def main():
     ap.add_argument("--out", metavar="FILE")
     ap.add_argument("--command", default="", help="command line recorded in a rocprof summary")
     ap.add_argument("--write-counters", action="store_true")
+    ap.add_argument("--counters-kind", choices=["attn", "lm"], default="attn")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--fetch-command", default="")
@@ -795,8 +821,9 @@ def main():
     args = ap.parse_args()
 
     if args.write_counters:
-        write_counters(args.fetch_dir, args.write_dir, args.out or COUNTERS_FILE, args.fetch_command,
-                       args.write_command)
+        write_counters(args.fetch_dir, args.write_dir,
+                       args.out or (LM_COUNTERS_FILE if args.counters_kind == "lm" else COUNTERS_FILE),
+                       args.fetch_command, args.write_command, args.counters_kind)
         return
 
     if args.summarize_rocprof:

@@ -83,19 +83,20 @@ def children(parents, v: int) -> list:
 
 
 def verify_attention_tree(q, k_cache, v_cache, block_table, seq_lens, parents, Hq: int, Hkv: int,
-                          block_size: int, sm_scale: float) -> np.ndarray:
-    """fp64 output [B][N+1][Hq][D]: node n attends keys 0..L-1 and the slots of its ancestors (T2)."""
+                          block_size: int, sm_scale: float, pairs=None) -> np.ndarray:
+    """fp64 output [B][N+1][Hq][D]: node n attends keys 0..L-1 and the slots of its ancestors (T2).
+    ``pairs`` restricts the work to a list of (b, kv_head); other rows are left as NaN."""
     B, N1, _, D = q.shape
     G = Hq // Hkv
-    out = np.empty((B, N1, Hq, D), dtype=np.float64)
-    for b in range(B):
+    out = np.full((B, N1, Hq, D), np.nan, dtype=np.float64)
+    todo = pairs if pairs is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in todo:
         L = int(seq_lens[b])
-        for g in range(Hkv):
-            K, Vv = gather_sequence_kv(k_cache, v_cache, block_table, b, g, L + N1, block_size)
-            for n in range(N1):
-                keys = list(range(L)) + [L + m for m in ancestors_or_self(parents[b], n)]
-                for h in range(g * G, (g + 1) * G):
-                    out[b, n, h] = attend(bf16_to_f64(q[b, n, h]), K[keys], Vv[keys], sm_scale)
+        K, Vv = gather_sequence_kv(k_cache, v_cache, block_table, b, g, L + N1, block_size)
+        for n in range(N1):
+            keys = list(range(L)) + [L + m for m in ancestors_or_self(parents[b], n)]
+            for h in range(g * G, (g + 1) * G):
+                out[b, n, h] = attend(bf16_to_f64(q[b, n, h]), K[keys], Vv[keys], sm_scale)
     return out
 
 
