@@ -228,11 +228,25 @@ __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) 
             const int c = c0 + u;
             const unsigned char* abase = s_a[c & 1] + (wm * MT * 16 + l16) * kAStride + 32 * lg;
             const WChunk& w = wr[u];
+            // A fragments read kPF row tiles ahead of their MFMAs (the order pinned), so the LDS
+            // latency overlaps the MFMAs of the tiles before
+            constexpr int kPF = 4;
+            uint4 af[kPF][2];
+#pragma unroll
+            for (int j = 0; j < kPF; ++j) {
+                const unsigned char* ap = abase + j * 16 * kAStride;
+                af[j][0] = *reinterpret_cast<const uint4*>(ap);
+                af[j][1] = *reinterpret_cast<const uint4*>(ap + 16);
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const unsigned char* ap = abase + mt * 16 * kAStride;
-                const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
+                const uint4 a0 = af[mt % kPF][0], a1 = af[mt % kPF][1];
+                if (mt + kPF < MT) {
+                    const unsigned char* ap = abase + (mt + kPF) * 16 * kAStride;
+                    af[mt % kPF][0] = *reinterpret_cast<const uint4*>(ap);
+                    af[mt % kPF][1] = *reinterpret_cast<const uint4*>(ap + 16);
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(w.w[t][0]),
@@ -240,9 +254,8 @@ __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) 
                     acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(w.w[t][1]),
                                                                         acc[mt][t], 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // keep the next loads and the LDS store (with its wait) after the MFMAs
-            __builtin_amdgcn_sched_barrier(0);
             load_a(ar[u], min(c + kRing, chunks - 1));
             load_w(wr[u], min(c + kRing, chunks - 1));
             store_a(ar[(u + 1) % kRing], (c + 1) & 1);   // after the last chunk: a copy nobody reads
