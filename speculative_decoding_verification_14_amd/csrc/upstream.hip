@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeArgs a) {
 // the row's 128-byte line; the NWM waves that share columns read the same lines, the
 // later ones from the cache.
 
-constexpr int kGemmM = 256;                    // rows per M block
+constexpr int kGemmM = 256;                    // rows per M block, at most
 constexpr int kGemmKC = 64;                    // K chunk
 constexpr int kAStride = kGemmKC * 2 + 16;     // LDS bytes per staged row (padded)
 // Loads of chunk j are issued RING chunks before the chunk that uses them, hidden
@@ -152,24 +152,25 @@ struct GemmArgs {
     int R, H, V;
 };
 
-template <int NWM, int NWN, int NT, int RING>
+template <int NWM, int NWN, int NT, int RING, int MB>
 __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) {
     constexpr int kRing = RING;
+    static_assert(MB == 64 || MB == 128 || MB == 256, "M block: 64, 128 or 256 rows");
     constexpr int kThreads = NWM * NWN * kWave;
-    constexpr int MT = 16 / NWM;                          // row tiles per wave
+    constexpr int MT = MB / 16 / NWM;                     // row tiles per wave
     constexpr int kCols = NWN * 16 * NT;                  // columns per workgroup
-    constexpr int AQ = kGemmM * kGemmKC * 2 / 16 / kThreads;   // 16-byte pieces of the hidden chunk per thread
+    constexpr int AQ = MB * kGemmKC * 2 / 16 / kThreads;   // 16-byte pieces of the hidden chunk per thread
     constexpr int kPartsPerRow = 8 / AQ;                  // threads per 128-byte chunk row
-    static_assert(AQ * kPartsPerRow == 8 && MT * NWM == 16, "tile shape");
+    static_assert(AQ >= 1 && AQ * kPartsPerRow == 8 && MT * NWM * 16 == MB, "tile shape");
     struct WChunk { uint4 w[NT][2]; };
     struct AChunk { uint4 v[AQ]; };
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][kGemmM * kAStride];
+    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][MB * kAStride];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / NWN, wn = wave % NWN;
     const int l16 = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * kCols + wn * 16 * NT;
-    const int m0 = blockIdx.y * kGemmM;
+    const int m0 = blockIdx.y * MB;
     const int chunks = a.H / kGemmKC;
 
     // this lane's W rows (clamped into range: columns >= V are computed, never stored)
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) 
             const WChunk& w = wr[u];
             // A fragments read kPF row tiles ahead of their MFMAs (the order pinned), so the LDS
             // latency overlaps the MFMAs of the tiles before
-            constexpr int kPF = 4;
+            constexpr int kPF = MT < 4 ? MT : 4;
             uint4 af[kPF][2];
 #pragma unroll
             for (int j = 0; j < kPF; ++j) {
@@ -315,10 +316,17 @@ hipError_t launch_lm_head(const LmHeadLaunch& p, hipStream_t stream) {
     a.R = p.R;
     a.H = p.H;
     a.V = p.V;
-    // one row of 8 waves, two 16-column tiles each (256 columns per workgroup), rings of two
+    // one row of 8 waves, two 16-column tiles each (256 columns per workgroup), rings of two; the
+    // M block is the smallest of 64, 128 and 256 rows that holds R (256-row blocks beyond that)
     constexpr int WM = 1, WN = 8, NT = 2, RING = kLmRing;
-    const dim3 grid((p.V + WN * 16 * NT - 1) / (WN * 16 * NT), (p.R + kGemmM - 1) / kGemmM);
-    hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING>), grid, dim3(WM * WN * kWave), 0, stream, a);
+    const int gx = (p.V + WN * 16 * NT - 1) / (WN * 16 * NT);
+    if (p.R <= 64)
+        hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING, 64>), dim3(gx, 1), dim3(WM * WN * kWave), 0, stream, a);
+    else if (p.R <= 128)
+        hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING, 128>), dim3(gx, 1), dim3(WM * WN * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING, kGemmM>), dim3(gx, (p.R + kGemmM - 1) / kGemmM),
+                           dim3(WM * WN * kWave), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ def _lm_gpu(x, device):
 
 
 @pytest.mark.parametrize("R,H,V", [(1, 256, 1), (5, 256, 1000), (37, 256, 4097), (256, 512, 16384), (300, 768, 777),
-                                   (513, 256, 300), (64, 1024, 2049)])
+                                   (513, 256, 300), (64, 1024, 2049), (100, 512, 5000), (128, 256, 257)])
 def test_lm_head_shapes(device, R, H, V):
     x = make_lm_head_inputs(R, H, V, seed=R + V)
     got = _lm_gpu(x, device)
