@@ -1370,6 +1370,20 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
     auto slot = [&](int e) { return slots0 + size_t(e) * kSampSlots * a.Q; };
     int ex = 0, v = 0, depth = 0;
     unsigned tested = 0u;
+    // A broken tree ends the sequence with num_accepted = -1. A failure before the group's first
+    // exchange must still count the group when this is its last sequence, or the call's epoch
+    // would never be stored (every workgroup of the group fails alike, so none exchanges after).
+    auto fail = [&]() {
+        flag_error(a, s);
+        if (s.wave == 0 && s.b + a.groups >= a.B) count_group(a, s, counted);   // wave 0 counts, as after a gather
+    };
+    for (int n = 1; n <= N; ++n) {   // every parent precedes its node
+        const int par = load_uniform(a.parents, b * N + n - 1);
+        if (par < 0 || par >= n) {
+            fail();
+            return;
+        }
+    }
     for (;;) {
         // children of v in index order, four bits each (scalar loads of the parents)
         unsigned chp = 0u;
@@ -1381,7 +1395,7 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
             }
         }
         if (m > kMaxBranch || ex + 4 + m > kTreeEx) {   // outside the documented shapes
-            flag_error(a, s);
+            fail();
             return;
         }
         const float* prow = tbase + size_t(v) * a.V;

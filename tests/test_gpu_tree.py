@@ -287,3 +287,30 @@ def test_tree_commit_then_causal_attention_is_the_tree_rows(device):
             r += 1
     say(f"[tree commit + attention] {r} path rows, max err {worst:.2e}")
     assert worst <= ATTN_TOL
+
+
+def test_tree_reject_broken_trees_then_a_valid_call(device):
+    """A node with five children and a parent index out of range end their sequences with -1 (the
+    failure comes before any exchange); the valid trees in the same call match the oracle, and a
+    following call on the same workspace with other logits still matches it (the failing call stored
+    its epoch, so no slot of it is taken for one of the next call)."""
+    good = [random_parents(np.random.default_rng(5), 6), np.arange(6, dtype=np.int32)]
+    wide = np.array([0, 0, 0, 0, 0, 1], dtype=np.int32)
+    out_of_range = np.array([0, 5, 1, 2, 3, 4], dtype=np.int32)
+    parents = np.stack([good[0], wide, out_of_range, good[1]])
+    inp = make_tree_reject_inputs(PRESETS["tiny"], parents, B=4)     # one workgroup per sequence
+    g = TreeDevice(inp, device).call(inp["seed"])
+    np.testing.assert_array_equal(g["num_accepted"][[1, 2]], [-1, -1])
+    sub = {k: inp[k][[0, 3]] for k in ("target_logits", "draft_logits", "draft_tokens", "parents", "seq_ids",
+                                       "seq_lens")}
+    o = otree.verify_batch_tree(sub["target_logits"], sub["draft_logits"], sub["draft_tokens"], sub["parents"],
+                                sub["seq_ids"], sub["seq_lens"], inp["temperature"], inp["seed"])
+    tally = Tally()
+    _compare_tree({k: v[[0, 3]] for k, v in g.items()}, o, tally)
+    inp2 = make_tree_reject_inputs(PRESETS["tiny"], np.stack([good[0], good[1], good[0], good[1]]), seed=77, B=4)
+    g2 = TreeDevice(inp2, device).call(inp2["seed"] + 1)
+    o2 = otree.verify_batch_tree(inp2["target_logits"], inp2["draft_logits"], inp2["draft_tokens"], inp2["parents"],
+                                 inp2["seq_ids"], inp2["seq_lens"], inp2["temperature"], inp2["seed"] + 1)
+    _compare_tree(g2, o2, tally)
+    say(f"[tree reject] broken trees, then a valid call: {tally.summary()}")
+    assert not tally.bad and tally.mismatches == 0, tally.summary()
