@@ -232,7 +232,10 @@ spec_status spec_reject_sample_ragged(const float* target_logits, const float* d
  * the caller has appended the KV rows of nodes 0 .. N at cache slots
  * L_b .. L_b + N), except that node n attends the committed keys 0 .. L_b - 1 and
  * the slots L_b + m of its ancestors m and itself (the tree mask). Workspace:
- * spec_verify_attn_workspace_size(B, N, ...). 1 <= N <= 15.
+ * spec_verify_attn_workspace_size(B, N, ...). 1 <= N <= 15. Parents are a
+ * device-side precondition: an index outside [0, n) is read as the nearest one
+ * inside (so every read stays within the sequence's slots), while
+ * spec_reject_sample_tree reports such a tree with num_accepted = -1.
  *
  * spec_reject_sample_tree: the walk. At node v (from the root) with children
  * c_1 .. c_m: r = p_v; for i = 1 .. m accept c_i's token x iff u_i < r(x)/q_v(x)
