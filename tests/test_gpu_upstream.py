@@ -61,9 +61,9 @@ def _check_rope(a, rows, theta, parents, device, label):
     assert n_off <= 1e-4 * (dq.size + dk.size)
 
 
-@pytest.mark.parametrize("D,bs,tree", [(64, 16, False), (128, 32, False), (128, 16, True), (64, 64, True)])
-def test_rope_append_small(device, D, bs, tree):
-    k = 6
+@pytest.mark.parametrize("D,bs,tree,k", [(64, 16, False, 6), (128, 32, False, 6), (128, 16, True, 6),
+                                         (64, 64, True, 6), (128, 16, False, 0), (64, 32, True, 1)])
+def test_rope_append_small(device, D, bs, tree, k):
     p = dataclasses.replace(PRESETS["tiny"], D=D, Hq=8, Hkv=2, block_size=bs, k=k, ctx=("uniform", 0, 900))
     a = make_attention_inputs(p, seed=D + bs)
     rows = make_new_rows(p, k, seed=D + bs)
@@ -71,7 +71,7 @@ def test_rope_append_small(device, D, bs, tree):
     if tree:
         rng = np.random.Generator(np.random.PCG64(77 + D))
         parents = np.stack([random_parents(rng, k) for _ in range(p.B)])
-    _check_rope(a, rows, 500000.0, parents, device, f"D{D} bs{bs} tree={tree}")
+    _check_rope(a, rows, 500000.0, parents, device, f"D{D} bs{bs} tree={tree} k={k}")
 
 
 def test_rope_append_long_positions(device):
@@ -129,7 +129,8 @@ def _lm_gpu(x, device):
 
 
 @pytest.mark.parametrize("R,H,V", [(1, 256, 1), (5, 256, 1000), (37, 256, 4097), (256, 512, 16384), (300, 768, 777),
-                                   (513, 256, 300), (64, 1024, 2049), (100, 512, 5000), (128, 256, 257)])
+                                   (513, 256, 300), (64, 1024, 2049), (100, 512, 5000), (128, 256, 257),
+                                   (3, 128, 50), (200, 128, 999)])
 def test_lm_head_shapes(device, R, H, V):
     x = make_lm_head_inputs(R, H, V, seed=R + V)
     got = _lm_gpu(x, device)
