@@ -91,6 +91,15 @@ def algorithmic_bytes(preset, seq_lens, num_accepted, draft_lens=None):
     return attn, reject, commit
 
 
+def dense_reject_figure(preset, seconds: float) -> dict:
+    """Context only: the rate the sampling call would show if every logits row were read,
+    all k + 1 target rows and all k draft rows (B * (2k + 1) * V * 4 bytes), whatever the
+    acceptance outcome. The call reads only the rows its chain examines."""
+    dense = preset.B * (2 * preset.k + 1) * preset.V * 4
+    gbs = dense / seconds / 1e9
+    return dict(bytes=dense, gbs=gbs, frac_of_peak=gbs / HBM_PEAK_GBS)
+
+
 def stored_traffic(path=None, sources=None):
     """HBM bytes per call of the dominant kernel from committed rocprofv3 counter runs, if still
     valid (the file records a hash of the kernel's sources)."""
@@ -267,6 +276,55 @@ def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, wri
                          "per dispatch")
         lines.append(f"hbm_bytes_per_call: {per_call(attn):.0f}")
         lines.append(f"reject_hbm_bytes_per_call: {per_call(rej):.0f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+MFMA_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_mfma_counters.txt")
+MFMA_PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA peak of the chip
+SIMDS = 256 * 4
+
+
+def attention_flops(preset, seq_lens, draft_lens=None) -> int:
+    """Algorithmic attention flops: 2*D for q.k and 2*D for p.v per (query row, visible key)."""
+    import numpy as np
+    L = np.asarray(seq_lens, dtype=np.int64)
+    k = np.full(L.shape, preset.k, dtype=np.int64) if draft_lens is None else np.asarray(draft_lens, np.int64)
+    # row i of sequence b sees L_b + i + 1 keys
+    keys = np.sum((k + 1) * L + (k + 1) * (k + 2) // 2)
+    return int(4 * preset.D * preset.Hq * keys)
+
+
+def write_mfma(pmc_dir: str, out: str, command: str) -> None:
+    """MFMA use of the verify attention from one rocprofv3 run with the MFMA counters and a
+    kernel trace: bf16 matrix flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of
+    512 flops), their rate over the traced duration, and the matrix pipes' busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES, summed over the 1024 SIMDs, over SIMDs x traced cycles at 2.4 GHz)."""
+    mops = _counter_means(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy = _counter_means(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    stats = sorted(glob.glob(os.path.join(pmc_dir, "**", "*kernel_stats.csv"), recursive=True))
+    dur = {}
+    for st in stats:
+        with open(st) as f:
+            for row in csv.DictReader(f):
+                dur[_kernel_label(row["Name"])] = float(row["AverageNs"]) * 1e-9
+    lines = ["# rocprofv3 MFMA counters, verify attention of the 8b workload (B=64, k=3, Hq=32, Hkv=8, D=128)",
+             f"# command: {command}",
+             "# flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 per dispatch; rate over the average traced duration",
+             "# of the same run (kernels are serialised while counters are read, so the duration can be longer",
+             "# than in an unprofiled run); busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * duration * 2.4 GHz)",
+             f"kernel_source_sha256_16: {kernel_source_hash()}",
+             f"mfma_peak_bf16_tflops: {MFMA_PEAK_BF16_TFLOPS:.0f}"]
+    for kname in sorted(k for k in mops if k.startswith("attn_")):
+        flops = mops[kname] * 512.0
+        d = dur.get(kname)
+        rate = flops / d / 1e12 if d else float("nan")
+        b = busy.get(kname, float("nan"))
+        bfrac = b / (SIMDS * d * 2.4e9) if d else float("nan")
+        lines.append(f"{kname}: mfma_flops {flops:.4g} per dispatch, traced avg {d * 1e6 if d else float('nan'):.1f} us, "
+                     f"{rate:.1f} TFLOP/s = {rate / MFMA_PEAK_BF16_TFLOPS:.4f} of bf16 peak, "
+                     f"MFMA busy cycles {b:.4g} ({bfrac:.4f} of SIMD cycles)")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -750,6 +808,7 @@ def gpu_bench(args) -> dict:
 
     tokens = int(np.sum(acc + 1))
     a_bytes, r_bytes, c_bytes = algorithmic_bytes(p, np.asarray(seq_lens0.cpu()), acc)
+    a_flops = attention_flops(p, np.asarray(seq_lens0.cpu()))
     mean = lambda v: sum(v) / len(v)
     med = lambda v: sorted(v)[len(v) // 2]
     attn_avg_s = mean(attn_ms) / 1e3
@@ -776,9 +835,12 @@ def gpu_bench(args) -> dict:
         step_gbs=(a_bytes + r_bytes + c_bytes) / step_s / 1e9,
         kernels=dict(
             verify_attn=dict(avg_us=attn_avg_s * 1e6, median_us=med(attn_ms) * 1e3, bytes=a_bytes, gbs=attn_gbs,
-                             frac_of_peak=attn_gbs / HBM_PEAK_GBS),
+                             frac_of_peak=attn_gbs / HBM_PEAK_GBS,
+                             mfma=dict(algorithmic_flops=a_flops, tflops=a_flops / attn_avg_s / 1e12,
+                                       frac_of_bf16_peak=a_flops / attn_avg_s / 1e12 / MFMA_PEAK_BF16_TFLOPS)),
             reject_sample=dict(avg_us=rej_avg_s * 1e6, median_us=med(rej_ms) * 1e3, bytes=r_bytes, gbs=rej_gbs,
-                               frac_of_peak=rej_gbs / HBM_PEAK_GBS),
+                               frac_of_peak=rej_gbs / HBM_PEAK_GBS,
+                               dense_equivalent=dense_reject_figure(p, rej_avg_s)),
             commit_lengths=dict(avg_us=com_avg_s * 1e6, bytes=c_bytes)),
         event_sum_ms_per_step=(attn_avg_s + rej_avg_s + com_avg_s) * 1e3,
         event_sampled_steps=len(evs),
@@ -813,12 +875,18 @@ def main():
     ap.add_argument("--out", metavar="FILE")
     ap.add_argument("--command", default="", help="command line recorded in a rocprof summary")
     ap.add_argument("--write-counters", action="store_true")
+    ap.add_argument("--write-mfma", metavar="PMC_DIR",
+                    help="write the attention's MFMA counter summary from a rocprofv3 run in PMC_DIR")
     ap.add_argument("--counters-kind", choices=["attn", "lm"], default="attn")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--fetch-command", default="")
     ap.add_argument("--write-command", default="")
     args = ap.parse_args()
+
+    if args.write_mfma:
+        write_mfma(args.write_mfma, args.out or MFMA_FILE, args.command)
+        return
 
     if args.write_counters:
         write_counters(args.fetch_dir, args.write_dir,

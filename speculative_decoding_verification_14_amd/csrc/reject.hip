@@ -1025,7 +1025,9 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
     c.Mp64 = Mu;
     c.Mq64 = 0.0;
     c.invT64 = a.invT64;
-    c.tp = heavy_threshold(Mu, Zu, a.T);
+    // A unit with no finite logit (all past V) has Z_u = 0: its threshold is +inf, so that
+    // no padding element is classified heavy (with -inf the test would read a NaN's sign).
+    c.tp = (Zu > 0.0) ? heavy_threshold(Mu, Zu, a.T) : INFINITY;
     c.tq = INFINITY;
     c.dn = 0.0f;
     const int lane = lane_id();
