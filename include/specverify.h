@@ -96,7 +96,7 @@ int32_t spec_abi_version(void);
  *  seq_lens     int32 [B]   committed length L_b (keys read: L_b + k + 1)
  *  out          bf16  [B][k+1][Hq][D]
  *
- * Shapes: B >= 1; 0 <= k <= 15; Hkv >= 1; Hq % Hkv == 0; D in {64, 128};
+ * Shapes: 1 <= B <= 65535; 0 <= k <= 15; Hkv >= 1; Hq % Hkv == 0; D in {64, 128};
  * block_size in {16, 32, 64}; max_blocks >= 1; num_blocks >= 1;
  * max_seq_len >= k + 1; sm_scale finite and > 0.
  * Device preconditions: L_b + k + 1 <= min(max_seq_len, max_blocks*block_size);
