@@ -10,17 +10,22 @@
 // after full acceptance sample p_k. Sampling is inverse CDF in ascending token id.
 //
 // How (one MI355X, one launch for the whole batch):
-//  * A row of V logits is cut into units of 4096; each unit of the current row
+//  * A row of V logits is cut into U units of 4096; each unit of the current row
 //    (pair) is held in the registers of one wavefront (16 x 16-byte loads per
-//    lane per row, all in flight together). Eight unit wavefronts form a
-//    512-thread workgroup (one per CU); the Q = ceil(U / 8) workgroups of a
-//    sequence form a group, and groups take sequences in turn.
+//    lane per row, all in flight together). W unit wavefronts form a workgroup:
+//    eight (one workgroup per CU) when the batch fills the device, four (a
+//    sequence over twice as many CUs, one workgroup on each) when B * ceil(U/4)
+//    workgroups fit one per CU, which shortens each step of a sequence's serial
+//    chain at small batches. The Q = ceil(U / W) workgroups of a sequence form a
+//    group, and groups take sequences in turn.
 //  * Level j: every wavefront reduces its units of p_j and q_j to (max, sum of
 //    exps) with an online softmax on the DPP network; wave 0 of the workgroup
-//    combines the eight through LDS and publishes the workgroup's pair; then it
-//    gathers the Q pairs of the group, combines them in a fixed order and takes
-//    the acceptance test. Every workgroup computes the same decision from the
-//    same published bits, so one cross-CU exchange per level suffices.
+//    combines them four at a time (quads of consecutive units) and publishes one
+//    entry per quad; then it gathers the ceil(U / 4) quads of the sequence,
+//    combines them in quad order and takes the acceptance test. Every workgroup
+//    computes the same decision from the same published bits, so one cross-CU
+//    exchange per level suffices; and as the quads are the same for W = 4 and
+//    W = 8, so are all results: a sequence's outputs do not depend on the batch.
 //  * Exchange is fence-free: each published 32-bit value travels in a 64-bit
 //    atomic slot together with the call's epoch, so a slot is either stale (old
 //    epoch, keep polling) or complete. No cache write-back or invalidation is
@@ -28,9 +33,9 @@
 //  * On the first rejection (or after k acceptances, on row p_k) the rows still
 //    in registers are turned into sampling weights: nothing is read twice. Unit
 //    sums go through LDS to the workgroup leader, one exchange gives every
-//    leader the workgroup totals, the leaders find the crossing workgroup, and
-//    that workgroup's leader finds the crossing unit, whose wavefront scans its
-//    per-load sums in LDS for the token.
+//    leader the quad totals, the leaders find the crossing quad, and the leader
+//    of the workgroup holding it finds the crossing unit, whose wavefront scans
+//    its per-load sums in LDS for the token.
 //  * Precision: the chain statistics use fp32 exps (relative error ~1e-7, ample
 //    for an acceptance test). The sampling pass takes logits whose probability
 //    exceeds 2^-14 in fp64 and the rest with an error-compensated fp32 exp,
@@ -51,9 +56,9 @@ constexpr int kUnit = kWave * kVecs * 4;   // 4096 logits: one wavefront's share
 constexpr int kStep = 4;                   // loads per online-softmax step (16 logits per lane)
 constexpr int kStatSlots = 6;              // M_p, M_q, Z_p (hi, lo), Z_q (hi, lo)
 constexpr int kSampSlots = 8;              // A, B, P, Q (hi, lo each); bonus row: weight sum, max
-constexpr int kUnitWaves = 8;              // unit wavefronts per workgroup
+constexpr int kUnitWaves = 8;              // unit wavefronts per workgroup (the tree walk; the chain: 8 or 4)
 constexpr int kRT = kUnitWaves * kWave;    // 512 threads
-constexpr int kMaxQ = 32;                  // workgroups per sequence: U <= 256, i.e. V <= 2^20
+constexpr int kMaxQ = 64;                  // workgroups per sequence: U <= 256 (V <= 2^20), four units each
 constexpr int kMaxBranch = 4;              // tree: children per node
 constexpr int kTreeEx = 24;                // tree: exchanges per sequence (levels, passes, the draw)
 constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this probability share use fp64
@@ -75,11 +80,11 @@ struct RejectArgs {
     float* out_probs;
     float* accept_probs;
     unsigned* ctl;                     // epoch of the last finished call, finished-wave count, error flag
-    unsigned long long* stat_slots;    // [B][k+1][kStatSlots][Q]: workgroup statistics per level
-    unsigned long long* samp_slots;    // [B][kSampSlots][Q]: workgroup sampling sums
+    unsigned long long* stat_slots;    // [B][k+1][kStatSlots][U]: unit statistics per level
+    unsigned long long* samp_slots;    // [B][kSampSlots][U]: unit sampling sums
     const int32_t* parents;            // tree: [B][k] parent of node n at [n-1]; null for a chain
     int32_t* out_nodes;                // tree: [B][k] accepted node indices, or null
-    unsigned long long* tree_slots;    // tree: [B][kTreeEx][kSampSlots][Q], one block per exchange
+    unsigned long long* tree_slots;    // tree: [B][kTreeEx][kSampSlots][U], one block per exchange
     int B, k, V, U, Q, groups;
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
@@ -94,12 +99,12 @@ struct RejectLayout {
     size_t ctl, stat, samp, total;
 };
 
-RejectLayout reject_layout(int B, int k, int Q) {
+RejectLayout reject_layout(int B, int k, int U) {
     RejectLayout L;
     size_t o = 0;
     L.ctl = o;  o = align256(o + 4 * sizeof(unsigned));
-    L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * Q * kStatSlots);
-    L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * Q * kSampSlots);
+    L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * U * kStatSlots);
+    L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * kSampSlots);
     L.total = o;
     return L;
 }
@@ -142,15 +147,16 @@ __device__ __forceinline__ void publish(unsigned long long* slots, const unsigne
 // words. Returns false if the bounded wait ran out (only possible if the group
 // were not resident at once).
 template <int N>
-__device__ __forceinline__ bool gather(unsigned long long* slots, int Q, unsigned epoch, unsigned (&out)[N]) {
+__device__ __forceinline__ bool gather_at(unsigned long long* slots, int stride, int first, int count, unsigned epoch,
+                                          unsigned (&out)[N]) {
     const int lane = lane_id();
     for (unsigned it = 0; it < kSpinLimit; ++it) {
         bool ok = true;
 #pragma unroll
         for (int s = 0; s < N; ++s) {
             unsigned long long v = 0;
-            if (lane < Q) {
-                v = slot_load(slots + size_t(s) * Q + lane);
+            if (lane < count) {
+                v = slot_load(slots + size_t(s) * stride + first + lane);
                 ok = ok && static_cast<unsigned>(v) == epoch;
             }
             out[s] = static_cast<unsigned>(v >> 32);
@@ -159,6 +165,55 @@ __device__ __forceinline__ bool gather(unsigned long long* slots, int Q, unsigne
         __builtin_amdgcn_s_sleep(4);
     }
     return false;
+}
+
+template <int N>
+__device__ __forceinline__ bool gather(unsigned long long* slots, int Q, unsigned epoch, unsigned (&out)[N]) {
+    return gather_at<N>(slots, Q, 0, Q, epoch, out);
+}
+
+// The first two steps of the DPP wavefront reductions (dpp_wave_max / dpp_wave_sum) alone: every lane ends with the
+// maximum / sum of its group of four lanes (lanes 4j .. 4j+3), with the same bits as
+// the full reduction gives when all other lanes hold the identity.
+__device__ __forceinline__ float dpp_quad_max(float v) {
+    const int id = __builtin_bit_cast(int, -INFINITY);
+    v = fmaxf(v, __builtin_bit_cast(float, dpp_move<0xB1>(__builtin_bit_cast(int, v), id)));
+    v = fmaxf(v, __builtin_bit_cast(float, dpp_move<0x4E>(__builtin_bit_cast(int, v), id)));
+    return v;
+}
+
+__device__ __forceinline__ double dpp_quad_sum(double v) {
+    v += dpp_move_f64<0xB1>(v);
+    v += dpp_move_f64<0x4E>(v);
+    return v;
+}
+
+// Exchanges go through quads: four consecutive units, combined in lanes 0..3 of the
+// workgroup's wave 0 and published as one entry. A workgroup of W unit wavefronts
+// holds W / 4 quads, and a sequence's nq = ceil(U / 4) quads are combined in quad
+// order, so every result is the same whatever W is.
+constexpr int kQuad = 4;
+
+__device__ __forceinline__ int quads_of(int U) { return (U + kQuad - 1) / kQuad; }
+
+// combine_pair over each group of four lanes: lane 4j .. 4j+3 end with the (M, Z) of
+// the units in those lanes (the same bits as combine_pair over them alone).
+__device__ __forceinline__ void combine_quad(float m, double z, double invT64, float& M, double& Z) {
+    M = dpp_quad_max(m);
+    Z = dpp_quad_sum((z > 0.0) ? z * exp_nonpos_f64((static_cast<double>(m) - M) * invT64) : 0.0);
+}
+
+// Lane 4j of wave 0 publishes quad j of its workgroup (quad index q * W/4 + j of the
+// sequence, when below nq): payload s to slots[s * nq + quad].
+template <int N>
+__device__ __forceinline__ void publish_quads(unsigned long long* slots, const unsigned (&payload)[N], unsigned epoch,
+                                              int q, int W, int nq) {
+    const int lane = lane_id();
+    const int qd = q * (W / kQuad) + lane / kQuad;
+    if ((lane & (kQuad - 1)) == 0 && lane < W && qd < nq) {
+#pragma unroll
+        for (int s = 0; s < N; ++s) slot_store(slots + size_t(s) * nq + qd, payload[s], epoch);
+    }
 }
 
 // Values that are equal in every lane (read by all lanes from one address, or
@@ -530,7 +585,7 @@ struct SeqCtx {
     int b;
     int kb;                   // drafts of this sequence
     size_t tb, db;            // its first target (and output) row, its first draft row
-    int u;                    // unit of this wavefront: q * kUnitWaves + wave
+    int u;                    // unit of this wavefront: q * (unit wavefronts per workgroup) + wave
     int q;                    // workgroup of the group
     int wave;                 // wavefront of the workgroup
     unsigned epoch;
@@ -564,13 +619,16 @@ struct SampRes {
     unsigned flags;    // kSampUseP, kSampExact, kSampError
     double run, t, Z1, Z2;
 };
-struct Shared {
-    LoadSums ls[kUnitWaves];
-    UnitStat unit[kUnitWaves];
-    double4 usum[kUnitWaves];
+template <int W>
+struct SharedT {
+    static constexpr int kW = W;   // unit wavefronts of the workgroup
+    LoadSums ls[W];
+    UnitStat unit[W];
+    double4 usum[W];
     LevelRes res;
     SampRes samp;
 };
+using Shared = SharedT<kUnitWaves>;
 
 enum : unsigned { kResAccepted = 1u, kResError = 2u };
 enum : unsigned { kSampUseP = 1u, kSampExact = 2u, kSampError = 4u };
@@ -754,7 +812,8 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
 
 // Reads wave 0's sampling decision and runs the final scan in the owning
 // wavefront (every wavefront of the workgroup calls this after the barrier).
-__device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, const Shared& sh, bool& use_p,
+template <typename SH>
+__device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, const SH& sh, bool& use_p,
                                           bool& exact, double& run, double& t, double& Z1, double& Z2) {
     const unsigned flags = static_cast<unsigned>(uniform(static_cast<int>(sh.samp.flags)));
     if (flags & kSampError) {
@@ -776,9 +835,9 @@ __device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, 
 // registers) into weights; wave 0 sums the workgroup's units, one exchange gives
 // it every workgroup's sums, it finds the crossing workgroup and, if that is its
 // own, the crossing unit, whose wavefront then scans it for the token.
-template <bool kVec4>
+template <bool kVec4, typename SH>
 __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s, int row, const f4 (&xp)[kVecs],
-                                           const f4 (&xq)[kVecs], const RowStats& st, Shared& sh) {
+                                           const f4 (&xq)[kVecs], const RowStats& st, SH& sh) {
     const float* prow = s.prow_base + size_t(row) * a.V;
     const float* qrow = s.qrow_base + size_t(row) * a.V;
     SampleCtx c;
@@ -794,24 +853,27 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
 
     const int lane = lane_id();
     const UnitSums us = unit_sums<kVec4, true>(xp, xq, c, prow, qrow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
+    unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
     if (lane == 0) sh.usum[s.wave] = make_double4(us.A, us.B, us.P, us.Q);
     __syncthreads();
     if (s.wave == 0) {
-        double Au = 0.0, Bu = 0.0, Pu = 0.0, Qu = 0.0;
-        if (lane < kUnitWaves) {
-            const double4 v = sh.usum[lane];
-            Au = v.x; Bu = v.y; Pu = v.z; Qu = v.w;
+        const int nq = quads_of(a.U);
+        {   // the workgroup's quads, all at once
+            double Au = 0.0, Bu = 0.0, Pu = 0.0, Qu = 0.0;
+            if (lane < SH::kW) {
+                const double4 v = sh.usum[lane];
+                Au = v.x; Bu = v.y; Pu = v.z; Qu = v.w;
+            }
+            const double Aw = dpp_quad_sum(Au), Bw = dpp_quad_sum(Bu), Pw = dpp_quad_sum(Pu), Qw = dpp_quad_sum(Qu);
+            const unsigned pay[kSampSlots] = {hi32(Aw), lo32(Aw), hi32(Bw), lo32(Bw),
+                                              hi32(Pw), lo32(Pw), hi32(Qw), lo32(Qw)};
+            publish_quads(slots, pay, s.epoch, s.q, SH::kW, nq);
         }
-        const double Aw = dpp_wave_sum(Au), Bw = dpp_wave_sum(Bu), Pw = dpp_wave_sum(Pu), Qw = dpp_wave_sum(Qu);
-        unsigned long long* slots = a.samp_slots + size_t(s.b) * a.Q * kSampSlots;
-        const unsigned pay[kSampSlots] = {hi32(Aw), lo32(Aw), hi32(Bw), lo32(Bw),
-                                          hi32(Pw), lo32(Pw), hi32(Qw), lo32(Qw)};
-        publish(slots + s.q, pay, s.epoch, a.Q);
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
         unsigned v[kSampSlots];
-        const bool ok = gather<kSampSlots>(slots, a.Q, s.epoch, v);
-        // lane l < Q: workgroup l's sums (zero in the other lanes)
+        const bool ok = gather<kSampSlots>(slots, nq, s.epoch, v);
+        // lane l < nq: quad l's sums (zero in the other lanes)
         const double Ag = join64(v[0], v[1]), Bg = join64(v[2], v[3]);
         const double Pg = join64(v[4], v[5]), Qg = join64(v[6], v[7]);
         const double Zp = dpp_wave_sum(Pg), Zq = dpp_wave_sum(Qg);
@@ -829,10 +891,15 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
         bool exact;
         const int qstar = find_crossing(Rg, 0.0, t, run, exact);
         int owner = -1;
-        if (qstar == s.q) {        // the crossing workgroup: find the crossing unit
-            const double Ru = use_p ? Pu : fmax(0.0, Au * invZp - Bu * invZq);
+        if (qstar / (SH::kW / kQuad) == s.q) {   // the crossing quad is this workgroup's: find its unit
+            const int j = qstar % (SH::kW / kQuad);
+            double Ru = 0.0;
+            if (lane < kQuad) {
+                const double4 v4 = sh.usum[kQuad * j + lane];
+                Ru = use_p ? v4.z : fmax(0.0, v4.x * invZp - v4.y * invZq);
+            }
             bool exact_u;
-            owner = find_crossing(Ru, run, t, run, exact_u);
+            owner = kQuad * j + find_crossing(Ru, run, t, run, exact_u);
             exact = exact && exact_u;
         }
         if (lane == 0) {
@@ -897,9 +964,9 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
 // group's, combines those in workgroup order and takes the acceptance test; every
 // workgroup reaches the same decision from the same bits. Returns the result flags
 // (kResAccepted, kResError) and the row's statistics in `st`.
-template <bool kVec4>
+template <bool kVec4, typename SH>
 __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx& s, const LevelRef& r,
-                                               f4 (&xp)[kVecs], f4 (&xq)[kVecs], RowStats& st, Shared& sh,
+                                               f4 (&xp)[kVecs], f4 (&xq)[kVecs], RowStats& st, SH& sh,
                                                bool& counted) {
     const float* prow = r.prow;
     const float* qrow = r.qrow;
@@ -937,30 +1004,32 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
     __syncthreads();
     if (s.wave == 0) {
         const int lane = lane_id();
-        float mpw = -INFINITY, mqw = -INFINITY;
-        double zpw = 0.0, zqw = 0.0;
-        if (lane < kUnitWaves) {
-            const UnitStat u = sh.unit[lane];
-            mpw = u.Mp; mqw = u.Mq; zpw = u.Zp; zqw = u.Zq;
+        const int nq = quads_of(a.U);
+        {   // the workgroup's quads, all at once: unit i in lane i, quad j's pair in lane 4j
+            float mpw = -INFINITY, mqw = -INFINITY;
+            double zpw = 0.0, zqw = 0.0;
+            if (lane < SH::kW) {
+                const UnitStat u = sh.unit[lane];
+                mpw = u.Mp; mqw = u.Mq; zpw = u.Zp; zqw = u.Zq;
+            }
+            float Mp_w, Mq_w;
+            double Zp_w, Zq_w;
+            combine_quad(mpw, zpw, a.invT64, Mp_w, Zp_w);
+            combine_quad(mqw, zqw, a.invT64, Mq_w, Zq_w);
+            const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_w), __builtin_bit_cast(unsigned, Mq_w),
+                                              hi32(Zp_w), lo32(Zp_w), hi32(Zq_w), lo32(Zq_w)};
+            publish_quads(r.slots, pay, s.epoch, s.q, SH::kW, nq);
         }
-        float Mp_w, Mq_w;
-        double Zp_w, Zq_w;
-        combine_pair(mpw, zpw, a.invT64, Mp_w, Zp_w);
-        combine_pair(mqw, zqw, a.invT64, Mq_w, Zq_w);
-        unsigned long long* slots = r.slots;
-        const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_w), __builtin_bit_cast(unsigned, Mq_w),
-                                          hi32(Zp_w), lo32(Zp_w), hi32(Zq_w), lo32(Zq_w)};
-        publish(slots + s.q, pay, s.epoch, a.Q);
         TokenLogits tl = tok;
         double u_smp;
         stream_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + r.pos, r.stream, &tl.u_acc, &u_smp);
         unsigned v[kStatSlots];
         unsigned flags = 0;
-        if (gather<kStatSlots>(slots, a.Q, s.epoch, v)) {
+        if (gather<kStatSlots>(r.slots, nq, s.epoch, v)) {
             count_group(a, s, counted);
             tl.zp = uniform(ztp);
             tl.zq = uniform(ztq);
-            const bool have = lane < a.Q;
+            const bool have = lane < nq;
             combine_pair(have ? __builtin_bit_cast(float, v[0]) : -INFINITY, have ? join64(v[2], v[3]) : 0.0,
                          a.invT64, st.Mp, st.Zp);
             combine_pair(have ? __builtin_bit_cast(float, v[1]) : -INFINITY, have ? join64(v[4], v[5]) : 0.0,
@@ -983,16 +1052,16 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
 }
 
 // Level `row` of the chain (rows p_row and q_row, draft row, position L + 1 + row).
-template <bool kVec4>
+template <bool kVec4, typename SH>
 __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
-                                               f4 (&xq)[kVecs], RowStats& st, Shared& sh, bool& counted) {
+                                               f4 (&xq)[kVecs], RowStats& st, SH& sh, bool& counted) {
     LevelRef r;
     r.prow = s.prow_base + size_t(row) * a.V;
     r.qrow = s.qrow_base + size_t(row) * a.V;
     r.tok_idx = s.db + row;
     r.pos = row;
     r.stream = 0u;
-    r.slots = a.stat_slots + (size_t(s.b) * (a.k + 1) + row) * a.Q * kStatSlots;
+    r.slots = a.stat_slots + (size_t(s.b) * (a.k + 1) + row) * a.U * kStatSlots;
     r.acc_idx = s.db + row;
     r.out_idx = s.tb + row;
     r.node_idx = -1;
@@ -1005,10 +1074,10 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
 // unit's own normaliser, a superset of the row's heavy set); wave 0 rescales its
 // units to the workgroup maximum and publishes (sum, maximum); the gathered pairs
 // are rescaled to the row maximum M, which also gives the row's Z.
-template <bool kVec4, typename E>
+template <bool kVec4, typename SH, typename E>
 __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s, const float* prow, int pos,
                                            unsigned long long* slots, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
-                                           Shared& sh, bool& counted, E&& emit) {
+                                           SH& sh, bool& counted, E&& emit) {
     const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, a.V);
     load_unit<kVec4, false>(rp, rp, a.V, s.u, xp, xq);
     float m = -INFINITY;
@@ -1036,22 +1105,25 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
     if (lane == 0) sh.usum[s.wave] = make_double4(us.P, Mu64, 0.0, 0.0);
     __syncthreads();
     if (s.wave == 0) {
-        double Pu = 0.0, Mv = -INFINITY;
-        if (lane < kUnitWaves) {
-            const double4 v = sh.usum[lane];
-            Pu = v.x;
-            Mv = v.y;
+        const int nq = quads_of(a.U);
+        {   // the workgroup's quads, all at once: (weight sum, maximum)
+            double Pu = 0.0, Mv = -INFINITY;
+            if (lane < SH::kW) {
+                const double4 v4 = sh.usum[lane];
+                Pu = v4.x;
+                Mv = v4.y;
+            }
+            const double Mw = dpp_quad_max(static_cast<float>(Mv));
+            const double Ww = dpp_quad_sum((Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - Mw) * a.invT64) : 0.0);
+            const unsigned pay[4] = {hi32(Ww), lo32(Ww), hi32(Mw), lo32(Mw)};
+            publish_quads(slots, pay, s.epoch, s.q, SH::kW, nq);
         }
-        const double Mw = dpp_wave_max(static_cast<float>(Mv));
-        const double Ww = dpp_wave_sum((Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - Mw) * a.invT64) : 0.0);
-        const unsigned pay[4] = {hi32(Ww), lo32(Ww), hi32(Mw), lo32(Mw)};
-        publish(slots + s.q, pay, s.epoch, a.Q);
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[4];
-        const bool ok = gather<4>(slots, a.Q, s.epoch, v);
+        const bool ok = gather<4>(slots, nq, s.epoch, v);
         count_group(a, s, counted);
-        const bool have = lane < a.Q;
+        const bool have = lane < nq;
         const double Wg = have ? join64(v[0], v[1]) : 0.0;
         const double Mg = have ? join64(v[2], v[3]) : -INFINITY;
         const double M = dpp_wave_max(static_cast<float>(Mg));
@@ -1062,10 +1134,15 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
         bool exact;
         const int qstar = find_crossing(Wr, 0.0, t, run, exact);
         int owner = -1;
-        if (qstar == s.q) {
-            const double Wu = (Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - M) * a.invT64) : 0.0;
+        if (qstar / (SH::kW / kQuad) == s.q) {   // the crossing quad is this workgroup's: find its unit
+            const int j = qstar % (SH::kW / kQuad);
+            double Wu = 0.0;
+            if (lane < kQuad) {
+                const double4 v4 = sh.usum[kQuad * j + lane];
+                Wu = (v4.x > 0.0) ? v4.x * exp_nonpos_f64((v4.y - M) * a.invT64) : 0.0;
+            }
             bool exact_u;
-            owner = find_crossing(Wu, run, t, run, exact_u);
+            owner = kQuad * j + find_crossing(Wu, run, t, run, exact_u);
             exact = exact && exact_u;
         }
         if (lane == 0) {
@@ -1101,12 +1178,12 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
 }
 
 // The bonus row p_k after k acceptances.
-template <bool kVec4>
+template <bool kVec4, typename SH>
 __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
-                                          Shared& sh, bool& counted) {
+                                          SH& sh, bool& counted) {
     const int row = s.kb;
     bonus_core<kVec4>(a, s, s.prow_base + size_t(row) * a.V, row,
-                      a.samp_slots + size_t(s.b) * a.Q * kSampSlots, xp, xq, sh, counted,
+                      a.samp_slots + size_t(s.b) * a.U * kSampSlots, xp, xq, sh, counted,
                       [&](int y, double py) { emit_chain(a, s, row, y, py); });
 }
 
@@ -1368,8 +1445,10 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
     const size_t b = s.b;
     const float* tbase = a.target + b * (N + 1) * a.V;
     const float* dbase = a.draft + b * (N + 1) * a.V;
-    unsigned long long* slots0 = a.tree_slots + b * kTreeEx * kSampSlots * a.Q;
-    auto slot = [&](int e) { return slots0 + size_t(e) * kSampSlots * a.Q; };
+    // one block of kSampSlots x U slots per exchange (unit-level exchanges fill it,
+    // workgroup-level ones use its first kSampSlots x Q)
+    unsigned long long* slots0 = a.tree_slots + b * kTreeEx * kSampSlots * a.U;
+    auto slot = [&](int e) { return slots0 + size_t(e) * kSampSlots * a.U; };
     int ex = 0, v = 0, depth = 0;
     unsigned tested = 0u;
     // A broken tree ends the sequence with num_accepted = -1. A failure before the group's first
@@ -1519,8 +1598,11 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <bool kVec4>
-__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
+// W unit wavefronts per workgroup: 8 (one workgroup per CU) when the batch fills the
+// device, 4 (a sequence over twice as many CUs, one workgroup on each) when there are
+// CUs to spare, which shortens every step of a sequence's serial chain.
+template <bool kVec4, int W>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
     // Workgroups go to the eight XCDs round-robin; with a multiple of eight groups,
     // group g takes the Q workgroups on XCD g % 8 (they start together and share
     // an L2). Any other count uses the plain mapping. Both are bijections.
@@ -1537,13 +1619,13 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     SeqCtx s;
     s.q = q;
     s.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    s.u = q * kUnitWaves + s.wave;
+    s.u = q * W + s.wave;
     {
         const unsigned last = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s.epoch = (last + 1u == 0u) ? 1u : last + 1u;
     }
     bool counted = q != 0;   // workgroup 0's wave 0 counts the group
-    __shared__ Shared sh;
+    __shared__ SharedT<W> sh;
     f4 xp[kVecs], xq[kVecs];
     for (int b = group; b < a.B; b += a.groups) {
         s.b = b;
@@ -1579,32 +1661,38 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <bool kVec4, bool kTree>
-hipError_t co_resident(int dev, int* wgs) {
-    static int memo[64];
-    if (dev >= 0 && dev < 64 && memo[dev] > 0) {
-        *wgs = memo[dev];
+// Workgroups of the kernel the device holds at once, and its CU count.
+template <bool kVec4, bool kTree, int W>
+hipError_t co_resident(int dev, int* wgs, int* cus_out) {
+    static int memo[64][2];
+    if (dev >= 0 && dev < 64 && memo[dev][0] > 0) {
+        *wgs = memo[dev][0];
+        *cus_out = memo[dev][1];
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
     hipError_t e = kTree
         ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_tree_kernel<kVec4>, kRT, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4>, kRT, 0);
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4, W>, W * kWave, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     *wgs = per_cu * cus;
-    if (dev >= 0 && dev < 64) memo[dev] = *wgs;
+    *cus_out = cus;
+    if (dev >= 0 && dev < 64) {
+        memo[dev][0] = *wgs;
+        memo[dev][1] = cus;
+    }
     return hipSuccess;
 }
 
-template <bool kVec4, bool kTree>
+template <bool kVec4, bool kTree, int W>
 hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int wgs = 0;
-    e = co_resident<kVec4, kTree>(dev, &wgs);
+    int wgs = 0, cus = 0;
+    e = co_resident<kVec4, kTree, W>(dev, &wgs, &cus);
     if (e != hipSuccess) return e;
     int groups = min(a.B, wgs / a.Q);
     if (groups < 1) return hipErrorInvalidConfiguration;
@@ -1616,25 +1704,50 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     // per call on this stack; should residency ever be partial, the waits are
     // bounded and the affected sequences report an error instead of hanging.)
     if (kTree) hipLaunchKernelGGL((reject_tree_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
-    else hipLaunchKernelGGL((reject_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
+    else hipLaunchKernelGGL((reject_kernel<kVec4, W>), dim3(groups * a.Q), dim3(W * kWave), 0, stream, a);
     return hipGetLastError();
+}
+
+// CUs of the current device (0 if it cannot be read).
+int device_cus() {
+    static int memo[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (memo[dev] > 0) return memo[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    memo[dev] = cus;
+    return cus;
+}
+
+// Workgroups per sequence with W unit wavefronts each.
+int groups_of(int V, int W) {
+    const int U = (V + kUnit - 1) / kUnit;
+    return (U + W - 1) / W;
 }
 
 }  // namespace
 
 size_t reject_workspace_bytes(int B, int k, int V) {
-    const int U = (V + kUnit - 1) / kUnit;
-    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
-    return reject_layout(B, k, Q).total;
+    return reject_layout(B, k, (V + kUnit - 1) / kUnit).total;
 }
 
-int reject_max_vocab() { return kUnit * kUnitWaves * kMaxQ; }
+int reject_max_vocab() { return kUnit * 256; }
 
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
-    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
+    // Four-wave workgroups when each of them can have a CU to itself, else eight.
+    const int cus = device_cus();
+    const int W = (cus > 0 && static_cast<long long>(p.B) * groups_of(p.V, 4) <= cus) ? 4 : 8;
+    const int Q = groups_of(p.V, W);
     if (Q > kMaxQ) return hipErrorInvalidValue;
-    const RejectLayout lay = reject_layout(p.B, p.k, Q);
+    const RejectLayout lay = reject_layout(p.B, p.k, U);
     char* ws = static_cast<char*>(p.workspace);
     RejectArgs a;
     a.target = p.target_logits;
@@ -1659,14 +1772,15 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.T = p.temperature;
     a.seed = p.seed;
-    return (p.V % 4) == 0 ? launch_variant<true, false>(a, stream) : launch_variant<false, false>(a, stream);
+    if (W == 4)
+        return (p.V % 4) == 0 ? launch_variant<true, false, 4>(a, stream) : launch_variant<false, false, 4>(a, stream);
+    return (p.V % 4) == 0 ? launch_variant<true, false, 8>(a, stream) : launch_variant<false, false, 8>(a, stream);
 }
 
 size_t reject_tree_workspace_bytes(int B, int nodes, int V) {
     const int U = (V + kUnit - 1) / kUnit;
-    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
     (void)nodes;
-    return align256(4 * sizeof(unsigned)) + sizeof(unsigned long long) * size_t(B) * kTreeEx * kSampSlots * Q;
+    return align256(4 * sizeof(unsigned)) + sizeof(unsigned long long) * size_t(B) * kTreeEx * kSampSlots * U;
 }
 
 int reject_tree_max_branch() { return kMaxBranch; }
@@ -1699,7 +1813,8 @@ hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.T = p.temperature;
     a.seed = p.seed;
-    return (p.V % 4) == 0 ? launch_variant<true, true>(a, stream) : launch_variant<false, true>(a, stream);
+    return (p.V % 4) == 0 ? launch_variant<true, true, kUnitWaves>(a, stream)
+                          : launch_variant<false, true, kUnitWaves>(a, stream);
 }
 
 }  // namespace specverify

@@ -81,6 +81,20 @@ def test_vocab_and_draft_length_edges(device, V, k, B):
     _check(inp, device, [11 + 13 * i for i in range(64)], label=f"V{V}/k{k}")
 
 
+def test_maximum_vocab(device):
+    """V = 2^20, the largest vocabulary the call takes: 256 units of 4096 logits, 32 workgroups per sequence."""
+    rng = np.random.default_rng(20)
+    inp = _custom(1 << 20, 1, 2, rng, sigma=3.0)
+    _check(inp, device, [3 + 7 * i for i in range(16)], label="V2^20")
+
+
+def test_maximum_batch(device):
+    """B = 65535, the largest batch: far more sequences than resident groups, taken in turn."""
+    rng = np.random.default_rng(21)
+    inp = _custom(5, 1, 65535, rng)
+    _check(inp, device, [9, 10], label="B65535")
+
+
 def test_temperature(device):
     rng = np.random.default_rng(3)
     inp = _custom(20000, 3, 16, rng, sigma=3.0)
@@ -145,6 +159,23 @@ def test_deterministic_and_batch_invariant(device):
     c = RejectDevice(sub, device).call(123)
     for key in a:
         np.testing.assert_array_equal(c[key], a[key][perm])
+
+
+def test_batch_invariant_across_workgroup_sizes(device):
+    """A full 8B batch (B = 64) runs eight unit wavefronts per workgroup, its first 32
+    sequences alone run four (a sequence then spans twice the CUs); the units are
+    combined in one order either way, so every output is bit-identical."""
+    inp = make_reject_inputs(PRESETS["8b"], B=64)
+    full = RejectDevice(inp, device)
+    half = dict(inp)
+    for key in ("target_logits", "draft_logits", "draft_tokens", "seq_ids", "seq_lens"):
+        half[key] = np.ascontiguousarray(inp[key][:32])
+    half["B"] = 32
+    part = RejectDevice(half, device)
+    for seed in (5, 77, 901):
+        a, c = full.call(seed), part.call(seed)
+        for key in a:
+            np.testing.assert_array_equal(c[key], a[key][:32])
 
 
 def test_commit_matches_oracle(device):
