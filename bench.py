@@ -24,6 +24,9 @@ Other modes:
                                nodes) through the tree attention and the tree walk
   --variant fused              RoPE + KV append, attention, the LM head (H = 4096),
                                rejection sampling on its logits, and the commit
+  --workload 7b --sweep 256,64,16,4
+                               the shrinking active batch: the same step on the
+                               first B sequences of the workload's seeded batch
   --cpu-baseline-only          time the oracle (run in a single-threaded child)
   --copy-calibration           also run an elementwise kernel of known traffic
                                (negation of 512 MiB fp32: 512 MiB read, 512 MiB
@@ -733,6 +736,8 @@ def gpu_bench(args) -> dict:
         return gpu_bench_tree(args, p, dev)
     if args.variant == "fused":
         return gpu_bench_fused(args, p, dev)
+    if args.sweep:
+        return gpu_bench_sweep(args, p, dev)
     print(f"[bench] generating {args.workload} inputs (k = {p.k})", file=sys.stderr, flush=True)
     inp = make_inputs(args.workload, preset=p)
 
@@ -857,6 +862,105 @@ def gpu_bench(args) -> dict:
     return result
 
 
+def gpu_bench_sweep(args, p, dev) -> dict:
+    """The shrinking active batch: the workload's seeded batch is generated once and the
+    same three calls are timed on its first B sequences for each B of --sweep (the
+    sequences that remain are the first B of the full batch, so every point reads a
+    subset of the same pages and rows)."""
+    import dataclasses
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_14_amd as sv
+    from workloads import make_inputs
+
+    sizes = [int(x) for x in args.sweep.split(",")]
+    if max(sizes) > p.B or min(sizes) < 1:
+        raise ValueError(f"--sweep sizes must lie in [1, {p.B}]")
+    print(f"[bench] generating {args.workload} inputs (B = {p.B}, k = {p.k})", file=sys.stderr, flush=True)
+    inp = make_inputs(args.workload, preset=p)
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    kc, vc = bf16(inp["k_cache"]), bf16(inp["v_cache"])
+    del inp["k_cache"], inp["v_cache"]
+    k = p.k
+    cap = inp["max_blocks"] * p.block_size
+    stream = torch.cuda.current_stream()
+    points = []
+    for Bs in sizes:
+        pb = dataclasses.replace(p, B=Bs)
+        q = bf16(inp["q"][:Bs])
+        bt = t(inp["block_table"][:Bs])
+        seq_lens0 = t(inp["seq_lens"][:Bs])
+        seq_lens = seq_lens0.clone()
+        tl, dl = t(inp["target_logits"][:Bs]), t(inp["draft_logits"][:Bs])
+        dt, sid = t(inp["draft_tokens"][:Bs]), t(inp["seq_ids"][:Bs])
+        msl = int(np.max(inp["seq_lens"][:Bs])) + k + 1
+        attn_out = torch.empty_like(q)
+        out_tokens = torch.empty((Bs, k + 1), dtype=torch.int32, device=dev)
+        num_acc = torch.empty(Bs, dtype=torch.int32, device=dev)
+        out_probs = torch.empty((Bs, k + 1), dtype=torch.float32, device=dev)
+        acc_probs = torch.empty((Bs, k), dtype=torch.float32, device=dev)
+        overflow = torch.empty(Bs, dtype=torch.int32, device=dev)
+        attn_ws = torch.zeros(max(256, sv.verify_attn_workspace_size(Bs, k, p.Hq, p.Hkv, p.D, msl)),
+                              dtype=torch.uint8, device=dev)
+        rej_ws = torch.zeros(sv.reject_sample_workspace_size(Bs, k, p.V), dtype=torch.uint8, device=dev)
+
+        def step(events=None):
+            seq_lens.copy_(seq_lens0)
+            if events is not None:
+                events[0].record(stream)
+            sv.verify_attn(q, kc, vc, bt, seq_lens, attn_out, msl, None, attn_ws, stream)
+            if events is not None:
+                events[1].record(stream)
+            sv.reject_sample(tl, dl, dt, sid, seq_lens, p.temperature, inp["seed"], out_tokens, num_acc,
+                             out_probs, acc_probs, rej_ws, stream)
+            if events is not None:
+                events[2].record(stream)
+            sv.commit_lengths(seq_lens, num_acc, k, cap, overflow, stream)
+            if events is not None:
+                events[3].record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        sampled = list(range(0, args.steps, EVENT_EVERY))
+        evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs.get(i))
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) / args.steps
+        mean = lambda v: sum(v) / len(v)
+        attn_s = mean([e[0].elapsed_time(e[1]) for e in evs.values()]) / 1e3
+        rej_s = mean([e[1].elapsed_time(e[2]) for e in evs.values()]) / 1e3
+        com_s = mean([e[2].elapsed_time(e[3]) for e in evs.values()]) / 1e3
+        acc = num_acc.cpu().numpy()
+        a_bytes, r_bytes, _ = algorithmic_bytes(pb, inp["seq_lens"][:Bs], acc)
+        tokens = int(np.sum(acc + 1))
+        points.append(dict(B=Bs, verified_tokens_per_s=tokens / wall, ms_per_step=wall * 1e3,
+                           tokens_per_step=tokens,
+                           verify_attn=dict(avg_us=attn_s * 1e6, bytes=a_bytes,
+                                            frac_of_peak=a_bytes / attn_s / 1e9 / HBM_PEAK_GBS),
+                           reject_sample=dict(avg_us=rej_s * 1e6, bytes=r_bytes,
+                                              frac_of_peak=r_bytes / rej_s / 1e9 / HBM_PEAK_GBS),
+                           commit_lengths=dict(avg_us=com_s * 1e6)))
+        print(f"[bench] B={Bs}: {tokens / wall:.0f} tokens/s, attn {attn_s * 1e6:.1f} us, "
+              f"reject {rej_s * 1e6:.1f} us", file=sys.stderr, flush=True)
+        del q, bt, seq_lens0, seq_lens, tl, dl, dt, sid, attn_out, attn_ws, rej_ws
+    return dict(metric="verified tokens/s per batch size (shrinking active batch)", unit="verified tokens/s",
+                n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True, dtype="bf16",
+                data="synthetic",
+                config=dict(workload=(f"{args.workload}: first B of a seeded batch of {p.B}, k={k}, Hq={p.Hq}, "
+                                      f"Hkv={p.Hkv}, D={p.D}, contexts {p.ctx}, block_size={p.block_size}, V={p.V}, "
+                                      "one attention layer + rejection sampling + commit")),
+                sweep=points)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -866,6 +970,8 @@ def main():
     ap.add_argument("--variant", choices=["uniform", "plain", "ragged", "tree", "fused"], default="uniform")
     ap.add_argument("--tree", default="2,2", metavar="T,D",
                     help="tree variant: branching factor and depth of the full draft tree")
+    ap.add_argument("--sweep", metavar="B1,B2,...",
+                    help="time the step on the first B sequences of the workload's batch for each B")
     ap.add_argument("--cold-steps", type=int, default=30,
                     help="steps timed per call after a cache-evicting write (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -907,7 +1013,7 @@ def main():
         sys.exit(2)
 
     result = gpu_bench(args)
-    if not args.no_cpu_baseline and args.variant == "uniform":
+    if not args.no_cpu_baseline and args.variant == "uniform" and not args.sweep:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = run_cpu_baseline_child(args.workload)
         if cb is not None:

@@ -55,6 +55,7 @@ constexpr int kBtEntries = kBtSpan / 16;
 constexpr int kLdsPrefix = 4096;                    // batch sizes whose work prefix each workgroup builds in LDS
 constexpr int kMaxP = 1024;                         // workgroups of the persistent grid (workspace is sized for this)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMergeBatch = 8;                      // split pieces whose loads the merge issues together
 
 struct AttnArgs {
     const uint16_t* q;
@@ -471,6 +472,46 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
     }
 }
 
+// One row (dims d0 .. d0 + D/16) of a split segment: M = max over the pieces w0 .. w1,
+// then their sums and outputs weighted by 2^(m - M), folded in workgroup order.
+// The loads of KB pieces are issued together (addresses clamped to the last piece,
+// weights past it 0, so the sums are the same bits as piece by piece). Returns 1 / sum.
+template <int D, int KB, typename PR>
+__device__ __forceinline__ float merge_row(const AttnArgs& a, PR&& prow_of, int w0, int w1, int n, int r, int d0,
+                                           float (&acc)[D / 16]) {
+    float M = -INFINITY;
+    for (int wb = w0; wb <= w1; wb += KB) {
+        float mv[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) mv[j] = a.part_ml[prow_of(min(wb + j, w1), n, r) * 2];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) M = fmaxf(M, (wb + j <= w1) ? mv[j] : -INFINITY);
+    }
+    float lsum = 0.0f;
+#pragma unroll
+    for (int dd = 0; dd < D / 16; ++dd) acc[dd] = 0.0f;
+    for (int wb = w0; wb <= w1; wb += KB) {
+        float ms[KB], ls[KB], po[KB][D / 16];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const size_t prow = prow_of(min(wb + j, w1), n, r);
+            ms[j] = a.part_ml[prow * 2];
+            ls[j] = a.part_ml[prow * 2 + 1];
+#pragma unroll
+            for (int dd = 0; dd < D / 16; ++dd) po[j][dd] = a.part_o[prow * D + d0 + dd];
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            // branch-free, so that all of the batch's loads stay in flight together
+            const float wt = (wb + j > w1 || ms[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M);
+            lsum += wt * ls[j];
+#pragma unroll
+            for (int dd = 0; dd < D / 16; ++dd) acc[dd] += wt * po[j][dd];
+        }
+    }
+    return 1.0f / lsum;
+}
+
 // Combine the pieces of every (sequence, KV head, row group) segment that was
 // split between workgroups, in workgroup order.
 template <int D>
@@ -490,33 +531,22 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
     const int first_slot = (S == range_start(w0, total, a.P)) ? 0 : 1;
     const int g = u / sh.row_groups, rg = u % sh.row_groups;
     const int tid = threadIdx.x;
+    // piece ww's partial row for tile n: workgroup w0's piece sits in slot first_slot,
+    // every later one in slot 0 of its workgroup
+    auto prow_of = [&](int ww, int n, int r) {
+        return (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * rgr + n * 16 + r;
+    };
     for (int n = 0; n < tiles; ++n) {
         const int r = tid / 16;
         const int d0 = (tid % 16) * (D / 16);
         const int row = rg * rgr + n * 16 + r;
         if (row >= sh.rows) continue;
-        float M = -INFINITY;
-        for (int ww = w0; ww <= w1; ++ww) {
-            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * rgr + n * 16 + r;
-            M = fmaxf(M, a.part_ml[prow * 2]);
-        }
-        float lsum = 0.0f;
         float acc[D / 16];
-#pragma unroll
-        for (int dd = 0; dd < D / 16; ++dd) acc[dd] = 0.0f;
-        for (int ww = w0; ww <= w1; ++ww) {
-            const size_t prow = (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * rgr + n * 16 + r;
-            const float ms = a.part_ml[prow * 2];
-            const float wt = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-            lsum += wt * a.part_ml[prow * 2 + 1];
-            const float* po = a.part_o + prow * D + d0;
-#pragma unroll
-            for (int dd = 0; dd < D / 16; ++dd) acc[dd] += wt * po[dd];
-        }
+        const float inv = (w1 - w0 < 2) ? merge_row<D, 2>(a, prow_of, w0, w1, n, r, d0, acc)
+                                        : merge_row<D, kMergeBatch>(a, prow_of, w0, w1, n, r, d0, acc);
         const int i = row / a.G;
         const int h = g * a.G + row % a.G;
         uint16_t* op = a.out + ((size_t(sh.row0) + i) * a.Hq + h) * D + d0;
-        const float inv = 1.0f / lsum;
 #pragma unroll
         for (int dd = 0; dd < D / 16; ++dd) op[dd] = f32_to_bf16_bits(acc[dd] * inv);
     }
