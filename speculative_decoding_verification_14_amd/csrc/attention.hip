@@ -139,6 +139,15 @@ __device__ __forceinline__ long long range_start(int w, long long total, int P) 
     return w * q + (w < r ? w : r);
 }
 
+// Workgroups that share the work: all P launched, or fewer when there is little work,
+// so that each takes at least kMinIters iterations and a segment is cut into fewer
+// pieces for the merge. Both launches derive it from the same total.
+constexpr int kMinIters = 4;
+__device__ __forceinline__ int sharing_workgroups(long long total, int P) {
+    const long long want = total / kMinIters;
+    return static_cast<int>(want < 1 ? 1 : (want < P ? want : P));
+}
+
 __device__ __forceinline__ int range_owner(long long x, long long total, int P) {
     const long long q = total / P, r = total % P;
     if (x < r * (q + 1)) return static_cast<int>(x / (q + 1));
@@ -204,7 +213,9 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
         prefix = s_prefix;
     }
     const long long total = prefix[a.B];
-    const long long r0 = range_start(w, total, a.P), r1 = range_start(w + 1, total, a.P);
+    const int P = sharing_workgroups(total, a.P);
+    if (w >= P) return;
+    const long long r0 = range_start(w, total, P), r1 = range_start(w + 1, total, P);
     if (r0 >= r1) return;
 
     // segment (b, u) starts at prefix[b] + u * iters_b; find the last b whose start is <= r0
@@ -526,9 +537,10 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
     if (iters_b <= 0) return;
     const long long S = static_cast<long long>(a.prefix[b]) + static_cast<long long>(u) * iters_b;
     const long long E = S + iters_b;
-    const int w0 = range_owner(S, total, a.P), w1 = range_owner(E - 1, total, a.P);
+    const int P = sharing_workgroups(total, a.P);
+    const int w0 = range_owner(S, total, P), w1 = range_owner(E - 1, total, P);
     if (w0 == w1) return;                      // one workgroup wrote the output directly
-    const int first_slot = (S == range_start(w0, total, a.P)) ? 0 : 1;
+    const int first_slot = (S == range_start(w0, total, P)) ? 0 : 1;
     const int g = u / sh.row_groups, rg = u % sh.row_groups;
     const int tid = threadIdx.x;
     // piece ww's partial row for tile n: workgroup w0's piece sits in slot first_slot,
