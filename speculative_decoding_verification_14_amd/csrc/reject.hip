@@ -203,14 +203,14 @@ __device__ __forceinline__ void combine_quad(float m, double z, double invT64, f
     Z = dpp_quad_sum((z > 0.0) ? z * exp_nonpos_f64((static_cast<double>(m) - M) * invT64) : 0.0);
 }
 
-// Lane 4j of wave 0 publishes quad j of its workgroup (quad index q * W/4 + j of the
-// sequence, when below nq): payload s to slots[s * nq + quad].
+// Lane 4j (j < lanes / 4) of wave 0 publishes the quad in its lanes, quad index
+// first + j of the sequence when below nq: payload s to slots[s * nq + quad].
 template <int N>
 __device__ __forceinline__ void publish_quads(unsigned long long* slots, const unsigned (&payload)[N], unsigned epoch,
-                                              int q, int W, int nq) {
+                                              int first, int lanes, int nq) {
     const int lane = lane_id();
-    const int qd = q * (W / kQuad) + lane / kQuad;
-    if ((lane & (kQuad - 1)) == 0 && lane < W && qd < nq) {
+    const int qd = first + lane / kQuad;
+    if ((lane & (kQuad - 1)) == 0 && lane < lanes && qd < nq) {
 #pragma unroll
         for (int s = 0; s < N; ++s) slot_store(slots + size_t(s) * nq + qd, payload[s], epoch);
     }
@@ -867,7 +867,7 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
             const double Aw = dpp_quad_sum(Au), Bw = dpp_quad_sum(Bu), Pw = dpp_quad_sum(Pu), Qw = dpp_quad_sum(Qu);
             const unsigned pay[kSampSlots] = {hi32(Aw), lo32(Aw), hi32(Bw), lo32(Bw),
                                               hi32(Pw), lo32(Pw), hi32(Qw), lo32(Qw)};
-            publish_quads(slots, pay, s.epoch, s.q, SH::kW, nq);
+            publish_quads(slots, pay, s.epoch, s.q * (SH::kW / kQuad), SH::kW, nq);
         }
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
@@ -964,7 +964,10 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
 // group's, combines those in workgroup order and takes the acceptance test; every
 // workgroup reaches the same decision from the same bits. Returns the result flags
 // (kResAccepted, kResError) and the row's statistics in `st`.
-template <bool kVec4, typename SH>
+// kSeq: the workgroup's quads one after another in lanes 0..3 instead of all at
+// once (the same bits; it leaves the tree walk, which is short of registers, with
+// fewer spills).
+template <bool kVec4, bool kSeq = false, typename SH>
 __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx& s, const LevelRef& r,
                                                f4 (&xp)[kVecs], f4 (&xq)[kVecs], RowStats& st, SH& sh,
                                                bool& counted) {
@@ -1005,11 +1008,13 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
     if (s.wave == 0) {
         const int lane = lane_id();
         const int nq = quads_of(a.U);
-        {   // the workgroup's quads, all at once: unit i in lane i, quad j's pair in lane 4j
+        constexpr int kLanes = kSeq ? kQuad : SH::kW;
+#pragma unroll 1
+        for (int j = 0; j < SH::kW / kLanes; ++j) {   // unit j * kLanes + i in lane i, a quad's pair in lane 4m
             float mpw = -INFINITY, mqw = -INFINITY;
             double zpw = 0.0, zqw = 0.0;
-            if (lane < SH::kW) {
-                const UnitStat u = sh.unit[lane];
+            if (lane < kLanes) {
+                const UnitStat u = sh.unit[j * kLanes + lane];
                 mpw = u.Mp; mqw = u.Mq; zpw = u.Zp; zqw = u.Zq;
             }
             float Mp_w, Mq_w;
@@ -1018,7 +1023,7 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
             combine_quad(mqw, zqw, a.invT64, Mq_w, Zq_w);
             const unsigned pay[kStatSlots] = {__builtin_bit_cast(unsigned, Mp_w), __builtin_bit_cast(unsigned, Mq_w),
                                               hi32(Zp_w), lo32(Zp_w), hi32(Zq_w), lo32(Zq_w)};
-            publish_quads(r.slots, pay, s.epoch, s.q, SH::kW, nq);
+            publish_quads(r.slots, pay, s.epoch, s.q * (SH::kW / kQuad) + j * (kLanes / kQuad), kLanes, nq);
         }
         TokenLogits tl = tok;
         double u_smp;
@@ -1074,7 +1079,7 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
 // unit's own normaliser, a superset of the row's heavy set); wave 0 rescales its
 // units to the workgroup maximum and publishes (sum, maximum); the gathered pairs
 // are rescaled to the row maximum M, which also gives the row's Z.
-template <bool kVec4, typename SH, typename E>
+template <bool kVec4, bool kSeq = false, typename SH, typename E>
 __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s, const float* prow, int pos,
                                            unsigned long long* slots, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
                                            SH& sh, bool& counted, E&& emit) {
@@ -1106,17 +1111,19 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
     __syncthreads();
     if (s.wave == 0) {
         const int nq = quads_of(a.U);
-        {   // the workgroup's quads, all at once: (weight sum, maximum)
+        constexpr int kLanes = kSeq ? kQuad : SH::kW;
+#pragma unroll 1
+        for (int j = 0; j < SH::kW / kLanes; ++j) {   // (weight sum, maximum) of each quad
             double Pu = 0.0, Mv = -INFINITY;
-            if (lane < SH::kW) {
-                const double4 v4 = sh.usum[lane];
+            if (lane < kLanes) {
+                const double4 v4 = sh.usum[j * kLanes + lane];
                 Pu = v4.x;
                 Mv = v4.y;
             }
             const double Mw = dpp_quad_max(static_cast<float>(Mv));
             const double Ww = dpp_quad_sum((Pu > 0.0) ? Pu * exp_nonpos_f64((Mv - Mw) * a.invT64) : 0.0);
             const unsigned pay[4] = {hi32(Ww), lo32(Ww), hi32(Mw), lo32(Mw)};
-            publish_quads(slots, pay, s.epoch, s.q, SH::kW, nq);
+            publish_quads(slots, pay, s.epoch, s.q * (SH::kW / kQuad) + j * (kLanes / kQuad), kLanes, nq);
         }
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
@@ -1482,7 +1489,7 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
         const float* prow = tbase + size_t(v) * a.V;
         auto emit = [&](int y, double py) { emit_tree(a, s, depth, tested, y, py); };
         if (m == 0) {   // a leaf: the bonus draw from p_v
-            bonus_core<kVec4>(a, s, prow, depth, slot(ex++), xp, xq, sh, counted, emit);
+            bonus_core<kVec4, true>(a, s, prow, depth, slot(ex++), xp, xq, sh, counted, emit);
             return;
         }
         const float* qrow = dbase + size_t(v) * a.V;
@@ -1499,7 +1506,7 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
         r.node_idx = static_cast<long long>(b * N + depth);
         r.node = c1;
         RowStats st;
-        const unsigned res = level_core<kVec4>(a, s, r, xp, xq, st, sh, counted);
+        const unsigned res = level_core<kVec4, true>(a, s, r, xp, xq, st, sh, counted);
         tested |= 1u << c1;
         if (res & kResError) {
             flag_error(a, s);
