@@ -63,6 +63,7 @@ constexpr int kMaxBranch = 4;              // tree: children per node
 constexpr int kTreeEx = 24;                // tree: exchanges per sequence (levels, passes, the draw)
 constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this probability share use fp64
 constexpr unsigned kSpinLimit = 1u << 20;
+constexpr int kMaxLevels = 16;             // decision slots per sequence (k <= 15)
 
 enum : unsigned { kCtlEpoch = 0, kCtlDone = 1, kCtlError = 2 };
 
@@ -85,6 +86,8 @@ struct RejectArgs {
     const int32_t* parents;            // tree: [B][k] parent of node n at [n-1]; null for a chain
     int32_t* out_nodes;                // tree: [B][k] accepted node indices, or null
     unsigned long long* tree_slots;    // tree: [B][kTreeEx][kSampSlots][U], one block per exchange
+    unsigned long long* dec_slots;     // level-parallel: [B][kMaxLevels] each level's decision
+    unsigned long long* bonus_slots;   // level-parallel: [B][4][U] the bonus row's exchange
     int B, k, V, U, Q, groups;
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
@@ -96,7 +99,7 @@ struct RejectArgs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RejectLayout {
-    size_t ctl, stat, samp, total;
+    size_t ctl, stat, samp, dec, bonus, total;
 };
 
 RejectLayout reject_layout(int B, int k, int U) {
@@ -105,6 +108,8 @@ RejectLayout reject_layout(int B, int k, int U) {
     L.ctl = o;  o = align256(o + 4 * sizeof(unsigned));
     L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * U * kStatSlots);
     L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * kSampSlots);
+    L.dec = o;  o = align256(o + sizeof(unsigned long long) * size_t(B) * kMaxLevels);
+    L.bonus = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * 4);
     L.total = o;
     return L;
 }
@@ -613,6 +618,8 @@ struct LevelRes {
     unsigned flags;
     float Mp, Mq;
     double Zp, Zq;
+    int tok;              // the candidate, its probability and min(1, p/q), for outputs written later
+    float pd, ratio;
 };
 struct SampRes {
     int owner;         // wavefront holding the crossing unit, -1 if in another workgroup
@@ -631,7 +638,8 @@ struct SharedT {
 using Shared = SharedT<kUnitWaves>;
 
 enum : unsigned { kResAccepted = 1u, kResError = 2u };
-enum : unsigned { kSampUseP = 1u, kSampExact = 2u, kSampError = 4u };
+enum : unsigned { kSampUseP = 1u, kSampExact = 2u, kSampError = 4u, kSampAbort = 8u };
+enum : unsigned { kDecRejected = 1u, kDecAccepted = 2u };   // payloads of the decision slots
 
 __device__ __forceinline__ void flag_error(const RejectArgs& a, const SeqCtx& s) {
     if (s.wave == 0 && lane_id() == 0) {
@@ -816,6 +824,7 @@ template <typename SH>
 __device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, const SH& sh, bool& use_p,
                                           bool& exact, double& run, double& t, double& Z1, double& Z2) {
     const unsigned flags = static_cast<unsigned>(uniform(static_cast<int>(sh.samp.flags)));
+    if (flags & kSampAbort) return false;   // the row is not reached: another level draws
     if (flags & kSampError) {
         flag_error(a, s);
         return false;
@@ -931,13 +940,15 @@ struct LevelRef {
     size_t acc_idx, out_idx;      // accept_probs index; out_tokens / out_probs index
     long long node_idx;           // out_nodes index (tree), -1: none
     int node;
+    bool defer;                   // leave the outputs to the caller (the level may not be reached)
 };
 
 // Acceptance test of one candidate from the combined statistics and its two
 // logits (loaded while the group was exchanging statistics); workgroup 0 writes
 // the outputs of the test.
 __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s, const LevelRef& r,
-                                            const RowStats& st, const TokenLogits& tl) {
+                                            const RowStats& st, const TokenLogits& tl, float& pd_out,
+                                            float& ratio_out) {
     double ep = 0.0, eq = 0.0;   // p and q of the token times Z_p and Z_q
     if (tl.ok) {
         ep = exp_nonpos_f64((static_cast<double>(tl.zp) - st.Mp) * a.invT64);
@@ -946,9 +957,11 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
     // u < p/q without a division on the way to the decision: u q Z_p Z_q < p Z_p Z_q.
     // (q = 0 makes the ratio +inf when p > 0 and 0 when p = 0, as the product form does.)
     const bool accepted = uniform(static_cast<int>(tl.u_acc * (eq * st.Zp) < ep * st.Zq)) != 0;
-    if (s.q == 0 && lane_id() == 0) {
-        const double p_d = ep / st.Zp, q_d = eq / st.Zq;
-        const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
+    const double p_d = ep / st.Zp, q_d = eq / st.Zq;
+    const double ratio = (q_d > 0.0) ? p_d / q_d : (p_d > 0.0 ? INFINITY : 0.0);
+    pd_out = static_cast<float>(p_d);
+    ratio_out = static_cast<float>(fmin(1.0, ratio));
+    if (!r.defer && s.q == 0 && lane_id() == 0) {
         if (a.accept_probs) a.accept_probs[r.acc_idx] = static_cast<float>(fmin(1.0, ratio));
         if (accepted) {
             a.out_tokens[r.out_idx] = tl.tok;
@@ -1030,6 +1043,7 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
         stream_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + r.pos, r.stream, &tl.u_acc, &u_smp);
         unsigned v[kStatSlots];
         unsigned flags = 0;
+        float pd = 0.0f, ratio = 0.0f;
         if (gather<kStatSlots>(r.slots, nq, s.epoch, v)) {
             count_group(a, s, counted);
             tl.zp = uniform(ztp);
@@ -1039,14 +1053,14 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
                          a.invT64, st.Mp, st.Zp);
             combine_pair(have ? __builtin_bit_cast(float, v[1]) : -INFINITY, have ? join64(v[4], v[5]) : 0.0,
                          a.invT64, st.Mq, st.Zq);
-            if (accept_test(a, s, r, st, tl)) flags |= kResAccepted;
+            if (accept_test(a, s, r, st, tl, pd, ratio)) flags |= kResAccepted;
         } else {
             count_group(a, s, counted);
             st.Mp = st.Mq = 0.0f;
             st.Zp = st.Zq = 1.0;
             flags |= kResError;
         }
-        if (lane == 0) sh.res = LevelRes{flags, st.Mp, st.Mq, st.Zp, st.Zq};
+        if (lane == 0) sh.res = LevelRes{flags, st.Mp, st.Mq, st.Zp, st.Zq, tl.tok, pd, ratio};
     }
     __syncthreads();
     st.Mp = uniform(sh.res.Mp);
@@ -1059,7 +1073,8 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
 // Level `row` of the chain (rows p_row and q_row, draft row, position L + 1 + row).
 template <bool kVec4, typename SH>
 __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx& s, int row, f4 (&xp)[kVecs],
-                                               f4 (&xq)[kVecs], RowStats& st, SH& sh, bool& counted) {
+                                               f4 (&xq)[kVecs], RowStats& st, SH& sh, bool& counted,
+                                               bool defer = false) {
     LevelRef r;
     r.prow = s.prow_base + size_t(row) * a.V;
     r.qrow = s.qrow_base + size_t(row) * a.V;
@@ -1071,6 +1086,7 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
     r.out_idx = s.tb + row;
     r.node_idx = -1;
     r.node = 0;
+    r.defer = defer;
     return level_core<kVec4>(a, s, r, xp, xq, st, sh, counted);
 }
 
@@ -1079,10 +1095,13 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
 // unit's own normaliser, a superset of the row's heavy set); wave 0 rescales its
 // units to the workgroup maximum and publishes (sum, maximum); the gathered pairs
 // are rescaled to the row maximum M, which also gives the row's Z.
+// With gate_dec, the row is drawn only if the decisions of levels 0 .. gate_levels - 1
+// (published by other groups) all accept; otherwise the call returns without output.
 template <bool kVec4, bool kSeq = false, typename SH, typename E>
 __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s, const float* prow, int pos,
                                            unsigned long long* slots, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
-                                           SH& sh, bool& counted, E&& emit) {
+                                           SH& sh, bool& counted, E&& emit,
+                                           unsigned long long* gate_dec = nullptr, int gate_levels = 0) {
     const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, a.V);
     load_unit<kVec4, false>(rp, rp, a.V, s.u, xp, xq);
     float m = -INFINITY;
@@ -1128,8 +1147,14 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[4];
-        const bool ok = gather<4>(slots, nq, s.epoch, v);
+        bool ok = gather<4>(slots, nq, s.epoch, v);
         count_group(a, s, counted);
+        bool reached = true;
+        if (gate_dec) {
+            unsigned dv[1];
+            ok = gather_at<1>(gate_dec, 1, 0, gate_levels, s.epoch, dv) && ok;
+            reached = __all(lane >= gate_levels || dv[0] == kDecAccepted);
+        }
         const bool have = lane < nq;
         const double Wg = have ? join64(v[0], v[1]) : 0.0;
         const double Mg = have ? join64(v[2], v[3]) : -INFINITY;
@@ -1154,7 +1179,7 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
         }
         if (lane == 0) {
             sh.samp.owner = owner;
-            sh.samp.flags = (exact ? kSampExact : 0u) | (ok ? 0u : kSampError);
+            sh.samp.flags = (exact ? kSampExact : 0u) | (ok ? 0u : kSampError) | (ok && !reached ? kSampAbort : 0u);
             sh.samp.run = run;
             sh.samp.t = t;
             sh.samp.Z1 = Z;
@@ -1505,6 +1530,7 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
         r.out_idx = b * (N + 1) + depth;
         r.node_idx = static_cast<long long>(b * N + depth);
         r.node = c1;
+        r.defer = false;
         RowStats st;
         const unsigned res = level_core<kVec4, true>(a, s, r, xp, xq, st, sh, counted);
         tested |= 1u << c1;
@@ -1668,6 +1694,83 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
 }
 
+// Small batches, k >= 1: the levels of a sequence run at once instead of one after
+// another, each on a group of its own (group g: sequence g / (k + 1), level
+// g % (k + 1); level k is the bonus row). Every group computes its row pair's
+// statistics and takes its acceptance test exactly as the chain does, then
+// publishes the decision; a level drawn from is the first rejected one, or the
+// bonus row if none is, and only the group of that level samples. The other groups
+// of levels past the first rejection finish without output. Rows after the first
+// rejection are read, which the chain avoids, but at these batch sizes the device
+// is far from its bandwidth and the serial exchanges are what cost. The arithmetic
+// of every level is the chain's, so the outputs are the same bits.
+template <bool kVec4, int W>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_levels_kernel(
+    RejectArgs a) {
+    const int w = blockIdx.x;
+    const int group = w / a.Q, q = w % a.Q;
+    const int b = group / (a.k + 1), j = group % (a.k + 1);
+    SeqCtx s;
+    s.q = q;
+    s.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    s.u = q * W + s.wave;
+    {
+        const unsigned last = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.epoch = (last + 1u == 0u) ? 1u : last + 1u;
+    }
+    bool counted = q != 0;   // workgroup 0's wave 0 counts the group
+    __shared__ SharedT<W> sh;
+    __shared__ int s_reached;
+    f4 xp[kVecs], xq[kVecs];
+    s.b = b;
+    s.kb = a.k;
+    s.db = size_t(b) * a.k;
+    s.tb = size_t(b) * (a.k + 1);
+    s.prow_base = a.target + s.tb * a.V;
+    s.qrow_base = a.draft + s.db * a.V;
+    s.sid = load_uniform(a.seq_ids, b);
+    s.L = load_uniform(a.seq_lens, b);
+    unsigned long long* dec = a.dec_slots + size_t(b) * kMaxLevels;
+    const int lane = lane_id();
+    if (j == a.k) {   // the bonus row, drawn if every level accepts
+        bonus_core<kVec4>(a, s, s.prow_base + size_t(j) * a.V, j, a.bonus_slots + size_t(b) * a.U * 4, xp, xq, sh,
+                          counted, [&](int y, double py) { emit_chain(a, s, j, y, py); }, dec, a.k);
+        return;
+    }
+    RowStats st;
+    const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, sh, counted, true);
+    const int tok = uniform(sh.res.tok);
+    const float pd = uniform(sh.res.pd), ratio = uniform(sh.res.ratio);
+    if (res & kResError) {
+        flag_error(a, s);
+        return;
+    }
+    const bool accepted = (res & kResAccepted) != 0;
+    if (s.q == 0 && s.wave == 0 && lane == 0)
+        slot_store(dec + j, accepted ? kDecAccepted : kDecRejected, s.epoch);
+    if (s.wave == 0) {   // is this level reached: did every earlier level accept?
+        unsigned dv[1];
+        const bool ok = gather_at<1>(dec, 1, 0, j, s.epoch, dv);
+        const bool reached = __all(lane >= j || dv[0] == kDecAccepted);
+        if (lane == 0) s_reached = ok ? (reached ? 1 : 0) : -1;
+    }
+    __syncthreads();
+    const int reached = uniform(s_reached);
+    if (reached < 0) {
+        flag_error(a, s);
+        return;
+    }
+    if (!reached) return;   // an earlier level rejected: this one is never tested
+    if (s.q == 0 && s.wave == 0 && lane == 0) {   // the outputs the chain writes at this level
+        if (a.accept_probs) a.accept_probs[s.db + j] = ratio;
+        if (accepted) {
+            a.out_tokens[s.tb + j] = tok;
+            if (a.out_probs) a.out_probs[s.tb + j] = pd;
+        }
+    }
+    if (!accepted) sample_row<kVec4>(a, s, j, xp, xq, st, sh);
+}
+
 // Workgroups of the kernel the device holds at once, and its CU count.
 template <bool kVec4, bool kTree, int W>
 hipError_t co_resident(int dev, int* wgs, int* cus_out) {
@@ -1715,6 +1818,15 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The level-parallel kernel: B (k + 1) groups of Q four-wavefront workgroups, at
+// most one workgroup per CU (the caller checks that they fit).
+template <bool kVec4>
+hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
+    a.groups = a.B * (a.k + 1);
+    hipLaunchKernelGGL((reject_levels_kernel<kVec4, 4>), dim3(a.groups * a.Q), dim3(4 * kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
 // CUs of the current device (0 if it cannot be read).
 int device_cus() {
     static int memo[64];
@@ -1749,9 +1861,13 @@ int reject_max_vocab() { return kUnit * 256; }
 
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
-    // Four-wave workgroups when each of them can have a CU to itself, else eight.
+    // The levels of each sequence at once when all of them fit one workgroup per CU
+    // (uniform k >= 1); else the chain, with four-wave workgroups when each can have a
+    // CU to itself, eight otherwise.
     const int cus = device_cus();
-    const int W = (cus > 0 && static_cast<long long>(p.B) * groups_of(p.V, 4) <= cus) ? 4 : 8;
+    const long long q4 = groups_of(p.V, 4);
+    const bool levels = !p.cu_drafts && p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= cus;
+    const int W = (levels || (cus > 0 && static_cast<long long>(p.B) * q4 <= cus)) ? 4 : 8;
     const int Q = groups_of(p.V, W);
     if (Q > kMaxQ) return hipErrorInvalidValue;
     const RejectLayout lay = reject_layout(p.B, p.k, U);
@@ -1770,6 +1886,8 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.ctl = reinterpret_cast<unsigned*>(ws + lay.ctl);
     a.stat_slots = reinterpret_cast<unsigned long long*>(ws + lay.stat);
     a.samp_slots = reinterpret_cast<unsigned long long*>(ws + lay.samp);
+    a.dec_slots = reinterpret_cast<unsigned long long*>(ws + lay.dec);
+    a.bonus_slots = reinterpret_cast<unsigned long long*>(ws + lay.bonus);
     a.parents = nullptr;
     a.out_nodes = nullptr;
     a.tree_slots = nullptr;
@@ -1779,6 +1897,7 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.T = p.temperature;
     a.seed = p.seed;
+    if (levels) return (p.V % 4) == 0 ? launch_levels<true>(a, stream) : launch_levels<false>(a, stream);
     if (W == 4)
         return (p.V % 4) == 0 ? launch_variant<true, false, 4>(a, stream) : launch_variant<false, false, 4>(a, stream);
     return (p.V % 4) == 0 ? launch_variant<true, false, 8>(a, stream) : launch_variant<false, false, 8>(a, stream);
@@ -1811,6 +1930,8 @@ hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
     a.ctl = reinterpret_cast<unsigned*>(ws);
     a.stat_slots = nullptr;
     a.samp_slots = nullptr;
+    a.dec_slots = nullptr;
+    a.bonus_slots = nullptr;
     a.parents = p.parents;
     a.out_nodes = p.out_nodes;
     a.tree_slots = reinterpret_cast<unsigned long long*>(ws + align256(4 * sizeof(unsigned)));
