@@ -1818,10 +1818,19 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The level-parallel kernel: B (k + 1) groups of Q four-wavefront workgroups, at
-// most one workgroup per CU (the caller checks that they fit).
+// The level-parallel kernel: B (k + 1) groups of Q four-wavefront workgroups, all
+// resident at once (the groups wait for each other's decisions). If the device
+// would not hold them all, the chain with the same workgroups runs instead (the
+// same bits).
 template <bool kVec4>
 hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int wgs = 0, cus = 0;   // the four-wave chain kernel has the same registers and LDS
+    e = co_resident<kVec4, false, 4>(dev, &wgs, &cus);
+    if (e != hipSuccess) return e;
+    if (static_cast<long long>(a.B) * (a.k + 1) * a.Q > wgs) return launch_variant<kVec4, false, 4>(a, stream);
     a.groups = a.B * (a.k + 1);
     hipLaunchKernelGGL((reject_levels_kernel<kVec4, 4>), dim3(a.groups * a.Q), dim3(4 * kWave), 0, stream, a);
     return hipGetLastError();
@@ -1863,7 +1872,9 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
     // The levels of each sequence at once when all of them fit one workgroup per CU
     // (uniform k >= 1); else the chain, with four-wave workgroups when each can have a
-    // CU to itself, eight otherwise.
+    // CU to itself, eight otherwise. (Two workgroups per CU made the 8B rows at B = 16
+    // faster but the long-tail shape, k = 7 with few acceptances, slower: all its
+    // levels are computed where the chain mostly stops at the first.)
     const int cus = device_cus();
     const long long q4 = groups_of(p.V, 4);
     const bool levels = !p.cu_drafts && p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= cus;
