@@ -1,0 +1,47 @@
+"""Host-side accounting of bench.py: the algorithmic bytes and flops its roofline
+figures divide by, checked against counts made element by element on tiny shapes."""
+
+import dataclasses
+
+import numpy as np
+
+import bench
+from workloads import PRESETS
+
+
+def _tiny(**kw):
+    return dataclasses.replace(PRESETS["tiny"], **kw)
+
+
+def test_attention_flops_count_every_visible_key():
+    p = _tiny(B=3, k=2, Hq=4, Hkv=2, D=64)
+    L = np.array([5, 0, 17])
+    want = 0
+    for b in range(p.B):
+        for i in range(p.k + 1):            # row i sees keys 0 .. L_b + i
+            want += p.Hq * 4 * p.D * (L[b] + i + 1)
+    assert bench.attention_flops(p, L) == want
+
+
+def test_algorithmic_bytes_read_each_examined_row_once():
+    p = _tiny(B=2, k=3, V=10, Hq=4, Hkv=2, D=64, block_size=16)
+    L = np.array([20, 3])
+    a = np.array([1, 3])                    # accepted drafts
+    attn, rej, commit = bench.algorithmic_bytes(p, L, a)
+    n_keys = L + p.k + 1
+    kv = int(np.sum(n_keys)) * p.Hkv * p.D * 2 * 2
+    qo = 2 * p.B * (p.k + 1) * p.Hq * p.D * 2
+    bt = int(np.sum((n_keys + p.block_size - 1) // p.block_size)) * 4 + p.B * 4
+    assert attn == kv + qo + bt
+    # sequence 0 rejects at level 1: p_0, p_1, q_0, q_1; sequence 1 accepts all: p_0..p_3, q_0..q_2
+    rows = (2 + 2) + (4 + 3)
+    small = p.B * p.k * 4 + p.B * (8 + 4) + p.B * (p.k + 1) * 8 + p.B * 4 + p.B * p.k * 4
+    assert rej == rows * p.V * 4 + small
+    assert commit == p.B * 4 * 3
+
+
+def test_dense_figure_counts_all_rows():
+    p = PRESETS["8b"]
+    d = bench.dense_reject_figure(p, 1e-3)
+    assert d["bytes"] == p.B * (2 * p.k + 1) * p.V * 4
+    assert abs(d["gbs"] - d["bytes"] / 1e-3 / 1e9) < 1e-6
