@@ -65,7 +65,8 @@ constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this pro
 constexpr unsigned kSpinLimit = 1u << 20;
 constexpr int kMaxLevels = 16;             // decision slots per sequence (k <= 15)
 
-enum : unsigned { kCtlEpoch = 0, kCtlDone = 1, kCtlError = 2 };
+enum : unsigned { kCtlEpoch = 0, kCtlDone = 1, kCtlError = 2, kCtlQueue = 3, kCtlFinished = 4 };
+constexpr int kMaxGroups = 1024;           // groups of one launch (the device holds at most 512 workgroups)
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -88,6 +89,7 @@ struct RejectArgs {
     unsigned long long* tree_slots;    // tree: [B][kTreeEx][kSampSlots][U], one block per exchange
     unsigned long long* dec_slots;     // level-parallel: [B][kMaxLevels] each level's decision
     unsigned long long* bonus_slots;   // level-parallel: [B][4][U] the bonus row's exchange
+    unsigned long long* next_slots;    // chain: [kMaxGroups] each group's next sequence
     int B, k, V, U, Q, groups;
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
@@ -99,17 +101,18 @@ struct RejectArgs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RejectLayout {
-    size_t ctl, stat, samp, dec, bonus, total;
+    size_t ctl, stat, samp, dec, bonus, next, total;
 };
 
 RejectLayout reject_layout(int B, int k, int U) {
     RejectLayout L;
     size_t o = 0;
-    L.ctl = o;  o = align256(o + 4 * sizeof(unsigned));
+    L.ctl = o;  o = align256(o + 8 * sizeof(unsigned));
     L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * U * kStatSlots);
     L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * kSampSlots);
     L.dec = o;  o = align256(o + sizeof(unsigned long long) * size_t(B) * kMaxLevels);
     L.bonus = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * 4);
+    L.next = o; o = align256(o + sizeof(unsigned long long) * kMaxGroups);
     L.total = o;
     return L;
 }
@@ -632,6 +635,7 @@ struct SharedT {
     LoadSums ls[W];
     UnitStat unit[W];
     double4 usum[W];
+    int next;             // the group's next sequence
     LevelRes res;
     SampRes samp;
 };
@@ -1660,7 +1664,15 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     bool counted = q != 0;   // workgroup 0's wave 0 counts the group
     __shared__ SharedT<W> sh;
     f4 xp[kVecs], xq[kVecs];
-    for (int b = group; b < a.B; b += a.groups) {
+    // Sequence g first; the sequences past the first `groups` go to the groups as
+    // they finish (a sequence's chain takes one to four levels, so a fixed share
+    // could pair two long chains): wave 0 of a group's workgroup 0 takes a ticket
+    // from a call-wide counter and publishes the group's next sequence in its slot,
+    // tagged with the call's epoch and the round; the group's other workgroups read
+    // it there. The last group to finish resets the counters for the next call.
+    const bool queued = a.B > a.groups;
+    int b = group;
+    for (int round = 1; b < a.B; ++round) {
         s.b = b;
         if (a.cu) {   // ragged: k_b drafts, rows packed by the offsets
             const int c0 = load_uniform(a.cu, b), c1 = load_uniform(a.cu, size_t(b) + 1);
@@ -1689,8 +1701,46 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                 done = true;
             }
         }
-        if (done) continue;
-        bonus_row<kVec4>(a, s, xp, xq, sh, counted);
+        if (!done) bonus_row<kVec4>(a, s, xp, xq, sh, counted);
+        if (!queued) break;
+        if (s.wave == 0) {
+            const int lane = lane_id();
+            unsigned long long* slot = a.next_slots + group;
+            int nb = -1;
+            if (q == 0) {
+                unsigned t = 0;
+                if (lane == 0) t = __hip_atomic_fetch_add(a.ctl + kCtlQueue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                t = static_cast<unsigned>(uniform(static_cast<int>(t)));
+                nb = (static_cast<long long>(a.groups) + t < a.B) ? a.groups + static_cast<int>(t) : a.B;
+                if (lane == 0) slot_store(slot, (static_cast<unsigned>(round) << 16) | static_cast<unsigned>(nb), s.epoch);
+            } else {
+                for (unsigned it = 0; it < kSpinLimit; ++it) {
+                    const unsigned long long v = slot_load(slot);
+                    const unsigned pay = static_cast<unsigned>(v >> 32);
+                    if (static_cast<unsigned>(v) == s.epoch && (pay >> 16) == static_cast<unsigned>(round)) {
+                        nb = static_cast<int>(pay & 0xFFFFu);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(4);
+                }
+                nb = uniform(nb);
+            }
+            if (lane == 0) sh.next = nb;
+        }
+        __syncthreads();
+        b = uniform(sh.next);
+        if (b < 0) {   // the wait ran out (only if the group were not resident at once)
+            if (s.wave == 0 && lane_id() == 0)
+                __hip_atomic_fetch_or(a.ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+    if (queued && q == 0 && s.wave == 0 && lane_id() == 0) {
+        const unsigned f = __hip_atomic_fetch_add(a.ctl + kCtlFinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (f + 1 == static_cast<unsigned>(a.groups)) {   // every group has taken its last ticket
+            __hip_atomic_store(a.ctl + kCtlQueue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ctl + kCtlFinished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -1899,6 +1949,7 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.samp_slots = reinterpret_cast<unsigned long long*>(ws + lay.samp);
     a.dec_slots = reinterpret_cast<unsigned long long*>(ws + lay.dec);
     a.bonus_slots = reinterpret_cast<unsigned long long*>(ws + lay.bonus);
+    a.next_slots = reinterpret_cast<unsigned long long*>(ws + lay.next);
     a.parents = nullptr;
     a.out_nodes = nullptr;
     a.tree_slots = nullptr;
@@ -1943,6 +1994,7 @@ hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
     a.samp_slots = nullptr;
     a.dec_slots = nullptr;
     a.bonus_slots = nullptr;
+    a.next_slots = nullptr;
     a.parents = p.parents;
     a.out_nodes = p.out_nodes;
     a.tree_slots = reinterpret_cast<unsigned long long*>(ws + align256(4 * sizeof(unsigned)));
