@@ -1791,13 +1791,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, sh, counted, true);
     const int tok = uniform(sh.res.tok);
     const float pd = uniform(sh.res.pd), ratio = uniform(sh.res.ratio);
+    const bool accepted = (res & kResAccepted) != 0;   // false on an error
+    if (s.q == 0 && s.wave == 0 && lane == 0)           // published even on an error, so later levels stop
+        slot_store(dec + j, accepted ? kDecAccepted : kDecRejected, s.epoch);
     if (res & kResError) {
         flag_error(a, s);
         return;
     }
-    const bool accepted = (res & kResAccepted) != 0;
-    if (s.q == 0 && s.wave == 0 && lane == 0)
-        slot_store(dec + j, accepted ? kDecAccepted : kDecRejected, s.epoch);
     if (s.wave == 0) {   // is this level reached: did every earlier level accept?
         unsigned dv[1];
         const bool ok = gather_at<1>(dec, 1, 0, j, s.epoch, dv);
