@@ -816,6 +816,7 @@ def gpu_bench(args) -> dict:
     a_flops = attention_flops(p, np.asarray(seq_lens0.cpu()))
     mean = lambda v: sum(v) / len(v)
     med = lambda v: sorted(v)[len(v) // 2]
+    pct = lambda v, f: sorted(v)[min(len(v) - 1, int(f * len(v)))]   # p10 / p90 of the sampled calls
     attn_avg_s = mean(attn_ms) / 1e3
     rej_avg_s = mean(rej_ms) / 1e3
     com_avg_s = mean(com_ms) / 1e3
@@ -839,11 +840,13 @@ def gpu_bench(args) -> dict:
         mean_emitted_per_sequence=tokens / B,
         step_gbs=(a_bytes + r_bytes + c_bytes) / step_s / 1e9,
         kernels=dict(
-            verify_attn=dict(avg_us=attn_avg_s * 1e6, median_us=med(attn_ms) * 1e3, bytes=a_bytes, gbs=attn_gbs,
+            verify_attn=dict(avg_us=attn_avg_s * 1e6, median_us=med(attn_ms) * 1e3,
+                             p10_us=pct(attn_ms, 0.1) * 1e3, p90_us=pct(attn_ms, 0.9) * 1e3, bytes=a_bytes, gbs=attn_gbs,
                              frac_of_peak=attn_gbs / HBM_PEAK_GBS,
                              mfma=dict(algorithmic_flops=a_flops, tflops=a_flops / attn_avg_s / 1e12,
                                        frac_of_bf16_peak=a_flops / attn_avg_s / 1e12 / MFMA_PEAK_BF16_TFLOPS)),
-            reject_sample=dict(avg_us=rej_avg_s * 1e6, median_us=med(rej_ms) * 1e3, bytes=r_bytes, gbs=rej_gbs,
+            reject_sample=dict(avg_us=rej_avg_s * 1e6, median_us=med(rej_ms) * 1e3,
+                               p10_us=pct(rej_ms, 0.1) * 1e3, p90_us=pct(rej_ms, 0.9) * 1e3, bytes=r_bytes, gbs=rej_gbs,
                                frac_of_peak=rej_gbs / HBM_PEAK_GBS,
                                dense_equivalent=dense_reject_figure(p, rej_avg_s)),
             commit_lengths=dict(avg_us=com_avg_s * 1e6, bytes=c_bytes)),
