@@ -612,7 +612,7 @@ struct TokenLogits {
 };
 
 // Workgroup-shared state: per-wavefront partials going to wave 0, and wave 0's
-// results going back to all eight wavefronts.
+// results going back to all of the workgroup's wavefronts.
 struct UnitStat {
     float Mp, Mq;
     double Zp, Zq;
@@ -845,9 +845,9 @@ __device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, 
 
 // Sampling from the residual of row `row` after its draft was rejected; `st`
 // holds the chain statistics of that row. Each wavefront turns its unit (still in
-// registers) into weights; wave 0 sums the workgroup's units, one exchange gives
-// it every workgroup's sums, it finds the crossing workgroup and, if that is its
-// own, the crossing unit, whose wavefront then scans it for the token.
+// registers) into weights; wave 0 sums the workgroup's units by quads, one
+// exchange gives it every quad's sums, it finds the crossing quad and, if that is
+// its workgroup's, the crossing unit, whose wavefront then scans it for the token.
 template <bool kVec4, typename SH>
 __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s, int row, const f4 (&xp)[kVecs],
                                            const f4 (&xq)[kVecs], const RowStats& st, SH& sh) {
@@ -977,10 +977,11 @@ __device__ __forceinline__ bool accept_test(const RejectArgs& a, const SeqCtx& s
 }
 
 // Level `row` of the chain (rows p_row and q_row): every wavefront reduces its
-// unit, wave 0 combines the workgroup's eight, publishes the pair and gathers the
-// group's, combines those in workgroup order and takes the acceptance test; every
-// workgroup reaches the same decision from the same bits. Returns the result flags
-// (kResAccepted, kResError) and the row's statistics in `st`.
+// unit, wave 0 combines the workgroup's units by quads, publishes one pair per quad
+// and gathers the sequence's quads, combines those in quad order and takes the
+// acceptance test; every workgroup reaches the same decision from the same bits.
+// Returns the result flags (kResAccepted, kResError) and the row's statistics in
+// `st`; with r.defer the outputs of the test are left in sh.res for the caller.
 // kSeq: the workgroup's quads one after another in lanes 0..3 instead of all at
 // once (the same bits; it leaves the tree walk, which is short of registers, with
 // fewer spills).
@@ -1097,8 +1098,8 @@ __device__ __forceinline__ unsigned level_step(const RejectArgs& a, const SeqCtx
 // The bonus row p_k after k acceptances, with one exchange: each wavefront weighs
 // its unit against the unit's own maximum M_u (heavy logits judged with the
 // unit's own normaliser, a superset of the row's heavy set); wave 0 rescales its
-// units to the workgroup maximum and publishes (sum, maximum); the gathered pairs
-// are rescaled to the row maximum M, which also gives the row's Z.
+// units to each quad's maximum and publishes (sum, maximum) per quad; the gathered
+// pairs are rescaled to the row maximum M, which also gives the row's Z.
 // With gate_dec, the row is drawn only if the decisions of levels 0 .. gate_levels - 1
 // (published by other groups) all accept; otherwise the call returns without output.
 template <bool kVec4, bool kSeq = false, typename SH, typename E>
