@@ -1747,7 +1747,8 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
 
 // Small batches, k >= 1: the levels of a sequence run at once instead of one after
 // another, each on a group of its own (group g: sequence g / (k + 1), level
-// g % (k + 1); level k is the bonus row). Every group computes its row pair's
+// g % (k + 1); level k_b is the bonus row, and with ragged draft lengths the
+// groups past a sequence's k_b only count themselves). Every group computes its row pair's
 // statistics and takes its acceptance test exactly as the chain does, then
 // publishes the decision; a level drawn from is the first rejected one, or the
 // bonus row if none is, and only the group of that level samples. The other groups
@@ -1774,18 +1775,29 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     __shared__ int s_reached;
     f4 xp[kVecs], xq[kVecs];
     s.b = b;
-    s.kb = a.k;
-    s.db = size_t(b) * a.k;
-    s.tb = size_t(b) * (a.k + 1);
+    if (a.cu) {   // ragged: k_b drafts, rows packed by the offsets (groups j > k_b have no level)
+        const int c0 = load_uniform(a.cu, b), c1 = load_uniform(a.cu, size_t(b) + 1);
+        s.kb = min(max(c1 - c0, 0), a.k);
+        s.db = static_cast<size_t>(c0);
+        s.tb = static_cast<size_t>(c0) + b;
+    } else {
+        s.kb = a.k;
+        s.db = size_t(b) * a.k;
+        s.tb = size_t(b) * (a.k + 1);
+    }
     s.prow_base = a.target + s.tb * a.V;
     s.qrow_base = a.draft + s.db * a.V;
     s.sid = load_uniform(a.seq_ids, b);
     s.L = load_uniform(a.seq_lens, b);
     unsigned long long* dec = a.dec_slots + size_t(b) * kMaxLevels;
     const int lane = lane_id();
-    if (j == a.k) {   // the bonus row, drawn if every level accepts
+    if (j > s.kb) {   // past this sequence's drafts: nothing to do but be counted
+        if (s.wave == 0) count_group(a, s, counted);
+        return;
+    }
+    if (j == s.kb) {   // the bonus row, drawn if every level accepts
         bonus_core<kVec4>(a, s, s.prow_base + size_t(j) * a.V, j, a.bonus_slots + size_t(b) * a.U * 4, xp, xq, sh,
-                          counted, [&](int y, double py) { emit_chain(a, s, j, y, py); }, dec, a.k);
+                          counted, [&](int y, double py) { emit_chain(a, s, j, y, py); }, dec, s.kb);
         return;
     }
     RowStats st;
@@ -1922,13 +1934,13 @@ int reject_max_vocab() { return kUnit * 256; }
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
     // The levels of each sequence at once when all of them fit one workgroup per CU
-    // (uniform k >= 1); else the chain, with four-wave workgroups when each can have a
+    // (k >= 1; ragged calls take k_max + 1 groups per sequence); else the chain, with four-wave workgroups when each can have a
     // CU to itself, eight otherwise. (Two workgroups per CU made the 8B rows at B = 16
     // faster but the long-tail shape, k = 7 with few acceptances, slower: all its
     // levels are computed where the chain mostly stops at the first.)
     const int cus = device_cus();
     const long long q4 = groups_of(p.V, 4);
-    const bool levels = !p.cu_drafts && p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= cus;
+    const bool levels = p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= cus;
     const int W = (levels || (cus > 0 && static_cast<long long>(p.B) * q4 <= cus)) ? 4 : 8;
     const int Q = groups_of(p.V, W);
     if (Q > kMaxQ) return hipErrorInvalidValue;

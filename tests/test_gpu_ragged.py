@@ -208,6 +208,28 @@ def test_reject_ragged_equal_lengths_matches_uniform(device):
         np.testing.assert_array_equal(g["accept_probs"], u["accept_probs"].ravel().astype(np.float64))
 
 
+def test_reject_ragged_level_parallel_matches_full_batch(device):
+    """Four ragged sequences of the 8B rows run every level at once (the groups past a
+    sequence's k_b only count themselves); the same sequences inside a batch of 64 run
+    the chain. Their packed outputs are bit-identical."""
+    base = make_reject_inputs(PRESETS["8b"], B=64)
+    lens = np.random.default_rng(17).integers(0, base["k"] + 1, size=64).astype(np.int32)
+    lens[:4] = [3, 0, 2, 1]
+    full = RaggedRejectDevice(pack_reject_inputs(base, lens), device)
+    small = dict(base)
+    for key in ("target_logits", "draft_logits", "draft_tokens", "seq_ids", "seq_lens"):
+        small[key] = np.ascontiguousarray(base[key][:4])
+    small["B"] = 4
+    part = RaggedRejectDevice(pack_reject_inputs(small, lens[:4]), device)
+    rows, drafts = int(np.sum(lens[:4] + 1)), int(np.sum(lens[:4]))
+    for seed in (2, 29, 311):
+        g, c = full.call(seed), part.call(seed)
+        np.testing.assert_array_equal(c["num_accepted"], g["num_accepted"][:4])
+        np.testing.assert_array_equal(c["out_tokens"], g["out_tokens"][:rows])
+        np.testing.assert_array_equal(c["out_probs"], g["out_probs"][:rows])
+        np.testing.assert_array_equal(c["accept_probs"], g["accept_probs"][:drafts])
+
+
 def test_reject_ragged_steps_with_commit(device):
     import torch
     import speculative_decoding_verification_14_amd as sv
