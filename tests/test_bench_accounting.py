@@ -45,3 +45,15 @@ def test_dense_figure_counts_all_rows():
     d = bench.dense_reject_figure(p, 1e-3)
     assert d["bytes"] == p.B * (2 * p.k + 1) * p.V * 4
     assert abs(d["gbs"] - d["bytes"] / 1e-3 / 1e9) < 1e-6
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """One GPU only: --gpus 2 exits with status 2 and says why, before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "exactly one GPU" in res.stderr
