@@ -1934,14 +1934,22 @@ int reject_max_vocab() { return kUnit * 256; }
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
     // The levels of each sequence at once when all of them fit one workgroup per CU
-    // (k >= 1; ragged calls take k_max + 1 groups per sequence); else the chain, with four-wave workgroups when each can have a
-    // CU to itself, eight otherwise. (Two workgroups per CU made the 8B rows at B = 16
-    // faster but the long-tail shape, k = 7 with few acceptances, slower: all its
-    // levels are computed where the chain mostly stops at the first.)
+    // (k >= 1; ragged calls take k_max + 1 groups per sequence); else the chain.
+    // (Two workgroups per CU made the 8B rows at B = 16 faster but the long-tail
+    // shape, k = 7 with few acceptances, slower: all its levels are computed where
+    // the chain mostly stops at the first.) The chain takes eight-wave workgroups
+    // only when the batch fills the device in one round of them (one per CU), and
+    // four-wave ones otherwise: when each can have a CU to itself, and when the
+    // sequences are handed out over several rounds, where two workgroups of
+    // different sequences share each CU (152K vocabulary, B = 256, inside the full
+    // step: 210 us instead of 215 us; at B = 64 the same time). The outputs do not
+    // depend on it.
     const int cus = device_cus();
-    const long long q4 = groups_of(p.V, 4);
+    const long long q4 = groups_of(p.V, 4), q8 = groups_of(p.V, 8);
     const bool levels = p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= cus;
-    const int W = (levels || (cus > 0 && static_cast<long long>(p.B) * q4 <= cus)) ? 4 : 8;
+    const bool one_round8 = static_cast<long long>(p.B) * q8 <= cus;
+    const bool own_cu4 = static_cast<long long>(p.B) * q4 <= cus;
+    const int W = (levels || own_cu4 || !one_round8) ? 4 : 8;
     const int Q = groups_of(p.V, W);
     if (Q > kMaxQ) return hipErrorInvalidValue;
     const RejectLayout lay = reject_layout(p.B, p.k, U);
