@@ -178,6 +178,27 @@ def test_batch_invariant_across_workgroup_sizes(device):
             np.testing.assert_array_equal(c[key], a[key][:32])
 
 
+def test_batch_invariant_across_queue_rounds(device):
+    """The 8B batch of 64 fills the device in one round of eight-wavefront
+    workgroups; with 32 more sequences appended (B = 96) the sequences are handed
+    out over several rounds of four-wavefront workgroups instead. The first 64
+    sequences' outputs are bit-identical either way."""
+    inp = make_reject_inputs(PRESETS["8b"], B=64)
+    extra = make_reject_inputs(PRESETS["8b"], B=32, seed=9)
+    big = dict(inp)
+    for key in ("target_logits", "draft_logits", "draft_tokens", "seq_ids", "seq_lens"):
+        big[key] = np.ascontiguousarray(np.concatenate([inp[key], extra[key]]))
+    big["seq_ids"] = np.ascontiguousarray(big["seq_ids"] + np.concatenate(
+        [np.zeros(64, np.int64), np.full(32, 1 << 40, np.int64)]))
+    big["B"] = 96
+    full = RejectDevice(inp, device)
+    queued = RejectDevice(big, device)
+    for seed in (8, 64, 4242):
+        a, c = full.call(seed), queued.call(seed)
+        for key in a:
+            np.testing.assert_array_equal(c[key][:64], a[key])
+
+
 def test_batch_invariant_across_level_parallel(device):
     """Four sequences of the 8B rows run the level-parallel kernel (every level of a
     sequence at once, each on its own group), the full batch of 64 the chain: the
