@@ -1893,9 +1893,19 @@ hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int wgs = 0, cus = 0;   // the four-wave chain kernel has the same registers and LDS
-    e = co_resident<kVec4, false, 4>(dev, &wgs, &cus);
-    if (e != hipSuccess) return e;
+    // Every group waits for the decisions of the levels before it, so all of them
+    // must be resident at once: the kernel's own occupancy decides.
+    static int memo[64];
+    int wgs = (dev >= 0 && dev < 64) ? memo[dev] : 0;
+    if (wgs <= 0) {
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_levels_kernel<kVec4, 4>, 4 * kWave, 0);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        wgs = per_cu * cus;
+        if (dev >= 0 && dev < 64) memo[dev] = wgs;
+    }
     if (static_cast<long long>(a.B) * (a.k + 1) * a.Q > wgs) return launch_variant<kVec4, false, 4>(a, stream);
     a.groups = a.B * (a.k + 1);
     hipLaunchKernelGGL((reject_levels_kernel<kVec4, 4>), dim3(a.groups * a.Q), dim3(4 * kWave), 0, stream, a);
@@ -1936,11 +1946,12 @@ int reject_max_vocab() { return kUnit * 256; }
 
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
-    // The levels of each sequence at once when all of them fit one workgroup per CU
-    // (k >= 1; ragged calls take k_max + 1 groups per sequence); else the chain.
-    // (Two workgroups per CU made the 8B rows at B = 16 faster but the long-tail
-    // shape, k = 7 with few acceptances, slower: all its levels are computed where
-    // the chain mostly stops at the first.) The chain takes eight-wave workgroups
+    // The levels of each sequence at once when all of them fit one workgroup per CU,
+    // or two per CU for drafts of at most three tokens (k >= 1; ragged calls take
+    // k_max + 1 groups per sequence); else the chain. Two per CU made the 8B rows at
+    // B = 16 (k = 3) faster but the long-tail shape, k = 7 with few acceptances,
+    // slower: all its levels are computed where the chain mostly stops at the first,
+    // and the longer the draft, the more of them go unused. The chain takes eight-wave workgroups
     // only when the batch fills the device in one round of them (one per CU), and
     // four-wave ones otherwise: when each can have a CU to itself, and when the
     // sequences are handed out over several rounds, where two workgroups of
@@ -1949,7 +1960,8 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     // depend on it.
     const int cus = device_cus();
     const long long q4 = groups_of(p.V, 4), q8 = groups_of(p.V, 8);
-    const bool levels = p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= cus;
+    const long long level_cap = static_cast<long long>(cus) * (p.k <= 3 ? 2 : 1);
+    const bool levels = p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= level_cap;
     const bool one_round8 = static_cast<long long>(p.B) * q8 <= cus;
     const bool own_cu4 = static_cast<long long>(p.B) * q4 <= cus;
     const int W = (levels || own_cu4 || !one_round8) ? 4 : 8;
