@@ -199,21 +199,23 @@ def test_batch_invariant_across_queue_rounds(device):
             np.testing.assert_array_equal(c[key][:64], a[key])
 
 
-def test_batch_invariant_across_level_parallel(device):
-    """Four sequences of the 8B rows run the level-parallel kernel (every level of a
-    sequence at once, each on its own group), the full batch of 64 the chain: the
-    outputs of those four sequences are bit-identical."""
+@pytest.mark.parametrize("n", [4, 16])
+def test_batch_invariant_across_level_parallel(device, n):
+    """The first n sequences of the 8B rows run the level-parallel kernel (every level
+    of a sequence at once, each on its own group: one workgroup per CU at n = 4, two
+    at n = 16), the full batch of 64 the chain: the outputs of those n sequences are
+    bit-identical."""
     inp = make_reject_inputs(PRESETS["8b"], B=64)
     full = RejectDevice(inp, device)
     small = dict(inp)
     for key in ("target_logits", "draft_logits", "draft_tokens", "seq_ids", "seq_lens"):
-        small[key] = np.ascontiguousarray(inp[key][:4])
-    small["B"] = 4
+        small[key] = np.ascontiguousarray(inp[key][:n])
+    small["B"] = n
     part = RejectDevice(small, device)
     for seed in (3, 41, 977, 5003):
         a, c = full.call(seed), part.call(seed)
         for key in a:
-            np.testing.assert_array_equal(c[key], a[key][:4])
+            np.testing.assert_array_equal(c[key], a[key][:n])
 
 
 def test_commit_matches_oracle(device):
