@@ -13,11 +13,13 @@
 //  * A row of V logits is cut into U units of 4096; each unit of the current row
 //    (pair) is held in the registers of one wavefront (16 x 16-byte loads per
 //    lane per row, all in flight together). W unit wavefronts form a workgroup:
-//    eight (one workgroup per CU) when the batch fills the device, four (a
-//    sequence over twice as many CUs, one workgroup on each) when B * ceil(U/4)
-//    workgroups fit one per CU, which shortens each step of a sequence's serial
-//    chain at small batches. The Q = ceil(U / W) workgroups of a sequence form a
-//    group, and groups take sequences in turn.
+//    eight (one workgroup per CU) when the batch fills the device in one round of
+//    them, four otherwise: a sequence over twice as many CUs (one workgroup on
+//    each) when B * ceil(U/4) workgroups fit one per CU, which shortens each step
+//    of a sequence's serial chain at small batches, and two workgroups of
+//    different sequences per CU when the batch takes several rounds. The
+//    Q = ceil(U / W) workgroups of a sequence form a group, and groups take
+//    sequences in turn.
 //  * Level j: every wavefront reduces its units of p_j and q_j to (max, sum of
 //    exps) with an online softmax on the DPP network; wave 0 of the workgroup
 //    combines them four at a time (quads of consecutive units) and publishes one
@@ -1637,8 +1639,9 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // W unit wavefronts per workgroup: 8 (one workgroup per CU) when the batch fills the
-// device, 4 (a sequence over twice as many CUs, one workgroup on each) when there are
-// CUs to spare, which shortens every step of a sequence's serial chain.
+// device in one round of them, 4 otherwise (a sequence over twice as many CUs when
+// there are CUs to spare, which shortens every step of a sequence's serial chain;
+// two sequences' workgroups per CU when the batch takes several rounds).
 template <bool kVec4, int W>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_kernel(RejectArgs a) {
     // Workgroups go to the eight XCDs round-robin; with a multiple of eight groups,
