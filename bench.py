@@ -58,6 +58,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 10
+EVENT_STEPS = 30    # at least this many steps with per-call events for the averages
 METRIC = "verified tokens/s + HBM GB/s (% of peak) for spec verify, 8B shape, k=3"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_counters.txt")
 LM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "lm_head_8b_counters.txt")
@@ -65,6 +66,8 @@ KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/attention.hip",
                   "speculative_decoding_verification_14_amd/csrc/common.hpp"]
 LM_KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/upstream.hip",
                      "speculative_decoding_verification_14_amd/csrc/common.hpp"]
+REJECT_KERNEL_SOURCES = [f"speculative_decoding_verification_14_amd/csrc/{f}"
+                         for f in ("reject.hip", "common.hpp", "heavy.hpp", "fastexp.hpp", "philox.hpp")]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -103,9 +106,10 @@ def dense_reject_figure(preset, seconds: float) -> dict:
     return dict(bytes=dense, gbs=gbs, frac_of_peak=gbs / HBM_PEAK_GBS)
 
 
-def stored_traffic(path=None, sources=None):
-    """HBM bytes per call of the dominant kernel from committed rocprofv3 counter runs, if still
-    valid (the file records a hash of the kernel's sources)."""
+def stored_traffic(path=None, sources=None, key="hbm_bytes_per_call"):
+    """HBM bytes per call of a kernel from committed rocprofv3 counter runs, if still valid: the
+    file records a hash of the attention kernel's sources, and of the sampling kernel's for
+    key "reject_hbm_bytes_per_call"; a value whose sources have changed since is not used."""
     path = COUNTERS_FILE if path is None else path
     if not os.path.exists(path):
         return None
@@ -113,52 +117,114 @@ def stored_traffic(path=None, sources=None):
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
-                key, _, v = line.partition(":")
-                vals[key.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if key == "reject_hbm_bytes_per_call":
+        if vals.get("reject_source_sha256_16") != kernel_source_hash(REJECT_KERNEL_SOURCES):
+            return None
+    elif vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
-        return int(float(vals["hbm_bytes_per_call"]))
+        return int(float(vals[key]))
     except (KeyError, ValueError):
         return None
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(workload: str, attn_pairs: int = 48, seed_offset: int = 0) -> dict:
-    """Oracle seconds per step, extrapolated from a bounded sample, on this process's threads."""
-    import numpy as np
+# Inputs of the CPU baseline, set before its worker pool forks (the workers read them
+# copy-on-write; the baseline runs in a child process that never touches the GPU).
+_CB: dict = {}
+
+
+def _cb_attention(pairs) -> int:
     from oracle import attention as oatt
-    from oracle import commit as ocommit
+    inp, p = _CB["inp"], _CB["p"]
+    oatt.verify_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"], p.k,
+                          p.Hq, p.Hkv, p.block_size, inp["sm_scale"], pairs=pairs)
+    return len(pairs)
+
+
+def _cb_reject(seqs) -> list:
+    import numpy as np
     from oracle import reject as orej
+    inp, p = _CB["inp"], _CB["p"]
+    idx = np.asarray(seqs, dtype=np.int64)
+    res = orej.verify_batch(inp["target_logits"][idx], inp["draft_logits"][idx], inp["draft_tokens"][idx],
+                            inp["seq_ids"][idx], inp["seq_lens"][idx], p.k, p.temperature, inp["seed"])
+    return res["num_accepted"].tolist()
+
+
+def cpu_workers() -> int:
+    """Worker processes for the pooled oracle: the cores this process may run on, at most 16
+    (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(workload: str) -> dict:
+    """The oracle on one whole step of the workload (every (sequence, KV head) pair of the
+    attention, every sequence's rejection sampling, the commit), timed two ways on this host:
+    (i) one process, one thread; (ii) a pool of worker processes, one BLAS thread each, the
+    attention split by (sequence, KV head) pair and the sampling by sequence."""
+    import multiprocessing
+
+    import numpy as np
+    from oracle import commit as ocommit
     from workloads import PRESETS, make_inputs
     p = PRESETS[workload]
     inp = make_inputs(workload)
-    rng = np.random.default_rng(1234 + seed_offset)
-    all_pairs = [(b, g) for b in range(p.B) for g in range(p.Hkv)]
-    pick = [all_pairs[i] for i in rng.choice(len(all_pairs), size=min(attn_pairs, len(all_pairs)), replace=False)]
+    _CB.update(inp=inp, p=p)
+    pairs = [(b, g) for b in range(p.B) for g in range(p.Hkv)]
+    seqs = list(range(p.B))
+    cap = inp["max_blocks"] * p.block_size
+
     t0 = time.perf_counter()
-    oatt.verify_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"], p.k,
-                          p.Hq, p.Hkv, p.block_size, inp["sm_scale"], pairs=pick)
-    t_attn_sample = time.perf_counter() - t0
-    # scale by keys covered, since pairs differ in context length
-    keys_all = float(np.sum(inp["seq_lens"].astype(np.int64) + p.k + 1)) * p.Hkv
-    keys_pick = float(sum(int(inp["seq_lens"][b]) + p.k + 1 for b, _ in pick))
-    t_attn = t_attn_sample * keys_all / keys_pick
+    _cb_attention(pairs)
+    t_attn1 = time.perf_counter() - t0
     t0 = time.perf_counter()
-    res = orej.verify_batch(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["seq_ids"],
-                            inp["seq_lens"], p.k, p.temperature, inp["seed"])
-    t_rej = time.perf_counter() - t0
+    acc1 = np.asarray(_cb_reject(seqs), dtype=np.int32)
+    t_rej1 = time.perf_counter() - t0
     t0 = time.perf_counter()
-    ocommit.commit_lengths(inp["seq_lens"], res["num_accepted"], inp["max_blocks"] * p.block_size)
-    t_commit = time.perf_counter() - t0
-    tokens = int(np.sum(res["num_accepted"] + 1))
-    total = t_attn + t_rej + t_commit
-    return dict(seconds_per_step=total, attn_seconds=t_attn, reject_seconds=t_rej, tokens_per_step=tokens,
-                tokens_per_s=tokens / total, attn_pairs=len(pick), attn_sample_seconds=t_attn_sample,
-                sample=(f"attention of {len(pick)} of {len(all_pairs)} (sequence, KV head) pairs timed and "
-                        f"scaled by key count; rejection sampling of all {p.B} sequences and the commit timed "
-                        f"in full; one step of the {workload} workload"))
+    ocommit.commit_lengths(inp["seq_lens"], acc1, cap)
+    t_com1 = time.perf_counter() - t0
+
+    n = cpu_workers()
+    # pairs in order of decreasing key count, dealt round-robin, so the shares are even
+    by_keys = sorted(pairs, key=lambda bg: -int(inp["seq_lens"][bg[0]]))
+    attn_chunks = [by_keys[i::n] for i in range(n)]
+    rej_chunks = [seqs[i::n] for i in range(n)]
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(n) as pool:
+        pool.map(_cb_reject, [[0]] * n)            # workers started and warm before timing
+        t0 = time.perf_counter()
+        pool.map(_cb_attention, attn_chunks)
+        t_attnN = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        parts = pool.map(_cb_reject, rej_chunks)
+        t_rejN = time.perf_counter() - t0
+    accN = np.zeros(p.B, dtype=np.int32)
+    for chunk, part in zip(rej_chunks, parts):
+        accN[chunk] = part
+    if not np.array_equal(acc1, accN):
+        raise RuntimeError("the pooled oracle disagrees with the single-process one")
+    t0 = time.perf_counter()
+    ocommit.commit_lengths(inp["seq_lens"], accN, cap)
+    t_comN = time.perf_counter() - t0
+    tokens = int(np.sum(acc1 + 1))
+    one = t_attn1 + t_rej1 + t_com1
+    pooled = t_attnN + t_rejN + t_comN
+    return dict(
+        tokens_per_step=tokens, workers=n,
+        single=dict(seconds_per_step=one, attn_seconds=t_attn1, reject_seconds=t_rej1, tokens_per_s=tokens / one),
+        pooled=dict(seconds_per_step=pooled, attn_seconds=t_attnN, reject_seconds=t_rejN,
+                    tokens_per_s=tokens / pooled),
+        sample=(f"one whole step of the {workload} workload: attention of all {len(pairs)} (sequence, KV head) "
+                f"pairs, rejection sampling of all {p.B} sequences, the commit; timed once in one process "
+                f"(one thread) and once over a pool of {n} worker processes (one BLAS thread each)"))
 
 
 def run_cpu_baseline_child(workload: str) -> dict | None:
@@ -273,6 +339,7 @@ def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, wri
         lines = ["# rocprofv3 hardware counters, 8b workload (B=64, k=3, V=128256), one call of each kernel per step",
                  f"# fetch command: {fetch_cmd}", f"# write command: {write_cmd}", *head,
                  f"kernel_source_sha256_16: {kernel_source_hash()}",
+                 f"reject_source_sha256_16: {kernel_source_hash(REJECT_KERNEL_SOURCES)}",
                  f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}"]
         for k in attn + rej:
             lines.append(f"{k}: FETCH_SIZE {fetch.get(k, 0.0):.1f} KiB, WRITE_SIZE {write.get(k, 0.0):.1f} KiB "
@@ -790,23 +857,28 @@ def gpu_bench(args) -> dict:
     torch.cuda.synchronize()
     acc_ref = num_acc.cpu().numpy().copy()
 
-    # Per-call HIP events on every EVENT_EVERY-th step only: each event record is a
-    # barrier packet that leaves a few-microsecond bubble in the stream.
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    # The timed steps carry no events (each event record is a barrier packet that leaves a
+    # few-microsecond bubble in the stream); the per-call times come from the same steps
+    # run again right after, with HIP events around every call of every step.
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs.get(i))
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    attn_ms = [e[0].elapsed_time(e[1]) for e in evs.values()]
-    rej_ms = [e[1].elapsed_time(e[2]) for e in evs.values()]
-    com_ms = [e[2].elapsed_time(e[3]) for e in evs.values()]
     acc = num_acc.cpu().numpy()
     if not np.array_equal(acc, acc_ref):
         raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
+    n_ev = max(args.steps, EVENT_STEPS)
+    print(f"[bench] per-call events on {n_ev} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rej_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    com_ms = [e[2].elapsed_time(e[3]) for e in evs]
     cold = cold_cache_calls(step, dev, args.cold_steps)
 
     copy_info = copy_calibration(dev) if args.copy_calibration else None
@@ -835,7 +907,11 @@ def gpu_bench(args) -> dict:
         roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=attn_gbs / HBM_PEAK_GBS, traffic=traffic,
                       kernel="spec_verify_attn (attn_streamk_kernel + attn_merge_kernel)",
-                      algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_avg_s * 1e6),
+                      algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_avg_s * 1e6, calls_timed=len(evs)),
+        roofline_reject=dict(bound="hbm", achieved=rej_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=rej_gbs / HBM_PEAK_GBS, traffic=stored_traffic(key="reject_hbm_bytes_per_call"),
+                             kernel="spec_reject_sample", algorithmic_bytes_per_call=r_bytes,
+                             avg_call_us=rej_avg_s * 1e6, calls_timed=len(evs)),
         verified_tokens_per_step=tokens,
         mean_emitted_per_sequence=tokens / B,
         step_gbs=(a_bytes + r_bytes + c_bytes) / step_s / 1e9,
@@ -851,7 +927,7 @@ def gpu_bench(args) -> dict:
                                dense_equivalent=dense_reject_figure(p, rej_avg_s)),
             commit_lengths=dict(avg_us=com_avg_s * 1e6, bytes=c_bytes)),
         event_sum_ms_per_step=(attn_avg_s + rej_avg_s + com_avg_s) * 1e3,
-        event_sampled_steps=len(evs),
+        event_timed_steps=len(evs),
     )
     if cold:
         cold["verify_attn"]["frac_of_peak"] = a_bytes / (cold["verify_attn"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
@@ -1020,9 +1096,11 @@ def main():
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cb = run_cpu_baseline_child(args.workload)
         if cb is not None:
-            result["cpu_baseline"] = dict(value=cb["tokens_per_s"], unit="verified tokens/s", cores=1,
-                                          kind="oracle", sample=cb["sample"],
-                                          seconds_per_step=cb["seconds_per_step"],
+            result["cpu_baseline"] = dict(value=cb["pooled"]["tokens_per_s"], unit="verified tokens/s",
+                                          cores=cb["workers"], kind="oracle", sample=cb["sample"],
+                                          seconds_per_step=cb["pooled"]["seconds_per_step"],
+                                          single_core=dict(value=cb["single"]["tokens_per_s"], cores=1,
+                                                           seconds_per_step=cb["single"]["seconds_per_step"]),
                                           cpu=_cpu_model())
     print(json.dumps(result))
 

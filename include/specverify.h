@@ -9,11 +9,15 @@
  *
  * Conventions shared by every call:
  *  - All data pointers are device pointers owned by the caller, contiguous and
- *    row-major as documented per argument. The library allocates nothing,
- *    keeps no global state and never synchronises: work is enqueued on
- *    `stream` (a hipStream_t; NULL means the default stream) and the caller
- *    synchronises. Calls on different streams may run concurrently if they
- *    use different workspaces and outputs.
+ *    row-major as documented per argument. The library allocates nothing and
+ *    never synchronises: work is enqueued on `stream` (a hipStream_t; NULL means
+ *    the default stream) and the caller synchronises. Its only global state is a
+ *    per-device cache of launch parameters read from the device (CU count,
+ *    resident workgroups per kernel, whether it is gfx950), filled on first use
+ *    with atomic stores, so host threads may call concurrently. Calls on
+ *    different streams may run concurrently if they use different workspaces and
+ *    outputs; spec_reject_sample* additionally needs the device to itself while
+ *    it runs (see there).
  *  - Host-side arguments are validated before anything is enqueued; on any
  *    error nothing is enqueued and an error code is returned. Device-resident
  *    data (token ids, block ids, lengths) is a documented precondition and is
@@ -31,6 +35,19 @@
  *    advanced by one. This is the switch between speculative and plain decoding
  *    that [RESP] (adaptive server) and [EFR] (speculation toggled by regime)
  *    make at run time, without a separate decode kernel.
+ *
+ * Beyond the plain three-call interface, by design:
+ *  - V pages are [num_blocks][Hkv][D][block_size] (key index fastest), not the K
+ *    pages' [num_blocks][Hkv][block_size][D]: a 16-byte load of a V page row is
+ *    then eight consecutive keys of one dimension, the B-operand fragment of the
+ *    P.V matrix product, so V streams from memory straight into matrix-core
+ *    registers. The caller's append writes V in this layout (spec_rope_append does).
+ *  - spec_reject_sample takes a workspace (and spec_reject_sample_workspace_size
+ *    sizes it): the workgroups that share a sequence's vocabulary exchange partial
+ *    statistics through it while the kernel runs.
+ *  - spec_reject_error_flag reports whether a sampling call had to give up a wait.
+ *  - Ragged draft lengths, tree verification and the upstream steps (RoPE with the
+ *    KV append, the LM head) have calls of their own.
  *
  * Sources for what is computed (page titles; the pages print no API):
  *  [ACC]  "Accelerating RL Post-Training Rollouts via System-Integrated
@@ -168,12 +185,23 @@ spec_status spec_verify_attn_ragged(const void* q, const void* k_cache, const vo
  * k = 0: no draft is tested; out_tokens[b][0] is drawn from p_0 with u_smp at
  * P = L_b + 1 and num_accepted[b] = 0. draft_logits, draft_tokens and
  * accept_probs are not read or written and may be NULL.
- * Rows after a sequence's first rejection are not read, and no row is read twice.
- * The workgroups of one sequence exchange partial sums while running, so the
- * grid is sized to what the device holds at once (SPEC_ERR_HIP if it cannot
- * hold one sequence's ceil(V / 32768) workgroups of 512 threads). Every wait is
- * bounded: should residency ever be partial (other streams filling the device)
- * and a wait time out, the affected sequence reports num_accepted = -1.
+ * Rows read: when the levels run one after another (the usual case) a row after
+ * a sequence's first rejection is not read and no row is read twice (the heavy
+ * logits, probability above 2^-14, are re-read for fp64 weights). When every
+ * level of every sequence fits the device at once (small batches: B (k+1)
+ * ceil(V / 16384) <= the CU count, or twice that for k <= 3) the levels run at
+ * once and all 2k+1 rows of each sequence are read; the outputs are the same bits.
+ * Residency: the workgroups of one sequence (ceil(V / 32768) of 512 threads, or
+ * ceil(V / 16384) of 256 threads) exchange partial sums while running, so the grid
+ * is sized to what the device holds at once and a plain launch assumes all of it
+ * is resident together (SPEC_ERR_HIP if the device cannot hold one sequence's
+ * workgroups). The call therefore needs the device to itself while it runs:
+ * another kernel running beside it can leave part of the grid waiting for a CU.
+ * Every wait is bounded (2^20 polls, about 10 ms): should one give up, the kernel
+ * still ends, the affected sequences report num_accepted = -1 (their other
+ * outputs are not written) and the workspace's error word is set; read it with
+ * spec_reject_error_flag. The outputs of a call do not depend on timing, so a call
+ * with any -1 can be repeated on an otherwise idle device for the intended result.
  * Workspace: spec_reject_sample_workspace_size(B, k, V).
  * ---------------------------------------------------------------------- */
 spec_status spec_reject_sample_workspace_size(int32_t B, int32_t k, int32_t V, size_t* bytes_out);
@@ -185,6 +213,22 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
                                int32_t* out_tokens, int32_t* num_accepted,
                                float* out_probs, float* accept_probs,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Error word of a sampling workspace (spec_reject_sample, _ragged or _tree).
+ *
+ * Copies the workspace's error word to *flag_out (a device int32) and clears it,
+ * in one single-thread launch on `stream` (no memset, so it may be captured in a
+ * graph). The word is nonzero if, since the last read, a bounded wait of a sampling
+ * call on this workspace gave up (see spec_reject_sample) or a tree broke its
+ * documented shape. Every sequence that reports num_accepted = -1 sets it; a
+ * sequence whose other workgroups completed it despite one giving up has correct
+ * outputs, though the word is set. Setting the
+ * environment variable SPECVERIFY_SPIN_LIMIT (polls per wait, 0 .. 2^20) before the
+ * first sampling call of a process shortens every wait; it exists to exercise this
+ * path in tests.
+ * ---------------------------------------------------------------------- */
+spec_status spec_reject_error_flag(void* workspace, int32_t* flag_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Rejection sampling with ragged draft lengths  [EFR] (acceptance-aware draft

@@ -18,7 +18,7 @@ import threading
 __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", "reject_sample",
            "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
            "reject_sample_ragged", "verify_attn_tree", "reject_sample_tree", "reject_sample_tree_workspace_size",
-           "commit_tree", "rope_append", "lm_head",
+           "commit_tree", "rope_append", "lm_head", "reject_error_flag", "reject_workspace",
            "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -46,6 +46,7 @@ SYMBOLS = {
     "spec_commit_tree": (_c_int32, [_vp] * 6 + [_c_int32] * 8 + [_vp, _vp]),
     "spec_rope_append": (_c_int32, [_vp] * 8 + [_c_int32] * 8 + [ctypes.c_double, _vp]),
     "spec_lm_head": (_c_int32, [_vp] * 3 + [_c_int32] * 3 + [_vp]),
+    "spec_reject_error_flag": (_c_int32, [_vp, _vp, _vp]),
 }
 
 
@@ -302,6 +303,26 @@ def reject_sample(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, 
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream_handle(stream)), "spec_reject_sample")
     return out_tokens, num_accepted
+
+
+def reject_workspace(device, kind: str = "reject"):
+    """The binding's own workspace for the sampling calls on `device` (kind "reject" for
+    spec_reject_sample and _ragged, "reject_tree" for the tree walk), or None if no call
+    has made one yet."""
+    return _workspaces.get((kind, str(device)))
+
+
+def reject_error_flag(workspace, flag_out, stream=None):
+    """spec_reject_error_flag: copy the sampling workspace's error word into flag_out (int32
+    device tensor of one element) and clear it. Nonzero iff some sequence of a call since the
+    last read reported num_accepted = -1."""
+    import torch
+    if flag_out.numel() < 1:
+        raise ValueError("flag_out needs one element")
+    _check(library().spec_reject_error_flag(_need(workspace, torch.uint8, "workspace"),
+                                            _need(flag_out, torch.int32, "flag_out"), _stream_handle(stream)),
+           "spec_reject_error_flag")
+    return flag_out
 
 
 def commit_lengths(seq_lens, num_accepted, k: int, capacity_tokens: int, overflow_flags=None, stream=None):

@@ -237,6 +237,13 @@ spec_status spec_reject_sample_tree(const float* target_logits, const float* dra
     return from_hip(launch_reject_tree(p, static_cast<hipStream_t>(stream)));
 }
 
+spec_status spec_reject_error_flag(void* workspace, int32_t* flag_out, void* stream) {
+    if (!workspace || !flag_out) return SPEC_ERR_NULL_POINTER;
+    const spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    return from_hip(launch_reject_error_flag(workspace, flag_out, static_cast<hipStream_t>(stream)));
+}
+
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
                                 int32_t capacity_tokens, int32_t* overflow_flags, void* stream) {
     if (!seq_lens || !num_accepted) return SPEC_ERR_NULL_POINTER;

@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
 }
 
 // Persistent-grid size per (device, kernel instantiation): CUs x resident workgroups.
-int g_grid_memo[64][16];
+DeviceMemo g_grid_memo[16];
 
 template <int D, int NT, bool kTree>
 int persistent_grid(int slot) {
@@ -574,8 +574,8 @@ int persistent_grid(int slot) {
         (void)hipGetLastError();
         return 256;
     }
-    int& memo = g_grid_memo[dev][slot];
-    if (memo > 0) return memo;
+    DeviceMemo& memo = g_grid_memo[slot];
+    if (memo.get(dev) > 0) return memo.get(dev);
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_streamk_kernel<D, NT, kTree>, kAT, 0) != hipSuccess) {
@@ -585,7 +585,7 @@ int persistent_grid(int slot) {
     int P = cus * (per_cu > 0 ? per_cu : 1);
     if (P > kMaxP) P = kMaxP;
     if (P < 1) P = 1;
-    memo = P;
+    memo.put(dev, P);
     return P;
 }
 

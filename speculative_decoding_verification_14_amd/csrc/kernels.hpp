@@ -5,7 +5,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace specverify {
+
+// Per-device cache of a launch parameter derived from the device (CU count,
+// resident workgroups of a kernel), 0 until filled. Relaxed atomics: host threads
+// calling on different streams may fill an entry at the same time, always with the
+// same value, without a data race.
+struct DeviceMemo {
+    std::atomic<int> v[64];
+    int get(int dev) const { return (dev >= 0 && dev < 64) ? v[dev].load(std::memory_order_relaxed) : 0; }
+    void put(int dev, int x) {
+        if (dev >= 0 && dev < 64) v[dev].store(x, std::memory_order_relaxed);
+    }
+};
 
 struct AttnLaunch {
     const void* q;
@@ -55,6 +69,8 @@ struct RejectLaunch {
 size_t reject_workspace_bytes(int B, int k, int V);
 int reject_max_vocab();   // largest V the reject kernel accepts
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream);
+// The error word of a reject (chain or tree) workspace, copied to *flag_out and cleared.
+hipError_t launch_reject_error_flag(void* workspace, int32_t* flag_out, hipStream_t stream);
 size_t reject_tree_workspace_bytes(int B, int nodes, int V);
 int reject_tree_max_branch();   // children per tree node the walk supports
 hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream);

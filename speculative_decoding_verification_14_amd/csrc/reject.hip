@@ -45,8 +45,12 @@
 //  * Co-residency of a group is required: the grid is sized to what the device
 //    holds at once, and every wait is bounded so that a wavefront always
 //    terminates (a timed-out sequence reports num_accepted = -1).
+#include <atomic>
+#include <cstdlib>
+
 #include "common.hpp"
 #include "fastexp.hpp"
+#include "heavy.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
 
@@ -63,8 +67,7 @@ constexpr int kRT = kUnitWaves * kWave;    // 512 threads
 constexpr int kMaxQ = 64;                  // workgroups per sequence: U <= 256 (V <= 2^20), four units each
 constexpr int kMaxBranch = 4;              // tree: children per node
 constexpr int kTreeEx = 24;                // tree: exchanges per sequence (levels, passes, the draw)
-constexpr float kLnTau = -9.70406052783923f;  // ln 2^-14: logits above this probability share use fp64
-constexpr unsigned kSpinLimit = 1u << 20;
+constexpr unsigned kSpinLimit = 1u << 20;    // polls per wait (see reject_spin_limit)
 constexpr int kMaxLevels = 16;             // decision slots per sequence (k <= 15)
 
 enum : unsigned { kCtlEpoch = 0, kCtlDone = 1, kCtlError = 2, kCtlQueue = 3, kCtlFinished = 4 };
@@ -92,6 +95,7 @@ struct RejectArgs {
     unsigned long long* dec_slots;     // level-parallel: [B][kMaxLevels] each level's decision
     unsigned long long* bonus_slots;   // level-parallel: [B][4][U] the bonus row's exchange
     unsigned long long* next_slots;    // chain: [kMaxGroups] each group's next sequence
+    unsigned spin;                     // polls before a wait gives up
     int B, k, V, U, Q, groups;
     float invT;                        // 1 / T
     float c2;                          // log2(e) / T
@@ -158,9 +162,9 @@ __device__ __forceinline__ void publish(unsigned long long* slots, const unsigne
 // were not resident at once).
 template <int N>
 __device__ __forceinline__ bool gather_at(unsigned long long* slots, int stride, int first, int count, unsigned epoch,
-                                          unsigned (&out)[N]) {
+                                          unsigned spin, unsigned (&out)[N]) {
     const int lane = lane_id();
-    for (unsigned it = 0; it < kSpinLimit; ++it) {
+    for (unsigned it = 0; it < spin; ++it) {
         bool ok = true;
 #pragma unroll
         for (int s = 0; s < N; ++s) {
@@ -178,8 +182,9 @@ __device__ __forceinline__ bool gather_at(unsigned long long* slots, int stride,
 }
 
 template <int N>
-__device__ __forceinline__ bool gather(unsigned long long* slots, int Q, unsigned epoch, unsigned (&out)[N]) {
-    return gather_at<N>(slots, Q, 0, Q, epoch, out);
+__device__ __forceinline__ bool gather(unsigned long long* slots, int Q, unsigned epoch, unsigned spin,
+                                       unsigned (&out)[N]) {
+    return gather_at<N>(slots, Q, 0, Q, epoch, spin, out);
 }
 
 // The first two steps of the DPP wavefront reductions (dpp_wave_max / dpp_wave_sum) alone: every lane ends with the
@@ -366,36 +371,13 @@ struct SampleCtx {
     double Mp64, Mq64, invT64;
 };
 
-// ln Z from the hardware log2 (a few ulp): it only places the heavy thresholds and
-// the support boundary, where any consistent value is correct and an error of
-// 1e-7 moves only logits whose weight is that small.
-__device__ __forceinline__ float ln_approx(double Z) {
-    return __builtin_amdgcn_logf(static_cast<float>(Z)) * 0.693147180559945f;
-}
-
-// Raw-logit threshold above which a logit's probability under (M, Z) exceeds tau:
-// p > tau  <=>  z > M + T (ln tau + ln Z). Monotone, so one compare per logit;
-// only its consistency matters (every site classifies with the same float).
-__device__ __forceinline__ float heavy_threshold(float M, double Z, float T) {
-    return fmaf(T, static_cast<float>(kLnTau) + ln_approx(Z), M);
-}
-
 // Log-weight of a logit in nats, (z - M) / T, and the residual-support test. The
 // operations are written with the no-contraction intrinsics so that every call
 // site rounds identically (the support must be the same set wherever it is judged).
 __device__ __forceinline__ float log_weight(float z, float M, float invT) { return __fmul_rn(__fsub_rn(z, M), invT); }
 __device__ __forceinline__ bool in_support(float xp, float xq, float dn) { return __fsub_rn(xp, xq) > dn; }
-// Heavy test as a sign bit: t - z < 0 exactly when z > t (the difference of two
-// distinct floats is never zero), so the bit is set iff z_p > t_p or z_q > t_q.
-// Kept in a vector register rather than as a lane mask, so that the 64 tests of a
-// unit can be packed into bits without tying up scalar registers. -inf padding is
-// never heavy.
-__device__ __forceinline__ unsigned heavy_sign(bool residual, float zp, float zq, const SampleCtx& c) {
-    const float d = residual ? fminf(c.tp - zp, c.tq - zq) : c.tp - zp;
-    return __builtin_bit_cast(unsigned, d);
-}
 __device__ __forceinline__ bool is_heavy(bool residual, float zp, float zq, const SampleCtx& c) {
-    return static_cast<int>(heavy_sign(residual, zp, zq, c)) < 0;
+    return static_cast<int>(heavy_sign(residual, zp, zq, c.tp, c.tq)) < 0;
 }
 
 // Light part of the unnormalised weights a = e^{(z_p - M_p)/T}, b = e^{(z_q - M_q)/T}
@@ -417,44 +399,6 @@ __device__ __forceinline__ void light_weights(bool residual, const f4& vp, const
     }
 }
 
-// The lane's heavy logits as two 32-bit masks: element k = 4i + e of the unit
-// (load i, component e) is bit 31 - k of lo for k < 32 and bit 63 - k of hi
-// otherwise (each mask is built by shifting in one bit per element).
-struct HeavyBits {
-    unsigned lo, hi;
-};
-
-__device__ __forceinline__ HeavyBits heavy_bits(bool residual, const f4 (&xp)[kVecs], const f4 (&xq)[kVecs],
-                                                const SampleCtx& c) {
-    HeavyBits hb{0u, 0u};
-#pragma unroll
-    for (int i = 0; i < kVecs; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // (mask << 1) | sign bit, one funnel shift
-            const unsigned d = heavy_sign(residual, xp[i][e], residual ? xq[i][e] : -INFINITY, c);
-            if (i < kVecs / 2) hb.lo = __builtin_amdgcn_alignbit(hb.lo, d, 31u);
-            else hb.hi = __builtin_amdgcn_alignbit(hb.hi, d, 31u);
-        }
-    }
-    return hb;
-}
-
-// Takes one heavy element off the masks: its index k in the unit, or -1.
-__device__ __forceinline__ int take_heavy(HeavyBits& hb) {
-    if (hb.lo != 0u) {
-        const int p = __builtin_ctz(hb.lo);
-        hb.lo &= hb.lo - 1u;
-        return 31 - p;
-    }
-    if (hb.hi != 0u) {
-        const int p = __builtin_ctz(hb.hi);
-        hb.hi &= hb.hi - 1u;
-        return 63 - p;
-    }
-    return -1;
-}
-
 // Up to four heavy logits of the lane, re-read from memory (rather than picked out
 // of the register arrays, which would need dynamic indexing and force the arrays
 // out of registers). Issued before the light pass so that the loads are in by the
@@ -469,17 +413,26 @@ __device__ __forceinline__ int round_k(const HeavyRound& r, int j) {
     return b == 0xFFu ? -1 : static_cast<int>(b);
 }
 
-__device__ __forceinline__ void heavy_fetch(bool residual, const float* prow, const float* qrow, int base,
-                                            HeavyBits& hb, HeavyRound& r) {
+__device__ __forceinline__ void heavy_fetch(bool residual, __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
+                                            int V, int base, HeavyBits& hb, HeavyRound& r) {
     r.ks = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int k = take_heavy(hb);
         r.ks |= static_cast<unsigned>(k & 0xFF) << (8 * j);
-        // heavy logits are never padding (-inf), so x < V; lanes without one read logit 0
-        const int x = k >= 0 ? base + (k >> 2) * (kWave * 4) + (k & 3) : 0;
-        r.zp[j] = prow[x];
-        r.zq[j] = residual ? qrow[x] : -INFINITY;
+        // Through the rows' buffer resources, like every other read of the logits: an
+        // offset past the row returns 0 without touching memory, so the read stays in
+        // bounds whatever the classification said. An element at or past V (padding,
+        // never heavy under the thresholds used, see heavy.hpp) is then taken as -inf,
+        // weight 0. Lanes without a heavy element read logit 0. Cached loads: the row
+        // was streamed moments ago.
+        const int x = k >= 0 ? heavy_element(base, k) : 0;
+        const bool pad = x >= V;
+        const float zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, x * 4, 0, 0));
+        const float zq = residual ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rq, x * 4, 0, 0))
+                                  : -INFINITY;
+        r.zp[j] = pad ? -INFINITY : zp;
+        r.zq[j] = pad ? -INFINITY : zq;
     }
 }
 
@@ -512,11 +465,12 @@ typedef double2 LoadSums[kVecs][kWave];
 // registers then hides the loads' latency.
 template <bool kVec4, bool kResidual>
 __device__ __forceinline__ UnitSums unit_sums(const f4 (&xp)[kVecs], const f4 (&xq)[kVecs], const SampleCtx& c,
-                                              const float* prow, const float* qrow, int base, LoadSums& ls) {
+                                              const float* prow, const float* qrow, int V, int base, LoadSums& ls) {
     const int lane = lane_id();
-    HeavyBits hb = heavy_bits(kResidual, xp, xq, c);
+    const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, V), rq = row_rsrc(qrow, V);
+    HeavyBits hb = heavy_bits<kVecs>(kResidual, xp, xq, c.tp, c.tq);
     HeavyRound hr;
-    heavy_fetch(kResidual, prow, qrow, base, hb, hr);
+    heavy_fetch(kResidual, rp, rq, V, base, hb, hr);
     double A = 0.0, Bs = 0.0, P = 0.0, Q = 0.0;
 #pragma unroll
     for (int i = 0; i < kVecs; ++i) {
@@ -555,7 +509,7 @@ __device__ __forceinline__ UnitSums unit_sums(const f4 (&xp)[kVecs], const f4 (&
     };
     heavy_weigh(kResidual, c, hr, add);
     while (__any((hb.lo | hb.hi) != 0u)) {   // lanes with more than four (rare)
-        heavy_fetch(kResidual, prow, qrow, base, hb, hr);
+        heavy_fetch(kResidual, rp, rq, V, base, hb, hr);
         heavy_weigh(kResidual, c, hr, add);
     }
     UnitSums s;
@@ -867,7 +821,7 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
     c.dn = ln_approx(st.Zp) - ln_approx(st.Zq);
 
     const int lane = lane_id();
-    const UnitSums us = unit_sums<kVec4, true>(xp, xq, c, prow, qrow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
+    const UnitSums us = unit_sums<kVec4, true>(xp, xq, c, prow, qrow, a.V, s.u * kUnit + lane * 4, sh.ls[s.wave]);
     unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
     if (lane == 0) sh.usum[s.wave] = make_double4(us.A, us.B, us.P, us.Q);
     __syncthreads();
@@ -887,7 +841,7 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
         unsigned v[kSampSlots];
-        const bool ok = gather<kSampSlots>(slots, nq, s.epoch, v);
+        const bool ok = gather<kSampSlots>(slots, nq, s.epoch, a.spin, v);
         // lane l < nq: quad l's sums (zero in the other lanes)
         const double Ag = join64(v[0], v[1]), Bg = join64(v[2], v[3]);
         const double Pg = join64(v[4], v[5]), Qg = join64(v[6], v[7]);
@@ -1051,7 +1005,7 @@ __device__ __forceinline__ unsigned level_core(const RejectArgs& a, const SeqCtx
         unsigned v[kStatSlots];
         unsigned flags = 0;
         float pd = 0.0f, ratio = 0.0f;
-        if (gather<kStatSlots>(r.slots, nq, s.epoch, v)) {
+        if (gather<kStatSlots>(r.slots, nq, s.epoch, a.spin, v)) {
             count_group(a, s, counted);
             tl.zp = uniform(ztp);
             tl.zq = uniform(ztq);
@@ -1126,12 +1080,12 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
     c.Mq64 = 0.0;
     c.invT64 = a.invT64;
     // A unit with no finite logit (all past V) has Z_u = 0: its threshold is +inf, so that
-    // no padding element is classified heavy (with -inf the test would read a NaN's sign).
-    c.tp = (Zu > 0.0) ? heavy_threshold(Mu, Zu, a.T) : INFINITY;
+    // no padding element is classified heavy.
+    c.tp = unit_heavy_threshold(Mu, Zu, a.T);
     c.tq = INFINITY;
     c.dn = 0.0f;
     const int lane = lane_id();
-    const UnitSums us = unit_sums<kVec4, false>(xp, xq, c, prow, prow, s.u * kUnit + lane * 4, sh.ls[s.wave]);
+    const UnitSums us = unit_sums<kVec4, false>(xp, xq, c, prow, prow, a.V, s.u * kUnit + lane * 4, sh.ls[s.wave]);
     const double Mu64 = Mu;
     if (lane == 0) sh.usum[s.wave] = make_double4(us.P, Mu64, 0.0, 0.0);
     __syncthreads();
@@ -1154,12 +1108,12 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[4];
-        bool ok = gather<4>(slots, nq, s.epoch, v);
+        bool ok = gather<4>(slots, nq, s.epoch, a.spin, v);
         count_group(a, s, counted);
         bool reached = true;
         if (gate_dec) {
             unsigned dv[1];
-            ok = gather_at<1>(gate_dec, 1, 0, gate_levels, s.epoch, dv) && ok;
+            ok = gather_at<1>(gate_dec, 1, 0, gate_levels, s.epoch, a.spin, dv) && ok;
             reached = __all(lane >= gate_levels || dv[0] == kDecAccepted);
         }
         const bool have = lane < nq;
@@ -1278,12 +1232,13 @@ __device__ __forceinline__ void tree_push(TreeRounds& R, double W) {
 // to the wavefront's LDS slab. Returns the wavefront's (sum w1, sum w2).
 template <bool kVec4, typename F>
 __device__ __forceinline__ double2 tree_unit_pass(const f4 (&xp)[kVecs], const f4 (&xq)[kVecs], const SampleCtx& c,
-                                                  const float* prow, const float* qrow, int base, LoadSums& ls,
-                                                  F&& f) {
+                                                  const float* prow, const float* qrow, int V, int base,
+                                                  LoadSums& ls, F&& f) {
     const int lane = lane_id();
-    HeavyBits hb = heavy_bits(true, xp, xq, c);
+    const __amdgpu_buffer_rsrc_t rp = row_rsrc(prow, V), rq = row_rsrc(qrow, V);
+    HeavyBits hb = heavy_bits<kVecs>(true, xp, xq, c.tp, c.tq);
     HeavyRound hr;
-    heavy_fetch(true, prow, qrow, base, hb, hr);
+    heavy_fetch(true, rp, rq, V, base, hb, hr);
     double S1 = 0.0, S2 = 0.0;
 #pragma unroll
     for (int i = 0; i < kVecs; ++i) {
@@ -1308,7 +1263,7 @@ __device__ __forceinline__ double2 tree_unit_pass(const f4 (&xp)[kVecs], const f
     };
     heavy_weigh(true, c, hr, add);
     while (__any((hb.lo | hb.hi) != 0u)) {
-        heavy_fetch(true, prow, qrow, base, hb, hr);
+        heavy_fetch(true, rp, rq, V, base, hb, hr);
         heavy_weigh(true, c, hr, add);
     }
     return make_double2(dpp_wave_sum(S1), dpp_wave_sum(S2));
@@ -1326,7 +1281,7 @@ __device__ __forceinline__ int tree_round(const RejectArgs& a, const SeqCtx& s, 
                                           const float* qrow, unsigned long long* slots, int pos, Shared& sh,
                                           bool draw, F&& f, E&& emit, double& T1, double& T2) {
     const int lane = lane_id();
-    const double2 ws = tree_unit_pass<kVec4>(xp, xq, c, prow, qrow, s.u * kUnit + lane * 4, sh.ls[s.wave], f);
+    const double2 ws = tree_unit_pass<kVec4>(xp, xq, c, prow, qrow, a.V, s.u * kUnit + lane * 4, sh.ls[s.wave], f);
     if (lane == 0) sh.usum[s.wave] = make_double4(ws.x, ws.y, 0.0, 0.0);
     __syncthreads();
     if (s.wave == 0) {
@@ -1342,7 +1297,7 @@ __device__ __forceinline__ int tree_round(const RejectArgs& a, const SeqCtx& s, 
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[4];
-        const bool ok = gather<4>(slots, a.Q, s.epoch, v);
+        const bool ok = gather<4>(slots, a.Q, s.epoch, a.spin, v);
         const double Wg = join64(v[0], v[1]);      // lane l < Q: workgroup l's sums (zero in the others)
         const double t1 = dpp_wave_sum(Wg), t2 = dpp_wave_sum(join64(v[2], v[3]));
         const double t = u_smp * t1;
@@ -1718,7 +1673,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                 nb = (static_cast<long long>(a.groups) + t < a.B) ? a.groups + static_cast<int>(t) : a.B;
                 if (lane == 0) slot_store(slot, (static_cast<unsigned>(round) << 16) | static_cast<unsigned>(nb), s.epoch);
             } else {
-                for (unsigned it = 0; it < kSpinLimit; ++it) {
+                for (unsigned it = 0; it < a.spin; ++it) {
                     const unsigned long long v = slot_load(slot);
                     const unsigned pay = static_cast<unsigned>(v >> 32);
                     if (static_cast<unsigned>(v) == s.epoch && (pay >> 16) == static_cast<unsigned>(round)) {
@@ -1816,7 +1771,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
     if (s.wave == 0) {   // is this level reached: did every earlier level accept?
         unsigned dv[1];
-        const bool ok = gather_at<1>(dec, 1, 0, j, s.epoch, dv);
+        const bool ok = gather_at<1>(dec, 1, 0, j, s.epoch, a.spin, dv);
         const bool reached = __all(lane >= j || dv[0] == kDecAccepted);
         if (lane == 0) s_reached = ok ? (reached ? 1 : 0) : -1;
     }
@@ -1840,10 +1795,10 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
 // Workgroups of the kernel the device holds at once, and its CU count.
 template <bool kVec4, bool kTree, int W>
 hipError_t co_resident(int dev, int* wgs, int* cus_out) {
-    static int memo[64][2];
-    if (dev >= 0 && dev < 64 && memo[dev][0] > 0) {
-        *wgs = memo[dev][0];
-        *cus_out = memo[dev][1];
+    static DeviceMemo memo_wgs, memo_cus;
+    if (memo_wgs.get(dev) > 0 && memo_cus.get(dev) > 0) {
+        *wgs = memo_wgs.get(dev);
+        *cus_out = memo_cus.get(dev);
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
@@ -1855,10 +1810,8 @@ hipError_t co_resident(int dev, int* wgs, int* cus_out) {
     if (e != hipSuccess) return e;
     *wgs = per_cu * cus;
     *cus_out = cus;
-    if (dev >= 0 && dev < 64) {
-        memo[dev][0] = *wgs;
-        memo[dev][1] = cus;
-    }
+    memo_wgs.put(dev, *wgs);
+    memo_cus.put(dev, cus);
     return hipSuccess;
 }
 
@@ -1898,8 +1851,8 @@ hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     // Every group waits for the decisions of the levels before it, so all of them
     // must be resident at once: the kernel's own occupancy decides.
-    static int memo[64];
-    int wgs = (dev >= 0 && dev < 64) ? memo[dev] : 0;
+    static DeviceMemo memo;
+    int wgs = memo.get(dev);
     if (wgs <= 0) {
         int per_cu = 0, cus = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_levels_kernel<kVec4, 4>, 4 * kWave, 0);
@@ -1907,7 +1860,7 @@ hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         wgs = per_cu * cus;
-        if (dev >= 0 && dev < 64) memo[dev] = wgs;
+        memo.put(dev, wgs);
     }
     if (static_cast<long long>(a.B) * (a.k + 1) * a.Q > wgs) return launch_variant<kVec4, false, 4>(a, stream);
     a.groups = a.B * (a.k + 1);
@@ -1917,20 +1870,47 @@ hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
 
 // CUs of the current device (0 if it cannot be read).
 int device_cus() {
-    static int memo[64];
+    static DeviceMemo memo;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
         return 0;
     }
-    if (memo[dev] > 0) return memo[dev];
+    if (memo.get(dev) > 0) return memo.get(dev);
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
-    memo[dev] = cus;
+    memo.put(dev, cus);
     return cus;
+}
+
+// Polls per bounded wait: 2^20 (~10 ms of polling, far beyond any wait of a
+// resident group), or the value of the environment variable SPECVERIFY_SPIN_LIMIT
+// when it is set the first time this is called. A small limit makes the waits
+// give up early, so that tests can exercise the error path from the host; every
+// wait still ends.
+unsigned reject_spin_limit() {
+    static std::atomic<long long> cached{-1};
+    long long v = cached.load(std::memory_order_relaxed);
+    if (v < 0) {
+        v = kSpinLimit;
+        if (const char* e = std::getenv("SPECVERIFY_SPIN_LIMIT")) {
+            char* end = nullptr;
+            const long long x = std::strtoll(e, &end, 10);
+            if (end != e && x >= 0 && x <= kSpinLimit) v = x;
+        }
+        cached.store(v, std::memory_order_relaxed);
+    }
+    return static_cast<unsigned>(v);
+}
+
+// Copies the workspace's error word into *flag_out and clears it. One thread; a
+// kernel rather than a memset or copy, so that it can sit in a captured graph.
+__global__ void reject_error_flag_kernel(unsigned* ctl, int32_t* flag_out) {
+    const unsigned v = __hip_atomic_exchange(ctl + kCtlError, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_out = static_cast<int32_t>(v);
 }
 
 // Workgroups per sequence with W unit wavefronts each.
@@ -1946,6 +1926,12 @@ size_t reject_workspace_bytes(int B, int k, int V) {
 }
 
 int reject_max_vocab() { return kUnit * 256; }
+
+hipError_t launch_reject_error_flag(void* workspace, int32_t* flag_out, hipStream_t stream) {
+    hipLaunchKernelGGL(reject_error_flag_kernel, dim3(1), dim3(1), 0, stream, static_cast<unsigned*>(workspace),
+                       flag_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
@@ -1998,6 +1984,7 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.T = p.temperature;
     a.seed = p.seed;
+    a.spin = reject_spin_limit();
     if (levels) return (p.V % 4) == 0 ? launch_levels<true>(a, stream) : launch_levels<false>(a, stream);
     if (W == 4)
         return (p.V % 4) == 0 ? launch_variant<true, false, 4>(a, stream) : launch_variant<false, false, 4>(a, stream);
@@ -2043,6 +2030,7 @@ hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
     a.invT64 = 1.0 / static_cast<double>(p.temperature);
     a.T = p.temperature;
     a.seed = p.seed;
+    a.spin = reject_spin_limit();
     return (p.V % 4) == 0 ? launch_variant<true, true, kUnitWaves>(a, stream)
                           : launch_variant<false, true, kUnitWaves>(a, stream);
 }

@@ -11,7 +11,10 @@ Parity bar:
 
 from __future__ import annotations
 
+import json
+import os
 import sys
+import time
 
 import numpy as np
 
@@ -90,6 +93,7 @@ class Tally:
     def __init__(self):
         self.decisions = 0
         self.mismatches = 0
+        self.mismatch_margins = []   # oracle margin of each mismatched decision
         self.bad = []          # mismatches above the margin threshold
         self.prob_err = 0.0
         self.sequences = 0
@@ -102,6 +106,19 @@ class Tally:
         return (f"decisions={self.decisions} mismatches={self.mismatches} "
                 f"(budget {MISMATCH_BUDGET * self.decisions:.1f}) over-margin={len(self.bad)} "
                 f"max_prob_err={self.prob_err:.2e}")
+
+    def record(self, label: str) -> None:
+        """Append this tally as one JSON line to the file named by SPECVERIFY_TALLY_OUT, if set,
+        so that a GPU run keeps the decision counts its parity tests saw."""
+        path = os.environ.get("SPECVERIFY_TALLY_OUT")
+        if not path:
+            return
+        rec = dict(label=label, decisions=self.decisions, mismatches=self.mismatches,
+                   max_mismatch_margin=max(self.mismatch_margins) if self.mismatch_margins else None,
+                   over_margin=len(self.bad), max_prob_err=self.prob_err, sequences=self.sequences,
+                   ok=self.ok(), time=time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()))
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
 
 
 def compare_reject(gpu: dict, oracle: dict, tally: Tally, k: int) -> Tally:
@@ -119,6 +136,7 @@ def compare_reject(gpu: dict, oracle: dict, tally: Tally, k: int) -> Tally:
                 same = (a_g == d.j) and int(toks_g[d.j]) == d.outcome
             if not same:
                 tally.mismatches += 1
+                tally.mismatch_margins.append(d.margin)
                 if not (d.margin < MARGIN):
                     tally.bad.append((b, d.kind, d.j, d.margin))
                 mismatch = True
@@ -139,3 +157,32 @@ def compare_reject(gpu: dict, oracle: dict, tally: Tally, k: int) -> Tally:
         if np.any(gpu["accept_probs"][b, nt:] != -1.0):
             tally.bad.append((b, "accept_probs_pad", -1, 0.0))
     return tally
+
+
+def summarise_tallies(src: str, dst: str, command: str) -> None:
+    """Text summary of a tally file written by GPU parity tests (one line per test case and a
+    total): decisions, mismatches and their largest oracle margin, probability error."""
+    recs = [json.loads(line) for line in open(src) if line.strip()]
+    dec = sum(r["decisions"] for r in recs)
+    mis = sum(r["mismatches"] for r in recs)
+    margins = [r["max_mismatch_margin"] for r in recs if r["max_mismatch_margin"] is not None]
+    lines = [f"# decision tallies of the GPU parity tests against the fp64 oracle ({len(recs)} cases)",
+             f"# command: {command}",
+             f"# bar: every mismatch has oracle margin < {MARGIN:g}; mismatches / decisions < {MISMATCH_BUDGET:g}; "
+             f"|prob error| <= {PROB_TOL:g}",
+             f"{'case':58s} {'decisions':>10s} {'mism.':>6s} {'ratio':>9s} {'max margin':>10s} {'prob err':>9s}"]
+    for r in recs:
+        ratio = r["mismatches"] / max(1, r["decisions"])
+        mm = "-" if r["max_mismatch_margin"] is None else f"{r['max_mismatch_margin']:.1e}"
+        lines.append(f"{r['label'][:58]:58s} {r['decisions']:10d} {r['mismatches']:6d} {ratio:9.2e} {mm:>10s} "
+                     f"{r['max_prob_err']:9.1e}")
+    lines.append(f"{'TOTAL':58s} {dec:10d} {mis:6d} {mis / max(1, dec):9.2e} "
+                 f"{(max(margins) if margins else 0.0):10.1e} {max(r['max_prob_err'] for r in recs):9.1e}")
+    lines.append(f"all cases within the bar: {all(r['ok'] for r in recs)}")
+    with open(dst, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    # python -m tests.parity SRC.jsonl DST.txt "command that produced SRC"
+    summarise_tallies(sys.argv[1], sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "")

@@ -161,3 +161,65 @@ def test_no_device_is_reported_not_crashed(lib):
     assert lib.spec_commit_tree(*_tree_commit_args()) == 5
     assert lib.spec_rope_append(*_rope_args()) == 5
     assert lib.spec_lm_head(FAKE, FAKE, FAKE, 4, 256, 100, NULL) == 5
+
+
+def test_error_flag_validation(lib):
+    assert lib.spec_reject_error_flag(NULL, FAKE, NULL) == 1
+    assert lib.spec_reject_error_flag(FAKE, NULL, NULL) == 1
+
+
+def test_concurrent_host_threads(lib):
+    """Eight host threads call every entry point at once, with invalid and valid host arguments
+    (valid ones end at the device check on a host without a GPU). The library's only shared state
+    is its per-device caches, filled with atomics; every call must return what it returns alone."""
+    import threading
+
+    import torch
+    no_gpu = not torch.cuda.is_available()
+    calls = [
+        (lambda: lib.spec_verify_attn(*_attn_args(D=96)), 2),
+        (lambda: lib.spec_reject_sample(*_rej_args(T=0.0)), 3),
+        (lambda: lib.spec_reject_sample(*_rej_args(wsb=8)), 4),
+        (lambda: lib.spec_commit_tree(*_tree_commit_args(N=0)), 2),
+        (lambda: lib.spec_rope_append(*_rope_args(Hq=7)), 2),
+        (lambda: lib.spec_reject_error_flag(NULL, FAKE, NULL), 1),
+    ]
+    if no_gpu:
+        calls += [
+            (lambda: lib.spec_verify_attn(*_attn_args()), 5),
+            (lambda: lib.spec_reject_sample(*_rej_args()), 5),
+            (lambda: lib.spec_commit_lengths(FAKE, FAKE, 4, 3, 100, NULL, NULL), 5),
+            (lambda: lib.spec_lm_head(FAKE, FAKE, FAKE, 4, 256, 100, NULL), 5),
+            (lambda: lib.spec_reject_error_flag(FAKE, FAKE, NULL), 5),
+        ]
+    sizes = []
+
+    def sizes_call():
+        n = ctypes.c_size_t(0)
+        assert lib.spec_reject_sample_workspace_size(64, 3, 128256, ctypes.byref(n)) == 0
+        m = ctypes.c_size_t(0)
+        assert lib.spec_verify_attn_workspace_size(64, 3, 32, 8, 128, 8196, ctypes.byref(m)) == 0
+        return n.value, m.value
+
+    errors = []
+    start = threading.Barrier(8)
+
+    def worker(t):
+        try:
+            start.wait()
+            for i in range(300):
+                fn, code = calls[(i + t) % len(calls)]
+                got = fn()
+                if got != code:
+                    errors.append((t, i, got, code))
+                sizes.append(sizes_call())
+        except Exception as e:     # noqa: BLE001 - reported below
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:5]
+    assert len(set(sizes)) == 1

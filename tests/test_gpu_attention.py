@@ -127,7 +127,7 @@ def test_8b_full_size_sampled(device):
         assert np.max(np.abs(got[b, 3, b % 32] - want)) <= ATTN_TOL
 
 
-@pytest.mark.parametrize("name,B", [("7b", 64), ("longtail", 8), ("262k", 2)])
+@pytest.mark.parametrize("name,B", [("7b", 256), ("7b", 64), ("7b", 16), ("7b", 4), ("longtail", 8), ("262k", 2)])
 def test_other_workloads_sampled(device, name, B):
     inp = make_attention_inputs(PRESETS[name], B=B)
     got = run_attention(inp, device)

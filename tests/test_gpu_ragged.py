@@ -139,6 +139,7 @@ def _compare_ragged(g, o, cu, tally):
                 a_g == d.j and int(toks[d.j]) == d.outcome)
             if not same:
                 tally.mismatches += 1
+                tally.mismatch_margins.append(d.margin)
                 if not (d.margin < MARGIN):
                     tally.bad.append((b, d.kind, d.j, d.margin))
                 bad = True
@@ -174,6 +175,7 @@ def _check_ragged(inp, device, seeds, label):
                                      inp["seq_ids"], inp["seq_lens"], inp["temperature"], s, rows_cache=rows)
         _compare_ragged(g, o, cu, tally)
     say(f"[ragged reject] {label} lens {np.diff(cu).tolist()[:16]}: {tally.summary()}")
+    tally.record(f"ragged reject {label}")
     assert not tally.bad, tally.bad[:10]
     assert tally.mismatches <= MISMATCH_BUDGET * max(1, tally.decisions) and tally.prob_err <= PROB_TOL
     return tally
@@ -248,4 +250,5 @@ def test_reject_ragged_steps_with_commit(device):
         torch.cuda.synchronize()
         L, _ = ocommit.commit_lengths(L, o["num_accepted"], 10**6)
         np.testing.assert_array_equal(rd.sl.cpu().numpy(), L)
+    tally.record("test_gpu_ragged::test_reject_ragged_steps_with_commit")
     assert not tally.bad and tally.mismatches <= MISMATCH_BUDGET * tally.decisions, tally.summary()

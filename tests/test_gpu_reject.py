@@ -41,6 +41,7 @@ def _check(inp, device, seeds, temperature=None, label=""):
         gpu = rd.call(s, temperature)
         compare_reject(gpu, _oracle(inp, s, rows, temperature), tally, inp["k"])
     say(f"[reject] {label}: {tally.summary()}")
+    tally.record(f"reject {label} B={inp['B']} k={inp['k']} V={inp['V']}")
     assert tally.ok(), (tally.summary(), tally.bad[:10])
     return tally
 
@@ -260,6 +261,7 @@ def test_step_chain_with_commit_matches_oracle(device):
         torch.cuda.synchronize()
         L, _ = ocommit.commit_lengths(L, o["num_accepted"], 10**6)
         np.testing.assert_array_equal(rd.sl.cpu().numpy(), L)
+    tally.record("test_gpu_reject::test_step_chain_with_commit_matches_oracle")
     assert tally.ok(), tally.summary()
 
 
@@ -292,4 +294,34 @@ def test_plain_decoding_k0_steps_with_commit(device):
         torch.cuda.synchronize()
         L = L + 1
         np.testing.assert_array_equal(rd.sl.cpu().numpy(), L)
+    tally.record("test_gpu_reject::test_plain_decoding_k0_steps_with_commit")
     assert tally.ok(), tally.summary()
+
+
+@pytest.mark.parametrize("limit", [0, 1])
+def test_wait_timeout_is_reported(device, limit):
+    """Bounded waits that give up, forced from the host: a child process runs the sampling calls
+    with SPECVERIFY_SPIN_LIMIT polls per wait (0: every wait gives up at once; 1: one poll, so
+    some may succeed). Every kernel ends; sequences whose waits gave up report num_accepted = -1,
+    the others equal the oracle; the workspace's error word is set whenever some sequence reported
+    -1 (it may also be set when a workgroup gave up while the others still completed the
+    sequence, which then has the oracle's outputs), and reading it clears it."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SPECVERIFY_SPIN_LIMIT=str(limit))
+    say(f"[reject] timeout child, {limit} polls per wait")
+    r = subprocess.run([sys.executable, "-u", os.path.join(root, "tests", "reject_timeout_child.py")], env=env,
+                       capture_output=True, text=True, timeout=240, cwd=root)
+    assert r.returncode == 0, r.stderr[-3000:]
+    cases = [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
+    assert len(cases) == 4, r.stdout
+    for c in cases:
+        say(f"[reject] spin {limit}: {c}")
+        assert c["differ"] == 0, c
+        assert c["errored"] == 0 or c["word"] != 0, c
+        assert c["word_after"] == 0, c
+        if limit == 0:
+            assert c["errored"] == c["B"], c

@@ -127,6 +127,7 @@ def _compare_tree(g, o, tally):
                 same = a_g == d.j and int(toks_g[d.j]) == d.outcome
             if not same:
                 tally.mismatches += 1
+                tally.mismatch_margins.append(d.margin)
                 if not (d.margin < MARGIN):
                     tally.bad.append((b, d.kind, d.j, node, d.margin))
                 bad = True
@@ -160,6 +161,7 @@ def _check_tree(inp, device, seeds, label):
                                     inp["seq_ids"], inp["seq_lens"], inp["temperature"], s)
         _compare_tree(g, o, tally)
     say(f"[tree reject] {label}: {tally.summary()}")
+    tally.record(f"tree walk {label}")
     assert not tally.bad, tally.bad[:10]
     assert tally.mismatches <= MISMATCH_BUDGET * max(1, tally.decisions) and tally.prob_err <= PROB_TOL
     return tally
@@ -201,6 +203,7 @@ def test_tree_steps_with_commit(device):
         torch.cuda.synchronize()
         L, _ = ocommit.commit_lengths(L, o["num_accepted"], 10**6)
         np.testing.assert_array_equal(td.sl.cpu().numpy(), L)
+    tally.record("test_gpu_tree::test_tree_steps_with_commit")
     assert not tally.bad and tally.mismatches <= MISMATCH_BUDGET * tally.decisions, tally.summary()
 
 
@@ -313,4 +316,5 @@ def test_tree_reject_broken_trees_then_a_valid_call(device):
                                  inp2["seq_ids"], inp2["seq_lens"], inp2["temperature"], inp2["seed"] + 1)
     _compare_tree(g2, o2, tally)
     say(f"[tree reject] broken trees, then a valid call: {tally.summary()}")
+    tally.record("test_gpu_tree::test_tree_reject_broken_trees_then_a_valid_call")
     assert not tally.bad and tally.mismatches == 0, tally.summary()

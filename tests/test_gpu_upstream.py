@@ -210,4 +210,5 @@ def test_fused_pass_on_the_device(device):
         new_len, _ = ocommit.commit_lengths(a["seq_lens"], got["num_accepted"], cap)
         np.testing.assert_array_equal(sl.cpu().numpy(), new_len)
     say(f"[fused pass] attention err {attn_err:.2e}; sampler {tally.summary()}")
+    tally.record("fused pass (LM-head logits) 8b")
     assert tally.ok(), tally.summary()
