@@ -215,6 +215,32 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Rejection sampling without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Computes exactly what spec_reject_sample computes, with the same arguments and
+ * outputs, but uses the library's own workspace: a 16 MiB device array of the
+ * library, one copy per GPU, zero when the library is loaded and held until the
+ * process ends. Nothing is allocated: the array's device address is looked up
+ * (hipGetSymbolAddress) on the first call on each device and kept.
+ * Limit: spec_reject_sample_workspace_size(B, k, V) must not exceed 16 MiB
+ * (SPEC_ERR_WORKSPACE_TOO_SMALL otherwise; e.g. B = 1024 at k = 3, V = 128256
+ * fits, B = 4096 does not). Every call on a GPU shares that GPU's array, which
+ * carries the call counter from one call to the next, so no clearing is needed
+ * between calls; calls that overlap on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller. As for
+ * spec_reject_sample, a sequence whose bounded wait gave up reports
+ * num_accepted = -1.
+ * ---------------------------------------------------------------------- */
+spec_status spec_reject_sample_noalloc(const float* target_logits, const float* draft_logits,
+                                       const int32_t* draft_tokens, const int64_t* seq_ids,
+                                       const int32_t* seq_lens, int32_t B, int32_t k, int32_t V,
+                                       float temperature, uint64_t seed,
+                                       int32_t* out_tokens, int32_t* num_accepted,
+                                       float* out_probs, float* accept_probs, void* stream);
+
+/* ------------------------------------------------------------------------
  * Error word of a sampling workspace (spec_reject_sample, _ragged or _tree).
  *
  * Copies the workspace's error word to *flag_out (a device int32) and clears it,

@@ -19,6 +19,7 @@ __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", 
            "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
            "reject_sample_ragged", "verify_attn_tree", "reject_sample_tree", "reject_sample_tree_workspace_size",
            "commit_tree", "rope_append", "lm_head", "reject_error_flag", "reject_workspace",
+           "reject_sample_noalloc",
            "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -47,6 +48,8 @@ SYMBOLS = {
     "spec_rope_append": (_c_int32, [_vp] * 8 + [_c_int32] * 8 + [ctypes.c_double, _vp]),
     "spec_lm_head": (_c_int32, [_vp] * 3 + [_c_int32] * 3 + [_vp]),
     "spec_reject_error_flag": (_c_int32, [_vp, _vp, _vp]),
+    "spec_reject_sample_noalloc": (_c_int32, [_vp] * 5 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
+                                   + [_vp] * 5),
 }
 
 
@@ -323,6 +326,29 @@ def reject_error_flag(workspace, flag_out, stream=None):
                                             _need(flag_out, torch.int32, "flag_out"), _stream_handle(stream)),
            "spec_reject_error_flag")
     return flag_out
+
+
+def reject_sample_noalloc(target_logits, draft_logits, draft_tokens, seq_ids, seq_lens, temperature: float,
+                          seed: int, out_tokens, num_accepted, out_probs=None, accept_probs=None, stream=None):
+    """spec_reject_sample_noalloc: spec_reject_sample on the library's own 16 MiB workspace (one per
+    GPU; calls that overlap on one GPU race on it). Arguments as for reject_sample."""
+    import torch
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    if k == 0:
+        draft_logits = draft_tokens = accept_probs = None
+    _check(library().spec_reject_sample_noalloc(_need(target_logits, torch.float32, "target_logits"),
+                                                _opt(draft_logits, torch.float32, "draft_logits"),
+                                                _opt(draft_tokens, torch.int32, "draft_tokens"),
+                                                _need(seq_ids, torch.int64, "seq_ids"),
+                                                _need(seq_lens, torch.int32, "seq_lens"),
+                                                B, k, V, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                                _need(out_tokens, torch.int32, "out_tokens"),
+                                                _need(num_accepted, torch.int32, "num_accepted"),
+                                                _opt(out_probs, torch.float32, "out_probs"),
+                                                _opt(accept_probs, torch.float32, "accept_probs"),
+                                                _stream_handle(stream)), "spec_reject_sample_noalloc")
+    return out_tokens, num_accepted
 
 
 def commit_lengths(seq_lens, num_accepted, k: int, capacity_tokens: int, overflow_flags=None, stream=None):

@@ -192,6 +192,31 @@ spec_status spec_reject_sample(const float* target_logits, const float* draft_lo
                        seed, out_tokens, num_accepted, out_probs, accept_probs, workspace, workspace_bytes, stream);
 }
 
+spec_status spec_reject_sample_noalloc(const float* target_logits, const float* draft_logits,
+                                       const int32_t* draft_tokens, const int64_t* seq_ids,
+                                       const int32_t* seq_lens, int32_t B, int32_t k, int32_t V,
+                                       float temperature, uint64_t seed,
+                                       int32_t* out_tokens, int32_t* num_accepted,
+                                       float* out_probs, float* accept_probs, void* stream) {
+    if (B < 1 || B > 65535 || k < 0 || k > 15 || V < 2 || V > reject_max_vocab()) return SPEC_ERR_BAD_SHAPE;
+    if (reject_workspace_bytes(B, k, V) > reject_noalloc_scratch_bytes()) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    // the rest of the host validation happens in reject_impl, before anything is enqueued
+    if (!target_logits || (k > 0 && (!draft_logits || !draft_tokens)) || !seq_ids || !seq_lens || !out_tokens ||
+        !num_accepted)
+        return SPEC_ERR_NULL_POINTER;
+    if (!(std::isfinite(temperature) && temperature > 0.0f)) return SPEC_ERR_BAD_VALUE;
+    spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    void* scratch = nullptr;
+    if (reject_noalloc_scratch(&scratch) != hipSuccess) {
+        (void)hipGetLastError();
+        return SPEC_ERR_HIP;
+    }
+    return reject_impl(target_logits, draft_logits, draft_tokens, nullptr, seq_ids, seq_lens, B, k, V, temperature,
+                       seed, out_tokens, num_accepted, out_probs, accept_probs, scratch,
+                       reject_noalloc_scratch_bytes(), stream);
+}
+
 spec_status spec_reject_sample_ragged(const float* target_logits, const float* draft_logits,
                                       const int32_t* draft_tokens, const int32_t* cu_drafts,
                                       const int64_t* seq_ids, const int32_t* seq_lens, int32_t B, int32_t max_k,

@@ -69,6 +69,10 @@ struct RejectLaunch {
 size_t reject_workspace_bytes(int B, int k, int V);
 int reject_max_vocab();   // largest V the reject kernel accepts
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream);
+// The library's own sampling workspace for callers that cannot allocate: its size, and the
+// current device's copy (looked up on the first call on each device; allocates nothing).
+size_t reject_noalloc_scratch_bytes();
+hipError_t reject_noalloc_scratch(void** ptr_out);
 // The error word of a reject (chain or tree) workspace, copied to *flag_out and cleared.
 hipError_t launch_reject_error_flag(void* workspace, int32_t* flag_out, hipStream_t stream);
 size_t reject_tree_workspace_bytes(int B, int nodes, int V);

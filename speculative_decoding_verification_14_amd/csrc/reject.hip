@@ -1919,7 +1919,35 @@ int groups_of(int V, int W) {
     return (U + W - 1) / W;
 }
 
+// The sampling workspace of spec_reject_sample_noalloc: a file-scope device array, one
+// copy per GPU, zero at module load and kept until the process ends. Its name is a
+// host-side stand-in in host code; the device address comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char g_reject_scratch[kNoAllocScratchBytes];
+
+// Device address of this GPU's copy of g_reject_scratch, looked up once per device (with
+// that device current) and kept; nullptr until then.
+std::atomic<void*> g_reject_scratch_ptr[64];
+
 }  // namespace
+
+size_t reject_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t reject_noalloc_scratch(void** ptr_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* ptr = g_reject_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_reject_scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_reject_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *ptr_out = ptr;
+    return hipSuccess;
+}
 
 size_t reject_workspace_bytes(int B, int k, int V) {
     return reject_layout(B, k, (V + kUnit - 1) / kUnit).total;
