@@ -329,8 +329,18 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                     const int vkey0 = min(t0 + 8 * lg, (s1 - 1) & ~7);
                     const int pg = s_bt[(vkey0 >> a.bs_log2) - p0];
                     const uint16_t* vp = a.vc + (size_t(pg) * a.Hkv + g) * head_stride + (vkey0 & (bs - 1));
+                    if (a.bs_log2 >= 6) {
+                        // 64-key pages: a V page row (one dimension) is a whole 128-byte line,
+                        // half of which is this block's; the other half belongs to the next
+                        // block, which another wave of the workgroup reads at the same time.
+                        // Cached loads let that read find the line in the L2 (streaming loads
+                        // fetched every such line twice: 1.26x the algorithmic bytes at 262K).
 #pragma unroll
-                    for (int j = 0; j < DJ; ++j) vr[j] = load16_nt(vp + size_t(16 * j + l16) * bs);
+                        for (int j = 0; j < DJ; ++j) vr[j] = load16(vp + size_t(16 * j + l16) * bs);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < DJ; ++j) vr[j] = load16_nt(vp + size_t(16 * j + l16) * bs);
+                    }
                 }
                 if (t0 + kBlockKeys > s1) {
                     // tail block: values of keys >= s1 (past the sequence, or another piece's) become 0

@@ -69,6 +69,7 @@ constexpr int kMaxBranch = 4;              // tree: children per node
 constexpr int kTreeEx = 24;                // tree: exchanges per sequence (levels, passes, the draw)
 constexpr unsigned kSpinLimit = 1u << 20;    // polls per wait (see reject_spin_limit)
 constexpr int kMaxLevels = 16;             // decision slots per sequence (k <= 15)
+constexpr int kDecSlots = 3;               // per level: decision, p of the draft, min(1, p/q)
 
 enum : unsigned { kCtlEpoch = 0, kCtlDone = 1, kCtlError = 2, kCtlQueue = 3, kCtlFinished = 4 };
 constexpr int kMaxGroups = 1024;           // groups of one launch (the device holds at most 512 workgroups)
@@ -92,7 +93,8 @@ struct RejectArgs {
     const int32_t* parents;            // tree: [B][k] parent of node n at [n-1]; null for a chain
     int32_t* out_nodes;                // tree: [B][k] accepted node indices, or null
     unsigned long long* tree_slots;    // tree: [B][kTreeEx][kSampSlots][U], one block per exchange
-    unsigned long long* dec_slots;     // level-parallel: [B][kMaxLevels] each level's decision
+    unsigned long long* dec_slots;     // level-parallel: [B][kDecSlots][kMaxLevels] each level's decision,
+                                       // the probability of its draft and min(1, p/q)
     unsigned long long* bonus_slots;   // level-parallel: [B][4][U] the bonus row's exchange
     unsigned long long* next_slots;    // chain: [kMaxGroups] each group's next sequence
     unsigned spin;                     // polls before a wait gives up
@@ -116,7 +118,7 @@ RejectLayout reject_layout(int B, int k, int U) {
     L.ctl = o;  o = align256(o + 8 * sizeof(unsigned));
     L.stat = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * (k + 1) * U * kStatSlots);
     L.samp = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * kSampSlots);
-    L.dec = o;  o = align256(o + sizeof(unsigned long long) * size_t(B) * kMaxLevels);
+    L.dec = o;  o = align256(o + sizeof(unsigned long long) * size_t(B) * kDecSlots * kMaxLevels);
     L.bonus = o; o = align256(o + sizeof(unsigned long long) * size_t(B) * U * 4);
     L.next = o; o = align256(o + sizeof(unsigned long long) * kMaxGroups);
     L.total = o;
@@ -158,27 +160,38 @@ __device__ __forceinline__ void publish(unsigned long long* slots, const unsigne
 // Waits until the N slots of each of the Q workgroups carry `epoch` and returns
 // their payloads: lane l gets workgroup l (lanes >= Q read zero). Slot s of
 // workgroup l is slots[s * Q + l], so each read instruction covers consecutive
-// words. Returns false if the bounded wait ran out (only possible if the group
-// were not resident at once).
+// words. Returns false if the bounded wait ran out after `spin` polls (only
+// possible if the group were not resident at once).
 template <int N>
 __device__ __forceinline__ bool gather_at(unsigned long long* slots, int stride, int first, int count, unsigned epoch,
                                           unsigned spin, unsigned (&out)[N]) {
+    // Two polls in flight: the next one is issued before the previous one is looked at,
+    // so a slot is seen about half a round trip sooner than with one poll at a time
+    // (on the 8B rows the call takes ~1.5 us less).
     const int lane = lane_id();
-    for (unsigned it = 0; it < spin; ++it) {
+    unsigned long long va[N], vb[N];
+    auto issue = [&](unsigned long long (&v)[N]) {
+#pragma unroll
+        for (int s = 0; s < N; ++s) v[s] = lane < count ? slot_load(slots + size_t(s) * stride + first + lane) : 0ull;
+    };
+    auto take = [&](const unsigned long long (&v)[N]) {
         bool ok = true;
 #pragma unroll
         for (int s = 0; s < N; ++s) {
-            unsigned long long v = 0;
-            if (lane < count) {
-                v = slot_load(slots + size_t(s) * stride + first + lane);
-                ok = ok && static_cast<unsigned>(v) == epoch;
-            }
-            out[s] = static_cast<unsigned>(v >> 32);
+            if (lane < count) ok = ok && static_cast<unsigned>(v[s]) == epoch;
+            out[s] = static_cast<unsigned>(v[s] >> 32);
         }
-        if (__all(ok)) return true;
-        __builtin_amdgcn_s_sleep(4);
+        return __all(ok);
+    };
+    if (spin == 0) return false;
+    issue(va);
+    for (unsigned it = 0; it + 1 < spin; it += 2) {
+        issue(vb);
+        if (take(va)) return true;
+        issue(va);
+        if (take(vb)) return true;
     }
-    return false;
+    return take(va);
 }
 
 template <int N>
@@ -600,6 +613,18 @@ using Shared = SharedT<kUnitWaves>;
 enum : unsigned { kResAccepted = 1u, kResError = 2u };
 enum : unsigned { kSampUseP = 1u, kSampExact = 2u, kSampError = 4u, kSampAbort = 8u };
 enum : unsigned { kDecRejected = 1u, kDecAccepted = 2u };   // payloads of the decision slots
+
+// Level-parallel sampling: the outputs of accepted level i (its draft token, p of it and
+// min(1, p/q)), written by the group that draws the sequence's last token once it has
+// seen every earlier level's published decision. A level never writes its own outputs:
+// one whose wait for the earlier decisions gave up would leave them unwritten while a
+// later group, trusting its published acceptance, completed the sequence.
+__device__ __forceinline__ void level_outputs(const RejectArgs& a, const SeqCtx& s, int i, unsigned pd_bits,
+                                              unsigned ratio_bits) {
+    a.out_tokens[s.tb + i] = a.draft_tokens[s.db + i];
+    if (a.out_probs) a.out_probs[s.tb + i] = __builtin_bit_cast(float, pd_bits);
+    if (a.accept_probs) a.accept_probs[s.db + i] = __builtin_bit_cast(float, ratio_bits);
+}
 
 __device__ __forceinline__ void flag_error(const RejectArgs& a, const SeqCtx& s) {
     if (s.wave == 0 && lane_id() == 0) {
@@ -1112,9 +1137,10 @@ __device__ __forceinline__ void bonus_core(const RejectArgs& a, const SeqCtx& s,
         count_group(a, s, counted);
         bool reached = true;
         if (gate_dec) {
-            unsigned dv[1];
-            ok = gather_at<1>(gate_dec, 1, 0, gate_levels, s.epoch, a.spin, dv) && ok;
+            unsigned dv[kDecSlots];
+            ok = gather_at<kDecSlots>(gate_dec, kMaxLevels, 0, gate_levels, s.epoch, a.spin, dv) && ok;
             reached = __all(lane >= gate_levels || dv[0] == kDecAccepted);
+            if (ok && reached && s.q == 0 && lane < gate_levels) level_outputs(a, s, lane, dv[1], dv[2]);
         }
         const bool have = lane < nq;
         const double Wg = have ? join64(v[0], v[1]) : 0.0;
@@ -1747,7 +1773,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     s.qrow_base = a.draft + s.db * a.V;
     s.sid = load_uniform(a.seq_ids, b);
     s.L = load_uniform(a.seq_lens, b);
-    unsigned long long* dec = a.dec_slots + size_t(b) * kMaxLevels;
+    unsigned long long* dec = a.dec_slots + size_t(b) * kDecSlots * kMaxLevels;
     const int lane = lane_id();
     if (j > s.kb) {   // past this sequence's drafts: nothing to do but be counted
         if (s.wave == 0) count_group(a, s, counted);
@@ -1760,19 +1786,26 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
     RowStats st;
     const unsigned res = level_step<kVec4>(a, s, j, xp, xq, st, sh, counted, true);
-    const int tok = uniform(sh.res.tok);
     const float pd = uniform(sh.res.pd), ratio = uniform(sh.res.ratio);
     const bool accepted = (res & kResAccepted) != 0;   // false on an error
-    if (s.q == 0 && s.wave == 0 && lane == 0)           // published even on an error, so later levels stop
+    if (s.q == 0 && s.wave == 0 && lane == 0) {        // published even on an error, so later levels stop
         slot_store(dec + j, accepted ? kDecAccepted : kDecRejected, s.epoch);
+        slot_store(dec + kMaxLevels + j, __builtin_bit_cast(unsigned, pd), s.epoch);
+        slot_store(dec + 2 * kMaxLevels + j, __builtin_bit_cast(unsigned, ratio), s.epoch);
+    }
     if (res & kResError) {
         flag_error(a, s);
         return;
     }
-    if (s.wave == 0) {   // is this level reached: did every earlier level accept?
-        unsigned dv[1];
-        const bool ok = gather_at<1>(dec, 1, 0, j, s.epoch, a.spin, dv);
+    if (accepted) return;   // its outputs are written by the group that draws the last token
+    if (s.wave == 0) {      // the first rejection draws: did every earlier level accept?
+        unsigned dv[kDecSlots];
+        const bool ok = gather_at<kDecSlots>(dec, kMaxLevels, 0, j, s.epoch, a.spin, dv);
         const bool reached = __all(lane >= j || dv[0] == kDecAccepted);
+        if (ok && reached && s.q == 0) {   // the outputs the chain writes at the earlier levels and this one
+            if (lane < j) level_outputs(a, s, lane, dv[1], dv[2]);
+            if (lane == 0 && a.accept_probs) a.accept_probs[s.db + j] = ratio;
+        }
         if (lane == 0) s_reached = ok ? (reached ? 1 : 0) : -1;
     }
     __syncthreads();
@@ -1782,14 +1815,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         return;
     }
     if (!reached) return;   // an earlier level rejected: this one is never tested
-    if (s.q == 0 && s.wave == 0 && lane == 0) {   // the outputs the chain writes at this level
-        if (a.accept_probs) a.accept_probs[s.db + j] = ratio;
-        if (accepted) {
-            a.out_tokens[s.tb + j] = tok;
-            if (a.out_probs) a.out_probs[s.tb + j] = pd;
-        }
-    }
-    if (!accepted) sample_row<kVec4>(a, s, j, xp, xq, st, sh);
+    sample_row<kVec4>(a, s, j, xp, xq, st, sh);
 }
 
 // Workgroups of the kernel the device holds at once, and its CU count.
