@@ -57,7 +57,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-EVENT_EVERY = 10
+EVENT_EVERY = 1     # per-call events on every timed step (a few microseconds of records per step)
 EVENT_STEPS = 30    # at least this many steps with per-call events for the averages
 METRIC = "verified tokens/s + HBM GB/s (% of peak) for spec verify, 8B shape, k=3"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_counters.txt")
@@ -618,6 +618,7 @@ def gpu_bench_fused(args, p, dev) -> dict:
         raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
     mean = lambda v: sum(v) / len(v)
     call_s = [mean([e[j].elapsed_time(e[j + 1]) for e in evs.values()]) / 1e3 for j in range(5)]
+    vs_lib = lm_head_vs_library(hidden, weight, tl, stream)
     a_bytes, r_bytes, _ = algorithmic_bytes(p, a["seq_lens"], acc)
     lm_bytes = p.V * H * 2 + R * H * 2 + R * p.V * 4
     lm_flops = 2.0 * R * H * p.V
@@ -653,7 +654,39 @@ def gpu_bench_fused(args, p, dev) -> dict:
             reject_sample=dict(avg_us=call_s[3] * 1e6, bytes=r_bytes, gbs=gbs(r_bytes, call_s[3]),
                                frac_of_peak=gbs(r_bytes, call_s[3]) / HBM_PEAK_GBS),
             commit_lengths=dict(avg_us=call_s[4] * 1e6)),
+        lm_head_vs_library=vs_lib,
     )
+
+
+def lm_head_vs_library(hidden, weight, logits, stream, rounds: int = 6, calls: int = 10) -> dict:
+    """spec_lm_head against torch's library GEMM (torch.nn.functional.linear, bf16 output) on the
+    same operands, back to back: rounds of `calls` calls of each, interleaved, every call timed
+    with events on the stream both run on; medians over all calls."""
+    import torch
+    import torch.nn.functional as F
+    import speculative_decoding_verification_14_amd as sv
+    times = {"spec_lm_head": [], "torch_linear": []}
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            sv.lm_head(hidden, weight, logits, stream)
+            F.linear(hidden, weight)
+        for _ in range(rounds):
+            for name in times:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+                ev[0].record(stream)
+                for i in range(calls):
+                    if name == "spec_lm_head":
+                        sv.lm_head(hidden, weight, logits, stream)
+                    else:
+                        F.linear(hidden, weight)
+                    ev[i + 1].record(stream)
+                torch.cuda.synchronize()
+                times[name] += [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(calls)]
+    med = {k: float(sorted(v)[len(v) // 2]) for k, v in times.items()}
+    return dict(spec_lm_head_median_us=med["spec_lm_head"], torch_linear_median_us=med["torch_linear"],
+                spec_lm_head_min_us=min(times["spec_lm_head"]), torch_linear_min_us=min(times["torch_linear"]),
+                speedup=med["torch_linear"] / med["spec_lm_head"], calls_each=rounds * calls,
+                library_call="torch.nn.functional.linear(hidden, weight): bf16 logits, half the output bytes")
 
 
 def tree_shape(spec: str) -> tuple[int, int]:

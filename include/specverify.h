@@ -425,7 +425,9 @@ spec_status spec_commit_tree(void* k_cache, void* v_cache, const int32_t* block_
  * target_logits as written.
  *
  *  hidden  bf16 [R][H]   weight  bf16 [V][H]   logits  fp32 [R][V] (written)
- * Shapes: 1 <= R <= 65535 * 256; V >= 1; H a positive multiple of 128; V * H <= 2^40.
+ * Shapes: 1 <= R <= 65535 * 256; V >= 1; H a positive multiple of 128, at most 2^20;
+ * V * H <= 2^40; ceil(V / 256) rounded up to a multiple of 8, times ceil(R / 256), at
+ * most 2^23 (the workgroups of the launch).
  * One launch.
  * ---------------------------------------------------------------------- */
 spec_status spec_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

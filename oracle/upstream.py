@@ -137,3 +137,37 @@ def lm_head_error_bound(hidden, weight) -> np.ndarray:
     gamma = H * u / (1.0 - H * u)
     mag = np.abs(bf16_to_f64(hidden)) @ np.abs(bf16_to_f64(weight)).T
     return gamma * mag + u * mag
+
+
+def lm_head_stat_bound(hidden, weight, lam: float = 9.0, chunk: int = 64) -> np.ndarray:
+    """A probabilistic bound on the fp32 accumulation error of each logit, far tighter than
+    the worst case above.
+
+    Model: the device sums the H exact products t_k = hidden[r][k] W[v][k] with fp32
+    additions in some order, in blocks of at most `chunk` consecutive k (in any order inside
+    a block) whose running total may start at any block. Each addition a rounds its exact
+    result p_a by a factor (1 + d_a), |d_a| <= u = 2^-24, the d_a independent with mean zero
+    (round to nearest on data without structure). The error is then sum_a p_a d_a, and
+    Hoeffding's inequality gives |error| <= lam u sqrt(sum_a p_a^2) with probability at least
+    1 - 2 exp(-lam^2 / 2) (the approach of Higham and Mary, "A new approach to probabilistic
+    rounding error analysis", SIAM J. Sci. Comput. 41 (2019), applied with the partial sums
+    themselves instead of sum |t_k|). Every partial result is a difference of two prefix sums
+    S_i = t_0 + .. + t_{i-1} (wrapping past H adds S_H), plus at most one block's worth of
+    terms, so |p_a| <= P = 2 max_i |S_i| + |S_H| + max over blocks of sum |t_k|; there are at
+    most H additions, hence the bound lam u sqrt(H) P, plus u |S_H| for good measure.
+    lam = 9: a false alarm has probability below 1e-17 per logit."""
+    h = bf16_to_f64(hidden)
+    w = bf16_to_f64(weight)
+    R, H = h.shape
+    if H % chunk:
+        raise ValueError("H must be a multiple of the block length")
+    u = 2.0 ** -24
+    out = np.empty((R, w.shape[0]))
+    for r in range(R):
+        t = w * h[r]                                    # [V][H] exact products
+        S = np.cumsum(t, axis=1)
+        total = S[:, -1]
+        block = np.abs(t).reshape(t.shape[0], H // chunk, chunk).sum(axis=2).max(axis=1)
+        P = 2.0 * np.max(np.abs(S), axis=1) + np.abs(total) + block
+        out[r] = lam * u * np.sqrt(H) * P + u * np.abs(total)
+    return out

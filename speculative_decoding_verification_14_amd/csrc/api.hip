@@ -324,7 +324,8 @@ spec_status spec_lm_head(const void* hidden, const void* weight, float* logits, 
     if (!hidden || !weight || !logits) return SPEC_ERR_NULL_POINTER;
     if (R < 1 || R > 65535 * 256 || V < 1 || H < lm_head_k_multiple() || H % lm_head_k_multiple() != 0)
         return SPEC_ERR_BAD_SHAPE;
-    if (static_cast<long long>(V) * H > (1LL << 40)) return SPEC_ERR_BAD_SHAPE;
+    if (H > (1 << 20) || static_cast<long long>(V) * H > (1LL << 40) || !lm_head_grid_ok(R, V))
+        return SPEC_ERR_BAD_SHAPE;
     const spec_status s = check_device();
     if (s != SPEC_OK) return s;
     LmHeadLaunch p;

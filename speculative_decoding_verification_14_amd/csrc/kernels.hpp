@@ -118,7 +118,9 @@ struct LmHeadLaunch {
     int R, H, V;
 };
 
-int lm_head_k_multiple();   // H must be a multiple of this
+int lm_head_k_multiple();
+// false when the launch grid for R rows and V columns would exceed 2^23 workgroups
+bool lm_head_grid_ok(int R, int V);   // H must be a multiple of this
 hipError_t launch_lm_head(const LmHeadLaunch& p, hipStream_t stream);
 
 }  // namespace specverify

@@ -12,6 +12,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <utility>
+
 namespace specverify {
 namespace {
 
@@ -123,84 +125,134 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeArgs a) {
 //
 // logits[r][v] = sum_h hidden[r][h] W[v][h]: M = R rows (small: the verify rows),
 // N = V (large), K = H. The weight is the stream (1 GB at the 8B shape), so each
-// W element is loaded from HBM once, straight into MFMA registers; the hidden
-// rows, read by every workgroup, are staged through LDS.
+// W element is loaded from HBM once, straight into MFMA registers; the hidden rows,
+// read by every workgroup, are staged through LDS.
 //
-// Workgroup: NWM x NWN waves over a 256-row M block and NWN * 16 * NT vocabulary
-// columns; wave (wm, wn) owns row tiles wm * MT .. + MT - 1 (MT = 16 / NWM) and 16 NT
-// columns, so MT * NT v_mfma_f32_16x16x32_bf16 accumulators. K runs in chunks of 64.
-// Inside a chunk the k order is permuted (the same way for both operands, so the sum
-// is unchanged): lane group lg of MFMA step s holds k = 16 lg + 8 s + j, j < 8. A lane
-// then reads 32 contiguous bytes of a W row per chunk, and the four lane groups cover
-// the row's 128-byte line; the NWM waves that share columns read the same lines, the
-// later ones from the cache.
+// Workgroup: 8 waves over an MB-row block (MB = 64, 128 or 256) and 256 vocabulary
+// columns; each wave owns 32 columns (two 16-column tiles) and all MB rows, so
+// MB / 16 x 2 v_mfma_f32_16x16x32_bf16 accumulators, 128 registers at MB = 256, which
+// leaves room for two waves per SIMD. K runs in chunks of 64. Inside a chunk the k
+// order is permuted (the same way for both operands, so the sum is unchanged): lane
+// group lg of MFMA step s holds k = 16 lg + 8 s + j, j < 8, so that a lane reads 32
+// contiguous bytes of its W row per chunk and the four lane groups cover the row's
+// 128 bytes.
+//
+// The hidden rows reach LDS by buffer-to-LDS loads (no register staging) into two
+// slots. A chunk row is 128 bytes; its eight 16-byte pieces are stored XOR-swizzled by
+// (row / 2) % 8, so the 16 rows of a fragment read land in 16 distinct bank groups.
+// The slots are two separate LDS arrays, each named by a compile-time index: the
+// compiler can then tell a read of one slot from a load into the other, and waits only
+// for the latter's own loads instead of draining every load in flight before each read
+// (which, with one array, it did: that wait serialised the W prefetch). W is loaded two
+// chunks ahead of its MFMAs.
+//
+// Each workgroup starts its walk over the K chunks at its own chunk (5 x its column
+// block, wrapping): W rows lie 8 KB apart, and with every workgroup at the same chunk
+// the requests in flight share their low address bits and pile onto a few HBM
+// channels; staggering the start took the 8B-shape call from 331 us to 294 us.
 
-constexpr int kGemmM = 256;                    // rows per M block, at most
 constexpr int kGemmKC = 64;                    // K chunk
-constexpr int kAStride = kGemmKC * 2 + 16;     // LDS bytes per staged row (padded)
-// Loads of chunk j are issued RING chunks before the chunk that uses them, hidden
-// rows and W alternating in one order (hidden j, W j, hidden j+1, ...). Vector loads
-// complete in issue order, so the wait for a staged hidden chunk also covers the W
-// loads issued before it; with both rings equally deep that costs W no lead.
-
-constexpr int kLmRing = 2;
+constexpr int kLmWaves = 8;                    // waves per workgroup, one 32-column strip each
+constexpr int kLmNT = 2;                       // 16-column tiles per wave
+constexpr int kLmCols = kLmWaves * 16 * kLmNT; // columns per workgroup
+constexpr int kLmStagger = 5;                  // starting chunk = 5 x column block (mod chunks)
 
 struct GemmArgs {
     const uint16_t* A;   // [R][H]
     const uint16_t* W;   // [V][H]
     float* C;            // [R][V]
     int R, H, V;
+    int gx, gy;          // column blocks, row blocks
 };
 
-template <int NWM, int NWN, int NT, int RING, int MB>
-__global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) {
-    constexpr int kRing = RING;
-    static_assert(MB == 64 || MB == 128 || MB == 256, "M block: 64, 128 or 256 rows");
-    constexpr int kThreads = NWM * NWN * kWave;
-    constexpr int MT = MB / 16 / NWM;                     // row tiles per wave
-    constexpr int kCols = NWN * 16 * NT;                  // columns per workgroup
-    constexpr int AQ = MB * kGemmKC * 2 / 16 / kThreads;   // 16-byte pieces of the hidden chunk per thread
-    constexpr int kPartsPerRow = 8 / AQ;                  // threads per 128-byte chunk row
-    static_assert(AQ >= 1 && AQ * kPartsPerRow == 8 && MT * NWM * 16 == MB, "tile shape");
-    struct WChunk { uint4 w[NT][2]; };
-    struct AChunk { uint4 v[AQ]; };
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1, each with its index as a constant.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_a[2][MB * kAStride];
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave / NWN, wn = wave % NWN;
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds + 16 l
+// (the LDS address must be the same in every lane); a read past the buffer's size
+// yields zeros.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+template <int MB>
+__global__ __launch_bounds__(kLmWaves * kWave) void lm_head_kernel(GemmArgs a) {
+    static_assert(MB == 64 || MB == 128 || MB == 256, "M block: 64, 128 or 256 rows");
+    constexpr int NT = kLmNT;
+    constexpr int MT = MB / 16;                                    // row tiles per wave
+    constexpr int kChunkBytes = MB * kGemmKC * 2;
+    constexpr int kDma = kChunkBytes / (kWave * 16) / kLmWaves;    // 1 KB loads per wave per chunk
+    static_assert(kDma >= 1, "chunk split");
+    constexpr int kWOps = 2 * NT;                                  // W loads per wave per chunk
+    // Issue order: hidden chunk 0, W chunks 0 and 1, then per chunk c: wait, hidden chunk
+    // c + 1, MFMAs of c, W chunk c + 2. Between hidden chunk c and chunk c's wait come W
+    // chunk c + 1's loads alone (W chunks 0 and 1 for c = 0), and vector loads complete in
+    // issue order, so waiting until kWOps loads are outstanding completes hidden chunk c.
+    constexpr int kAfter = kWOps;
+    struct WChunk { uint4 w[NT][2]; };
+
+    // one array per slot, each addressed only through a compile-time slot number
+    __shared__ __attribute__((aligned(1024))) unsigned char s_a0[kChunkBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_a1[kChunkBytes];
+    auto slot = [&](auto S) __attribute__((always_inline)) -> unsigned char* {
+        if constexpr (decltype(S)::value == 0) return s_a0;
+        else return s_a1;
+    };
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int n0 = blockIdx.x * kCols + wn * 16 * NT;
-    const int m0 = blockIdx.y * MB;
-    const int chunks = a.H / kGemmKC;
+    // workgroup -> (column block, row block). Workgroups are dealt to the 8 XCDs in turn; the
+    // row blocks of one column block (R > 256) go to one XCD one after another, so that they
+    // tend to run together and find W in that XCD's L2.
+    const unsigned id = blockIdx.x, xcd = id % 8u, sx = id / 8u;
+    const int rb = static_cast<int>(sx % static_cast<unsigned>(a.gy));
+    const int cb = static_cast<int>(sx / static_cast<unsigned>(a.gy)) * 8 + static_cast<int>(xcd);
+    if (cb >= a.gx) return;   // padding of the grid to whole rounds of 8
+    const int n0 = cb * kLmCols + wave * 16 * NT;
+    const int m0 = rb * MB;
+    const int chunks = a.H / kGemmKC;   // even
+    const int k_start = static_cast<int>((static_cast<unsigned>(cb) * kLmStagger) % static_cast<unsigned>(chunks));
+    auto rot = [&](int kc) { kc += k_start; return kc >= chunks ? kc - chunks : kc; };
 
     // this lane's W rows (clamped into range: columns >= V are computed, never stored)
     const uint16_t* wrow[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int n = min(n0 + 16 * t + l16, a.V - 1);
-        wrow[t] = a.W + size_t(n) * a.H + 16 * lg;
-    }
+    for (int t = 0; t < NT; ++t) wrow[t] = a.W + size_t(min(n0 + 16 * t + l16, a.V - 1)) * a.H + 16 * lg;
     auto load_w = [&](WChunk& c, int kc) {
+        kc = rot(kc);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint16_t* p = wrow[t] + size_t(kc) * kGemmKC;
-            c.w[t][0] = load16_nt(p);
-            c.w[t][1] = load16_nt(p + 8);
+            c.w[t][0] = load16(p);
+            c.w[t][1] = load16(p + 8);
         }
     };
 
-    // hidden staging: thread -> (row, part of the 128-byte chunk row). Rows >= R stage a copy of
-    // row R-1: output row m depends on hidden row m alone, and rows >= R are never written out.
-    const int arow = tid / kPartsPerRow, apart = tid % kPartsPerRow;
-    const uint16_t* asrc = a.A + size_t(min(m0 + arow, a.R - 1)) * a.H + 8 * AQ * apart;
-    auto load_a = [&](AChunk& c, int kc) {
+    // hidden rows m0 .. m0 + MB - 1 through a buffer resource: rows >= R read as zero (their
+    // outputs are never stored). Load i of this wave fills LDS slots (wave kDma + i) 64 + lane:
+    // row r = slot / 8, physical piece slot % 8, holding logical piece (slot % 8) ^ ((r / 2) % 8).
+    const int rows_here = min(MB, a.R - m0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.A + size_t(m0) * a.H), static_cast<short>(0), rows_here * a.H * 2, 0x00020000);
+    int voff[kDma];
 #pragma unroll
-        for (int q = 0; q < AQ; ++q) c.v[q] = load16(asrc + size_t(kc) * kGemmKC + 8 * q);
-    };
-    auto store_a = [&](const AChunk& c, int buf) {
-        unsigned char* dst = s_a[buf] + arow * kAStride + 16 * AQ * apart;
+    for (int i = 0; i < kDma; ++i) {
+        const int r = (wave * kDma + i) * 8 + (lane >> 3);
+        voff[i] = r * a.H * 2 + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    }
+    auto dma = [&](int chunk, unsigned char* buf) {
+        const int kc = rot(min(chunk, chunks - 1));   // past the last chunk: a copy nobody reads
 #pragma unroll
-        for (int q = 0; q < AQ; ++q) *reinterpret_cast<uint4*>(dst + 16 * q) = c.v[q];
+        for (int i = 0; i < kDma; ++i)
+            load_to_lds16(ra, buf + (wave * kDma + i) * (kWave * 16), voff[i], kc * kGemmKC * 2);
     };
 
     f32x4 acc[MT][NT];
@@ -209,25 +261,25 @@ __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) 
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Every load is issued unconditionally (chunk indices clamped at the end; the extra loads
-    // re-read the last chunk and are never used), so the wait counts before each use are exact
-    // and never drain the loads still in flight. The prologue issues in the loop's own order, so
-    // the wait counts at the loop head are the same from both paths into it.
-    WChunk wr[kRing];
-    AChunk ar[kRing];
-#pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-        load_a(ar[j], min(j, chunks - 1));
-        load_w(wr[j], min(j, chunks - 1));
-    }
-    store_a(ar[0], 0);
-    __syncthreads();
+    WChunk wr[2];
+    dma(0, s_a0);
+    load_w(wr[0], 0);
+    load_w(wr[1], min(1, chunks - 1));
 
-    for (int c0 = 0; c0 < chunks; c0 += kRing) {   // chunks is a multiple of kRing
-#pragma unroll
-        for (int u = 0; u < kRing; ++u) {
+    // fragment reads: row 16 mt + l16, logical pieces 2 lg and 2 lg + 1
+    const int sw = (l16 >> 1) & 7;
+    const int rd0 = l16 * 128 + (((2 * lg) ^ sw) << 4);
+    const int rd1 = l16 * 128 + (((2 * lg + 1) ^ sw) << 4);
+
+    for (int c0 = 0; c0 < chunks; c0 += 2) {
+        static_for<2>([&](auto U) __attribute__((always_inline)) {
+            constexpr int u = decltype(U)::value;
             const int c = c0 + u;
-            const unsigned char* abase = s_a[c & 1] + (wm * MT * 16 + l16) * kAStride + 32 * lg;
+            // this wave's loads of chunk c have landed and its reads of chunk c - 1 are done; after
+            // the barrier, every wave's are, so chunk c is readable and c - 1's slot refillable
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAfter) : "memory");
+            dma(c + 1, slot(std::integral_constant<int, 1 - u>{}));
+            const unsigned char* buf = slot(std::integral_constant<int, u>{});
             const WChunk& w = wr[u];
             // A fragments read kPF row tiles ahead of their MFMAs (the order pinned), so the LDS
             // latency overlaps the MFMAs of the tiles before
@@ -235,36 +287,35 @@ __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) 
             uint4 af[kPF][2];
 #pragma unroll
             for (int j = 0; j < kPF; ++j) {
-                const unsigned char* ap = abase + j * 16 * kAStride;
-                af[j][0] = *reinterpret_cast<const uint4*>(ap);
-                af[j][1] = *reinterpret_cast<const uint4*>(ap + 16);
+                af[j][0] = *reinterpret_cast<const uint4*>(buf + j * 2048 + rd0);
+                af[j][1] = *reinterpret_cast<const uint4*>(buf + j * 2048 + rd1);
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const uint4 a0 = af[mt % kPF][0], a1 = af[mt % kPF][1];
                 if (mt + kPF < MT) {
-                    const unsigned char* ap = abase + (mt + kPF) * 16 * kAStride;
-                    af[mt % kPF][0] = *reinterpret_cast<const uint4*>(ap);
-                    af[mt % kPF][1] = *reinterpret_cast<const uint4*>(ap + 16);
+                    af[mt % kPF][0] = *reinterpret_cast<const uint4*>(buf + (mt + kPF) * 2048 + rd0);
+                    af[mt % kPF][1] = *reinterpret_cast<const uint4*>(buf + (mt + kPF) * 2048 + rd1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                // step 0 of every tile, then step 1: back-to-back MFMAs on one accumulator stall
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
+                for (int t = 0; t < NT; ++t)
                     acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(w.w[t][0]),
                                                                         acc[mt][t], 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
                     acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(w.w[t][1]),
                                                                         acc[mt][t], 0, 0, 0);
-                }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            load_a(ar[u], min(c + kRing, chunks - 1));
-            load_w(wr[u], min(c + kRing, chunks - 1));
-            store_a(ar[(u + 1) % kRing], (c + 1) & 1);   // after the last chunk: a copy nobody reads
-            __syncthreads();
-        }
+            load_w(wr[u], min(c + 2, chunks - 1));
+        });
     }
+    // the surplus loads past the last chunk land before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // C tile: lane holds rows 16 (wm MT + mt) + 4 lg + e of column n0 + 16 t + l16
+    // C tile: lane holds rows 16 mt + 4 lg + e of column n0 + 16 t + l16
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int n = n0 + 16 * t + l16;
@@ -273,7 +324,7 @@ __global__ __launch_bounds__(NWM * NWN * kWave) void lm_head_kernel(GemmArgs a) 
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int m = m0 + 16 * (wm * MT + mt) + 4 * lg + e;
+                const int m = m0 + 16 * mt + 4 * lg + e;
                 if (m < a.R) a.C[size_t(m) * a.V + n] = acc[mt][t][e];
             }
     }
@@ -306,7 +357,14 @@ hipError_t launch_rope_append(const RopeLaunch& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int lm_head_k_multiple() { return kGemmKC * kLmRing; }
+int lm_head_k_multiple() { return 2 * kGemmKC; }
+
+bool lm_head_grid_ok(int R, int V) {
+    const long long mb = R <= 64 ? 64 : (R <= 128 ? 128 : 256);
+    const long long gx = (static_cast<long long>(V) + kLmCols - 1) / kLmCols;
+    const long long gy = (R + mb - 1) / mb;
+    return (gx + 7) / 8 * 8 * gy <= (1LL << 23);
+}
 
 hipError_t launch_lm_head(const LmHeadLaunch& p, hipStream_t stream) {
     GemmArgs a;
@@ -316,17 +374,17 @@ hipError_t launch_lm_head(const LmHeadLaunch& p, hipStream_t stream) {
     a.R = p.R;
     a.H = p.H;
     a.V = p.V;
-    // one row of 8 waves, two 16-column tiles each (256 columns per workgroup), rings of two; the
-    // M block is the smallest of 64, 128 and 256 rows that holds R (256-row blocks beyond that)
-    constexpr int WM = 1, WN = 8, NT = 2, RING = kLmRing;
-    const int gx = (p.V + WN * 16 * NT - 1) / (WN * 16 * NT);
-    if (p.R <= 64)
-        hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING, 64>), dim3(gx, 1), dim3(WM * WN * kWave), 0, stream, a);
-    else if (p.R <= 128)
-        hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING, 128>), dim3(gx, 1), dim3(WM * WN * kWave), 0, stream, a);
+    // the M block is the smallest of 64, 128 and 256 rows that holds R (256-row blocks beyond that)
+    const int mb = p.R <= 64 ? 64 : (p.R <= 128 ? 128 : 256);
+    a.gx = (p.V + kLmCols - 1) / kLmCols;
+    a.gy = (p.R + mb - 1) / mb;
+    const dim3 grid(static_cast<unsigned>((a.gx + 7) / 8) * 8u * static_cast<unsigned>(a.gy));
+    if (mb == 64)
+        hipLaunchKernelGGL(lm_head_kernel<64>, grid, dim3(kLmWaves * kWave), 0, stream, a);
+    else if (mb == 128)
+        hipLaunchKernelGGL(lm_head_kernel<128>, grid, dim3(kLmWaves * kWave), 0, stream, a);
     else
-        hipLaunchKernelGGL((lm_head_kernel<WM, WN, NT, RING, kGemmM>), dim3(gx, (p.R + kGemmM - 1) / kGemmM),
-                           dim3(WM * WN * kWave), 0, stream, a);
+        hipLaunchKernelGGL(lm_head_kernel<256>, grid, dim3(kLmWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
 

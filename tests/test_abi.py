@@ -129,6 +129,7 @@ def test_rope_append_validation(lib, over, code):
     ((NULL, FAKE, FAKE, 4, 256, 100), 1), ((FAKE, FAKE, NULL, 4, 256, 100), 1),
     ((FAKE, FAKE, FAKE, 0, 256, 100), 2), ((FAKE, FAKE, FAKE, 4, 64, 100), 2), ((FAKE, FAKE, FAKE, 4, 320, 100), 2),
     ((FAKE, FAKE, FAKE, 4, 256, 0), 2), ((FAKE, FAKE, FAKE, 4, 1 << 24, 1 << 17), 2),
+    ((FAKE, FAKE, FAKE, 4, 1 << 21, 100), 2), ((FAKE, FAKE, FAKE, 65535 * 256, 128, 1 << 20), 2),
 ])
 def test_lm_head_validation(lib, args, code):
     assert lib.spec_lm_head(*args, NULL) == code

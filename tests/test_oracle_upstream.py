@@ -172,3 +172,46 @@ def test_lm_head_orientation_and_rounding_bound():
     for h in range(H):
         seq += prods[:, :, h]
     assert np.all(np.abs(seq.astype(np.float64) - exact) <= bound)
+
+
+def _fp32_blocked_sum(prods: np.ndarray, block: int, start_block: int, perm: np.ndarray) -> np.ndarray:
+    """fp32 sum over the last axis the way a blocked device sum runs: blocks of `block` terms
+    from block `start_block` on (wrapping), each block's terms added in the order `perm`."""
+    n = prods.shape[-1]
+    nb = n // block
+    acc = np.zeros(prods.shape[:-1], dtype=np.float32)
+    for bi in range(nb):
+        b = (start_block + bi) % nb
+        for j in perm:
+            acc = (acc + prods[..., b * block + j]).astype(np.float32)
+    return acc
+
+
+def test_lm_head_stat_bound_holds_for_fp32_sums_and_catches_a_lost_block():
+    """The statistical bound against fp32 sums actually carried out in float32 (numpy adds
+    rounded to nearest): sequential, blocked with a permuted order inside the block, and
+    rotated to start at another block; it is much tighter than the worst-case bound, and a
+    sum that loses one block of terms, or adds one block twice, breaks it."""
+    rng = np.random.default_rng(11)
+    R, H, V = 6, 1024, 40
+    hid = oup.f64_to_bf16(rng.standard_normal((R, H)))
+    w = oup.f64_to_bf16(rng.standard_normal((V, H)) * 0.05)
+    w[3] = oup.f64_to_bf16(np.abs(rng.standard_normal(H)) * 0.05)     # one same-sign column
+    exact = oup.lm_head(hid, w)
+    stat = oup.lm_head_stat_bound(hid, w)
+    worst = oup.lm_head_error_bound(hid, w)
+    prods = (oatt.bf16_to_f64(hid)[:, None, :] * oatt.bf16_to_f64(w)[None, :, :]).astype(np.float32)
+    assert np.array_equal(prods.astype(np.float64),
+                          oatt.bf16_to_f64(hid)[:, None, :] * oatt.bf16_to_f64(w)[None, :, :])   # exact in fp32
+    perm = np.array([16 * g + 8 * s + j for s in range(2) for g in range(4) for j in range(8)])
+    orders = [_fp32_blocked_sum(prods, H, 0, np.arange(H)),          # sequential
+              _fp32_blocked_sum(prods, 64, 0, perm),
+              _fp32_blocked_sum(prods, 64, 5, perm)]
+    for got in orders:
+        err = np.abs(got.astype(np.float64) - exact)
+        assert np.all(err <= stat)
+    assert np.all(stat < worst) and np.median(worst / stat) >= 10.0
+    lost = orders[1].astype(np.float64) - prods[..., 64:128].astype(np.float64).sum(axis=-1)
+    twice = orders[1].astype(np.float64) + prods[..., 64:128].astype(np.float64).sum(axis=-1)
+    for bad in (lost, twice):
+        assert np.mean(np.abs(bad - exact) > stat) > 0.9
