@@ -315,7 +315,8 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lm_head_kernel(GemmArgs a) {
     // the surplus loads past the last chunk land before the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // C tile: lane holds rows 16 mt + 4 lg + e of column n0 + 16 t + l16
+    // C tile: lane holds rows 16 mt + 4 lg + e of column n0 + 16 t + l16; streaming stores (the
+    // logits are written once here and read once by the sampler, from HBM either way)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int n = n0 + 16 * t + l16;
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lm_head_kernel(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = m0 + 16 * mt + 4 * lg + e;
-                if (m < a.R) a.C[size_t(m) * a.V + n] = acc[mt][t][e];
+                if (m < a.R) __builtin_nontemporal_store(acc[mt][t][e], a.C + size_t(m) * a.V + n);
             }
     }
 }
