@@ -57,7 +57,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-EVENT_EVERY = 1     # per-call events on every timed step (a few microseconds of records per step)
 EVENT_STEPS = 30    # at least this many steps with per-call events for the averages
 METRIC = "verified tokens/s + HBM GB/s (% of peak) for spec verify, 8B shape, k=3"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_counters.txt")
@@ -95,6 +94,30 @@ def algorithmic_bytes(preset, seq_lens, num_accepted, draft_lens=None):
                  + (0 if draft_lens is None else (B + 1) * 4))
     commit = int(B * 4 * 3)
     return attn, reject, commit
+
+
+def event_steps(step, n_events: int, steps: int) -> dict:
+    """Per-call HIP events from a loop of its own, after the wall-clock loop: every event record
+    leaves a bubble of a few microseconds, which belongs in the per-call averages but not in
+    the wall-clock step time. At least EVENT_STEPS steps."""
+    import torch
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+           for i in range(max(EVENT_STEPS, min(steps, 100)))}
+    for e in evs.values():
+        step(e)
+    torch.cuda.synchronize()
+    return evs
+
+
+def reject_read_figure(B: int, k: int, V: int, seconds: float, algorithmic: int) -> dict:
+    """How the sampling call ran this shape (spec_reject_sample_plan) and the logits bytes it
+    read: the examined rows (the algorithmic count) when the levels run one after another,
+    all 2k + 1 rows of every sequence when they run at once (small batches)."""
+    import speculative_decoding_verification_14_amd as sv
+    mode = sv.reject_sample_plan(B, k, V)
+    read = B * (2 * k + 1) * V * 4 if mode == 2 else algorithmic
+    gbs = read / seconds / 1e9
+    return dict(launch=sv.REJECT_PLANS[mode], bytes_read=read, gbs_read=gbs, frac_of_peak_read=gbs / HBM_PEAK_GBS)
 
 
 def dense_reject_figure(preset, seconds: float) -> dict:
@@ -489,14 +512,13 @@ def gpu_bench_ragged(args, p, dev) -> dict:
         step()
     torch.cuda.synchronize()
     acc_ref = num_acc.cpu().numpy().copy()
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs.get(i))
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    evs = event_steps(step, 4, args.steps)
     acc = num_acc.cpu().numpy()
     if not np.array_equal(acc, acc_ref):
         raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
@@ -604,15 +626,14 @@ def gpu_bench_fused(args, p, dev) -> dict:
         step()
     torch.cuda.synchronize()
     acc_ref = num_acc.cpu().numpy().copy()
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(6)] for i in sampled}
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs.get(i))
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    evs = event_steps(step, 6, args.steps)
     acc = num_acc.cpu().numpy()
     if not np.array_equal(acc, acc_ref):
         raise RuntimeError("accepted lengths changed between steps; the step is not repeatable")
@@ -756,15 +777,14 @@ def gpu_bench_tree(args, p, dev) -> dict:
         step()
     torch.cuda.synchronize()
     acc_ref = num_acc.cpu().numpy().copy()
-    sampled = list(range(0, args.steps, EVENT_EVERY))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs.get(i))
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    evs = event_steps(step, 4, args.steps)
     acc = num_acc.cpu().numpy()
     nodes = acc_nodes.cpu().numpy()
     if not np.array_equal(acc, acc_ref):
@@ -957,7 +977,8 @@ def gpu_bench(args) -> dict:
             reject_sample=dict(avg_us=rej_avg_s * 1e6, median_us=med(rej_ms) * 1e3,
                                p10_us=pct(rej_ms, 0.1) * 1e3, p90_us=pct(rej_ms, 0.9) * 1e3, bytes=r_bytes, gbs=rej_gbs,
                                frac_of_peak=rej_gbs / HBM_PEAK_GBS,
-                               dense_equivalent=dense_reject_figure(p, rej_avg_s)),
+                               dense_equivalent=dense_reject_figure(p, rej_avg_s),
+                               read=reject_read_figure(p.B, p.k, p.V, rej_avg_s, r_bytes)),
             commit_lengths=dict(avg_us=com_avg_s * 1e6, bytes=c_bytes)),
         event_sum_ms_per_step=(attn_avg_s + rej_avg_s + com_avg_s) * 1e3,
         event_timed_steps=len(evs),
@@ -1040,13 +1061,12 @@ def gpu_bench_sweep(args, p, dev) -> dict:
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        sampled = list(range(0, args.steps, EVENT_EVERY))
-        evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
         w0 = time.perf_counter()
         for i in range(args.steps):
-            step(evs.get(i))
+            step()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - w0) / args.steps
+        evs = event_steps(step, 4, args.steps)
         mean = lambda v: sum(v) / len(v)
         attn_s = mean([e[0].elapsed_time(e[1]) for e in evs.values()]) / 1e3
         rej_s = mean([e[1].elapsed_time(e[2]) for e in evs.values()]) / 1e3
@@ -1059,7 +1079,8 @@ def gpu_bench_sweep(args, p, dev) -> dict:
                            verify_attn=dict(avg_us=attn_s * 1e6, bytes=a_bytes,
                                             frac_of_peak=a_bytes / attn_s / 1e9 / HBM_PEAK_GBS),
                            reject_sample=dict(avg_us=rej_s * 1e6, bytes=r_bytes,
-                                              frac_of_peak=r_bytes / rej_s / 1e9 / HBM_PEAK_GBS),
+                                              frac_of_peak=r_bytes / rej_s / 1e9 / HBM_PEAK_GBS,
+                                              read=reject_read_figure(Bs, k, p.V, rej_s, r_bytes)),
                            commit_lengths=dict(avg_us=com_s * 1e6)))
         print(f"[bench] B={Bs}: {tokens / wall:.0f} tokens/s, attn {attn_s * 1e6:.1f} us, "
               f"reject {rej_s * 1e6:.1f} us", file=sys.stderr, flush=True)

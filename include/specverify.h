@@ -45,7 +45,8 @@
  *  - spec_reject_sample takes a workspace (and spec_reject_sample_workspace_size
  *    sizes it): the workgroups that share a sequence's vocabulary exchange partial
  *    statistics through it while the kernel runs.
- *  - spec_reject_error_flag reports whether a sampling call had to give up a wait.
+ *  - spec_reject_error_flag reports whether a sampling call had to give up a wait;
+ *    spec_reject_sample_plan says which way a sampling call of a given shape runs.
  *  - Ragged draft lengths, tree verification and the upstream steps (RoPE with the
  *    KV append, the LM head) have calls of their own.
  *
@@ -255,6 +256,19 @@ spec_status spec_reject_sample_noalloc(const float* target_logits, const float* 
  * path in tests.
  * ---------------------------------------------------------------------- */
 spec_status spec_reject_error_flag(void* workspace, int32_t* flag_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * How spec_reject_sample (or _ragged, with k = the largest k_b) runs a call of
+ * shape (B, k, V) on the current device, so that a caller can account for the rows
+ * it reads (see "Rows read" under spec_reject_sample):
+ *   *mode_out = 0  the levels one after another, workgroups of 512 threads
+ *               (rows after a sequence's first rejection are not read);
+ *   *mode_out = 1  the same with workgroups of 256 threads;
+ *   *mode_out = 2  every level of every sequence at once (all 2k+1 rows read).
+ * Host only: enqueues nothing. Errors: SPEC_ERR_NULL_POINTER, SPEC_ERR_BAD_SHAPE
+ * (the shape spec_reject_sample accepts), SPEC_ERR_HIP / SPEC_ERR_NO_DEVICE.
+ * ---------------------------------------------------------------------- */
+spec_status spec_reject_sample_plan(int32_t B, int32_t k, int32_t V, int32_t* mode_out);
 
 /* ------------------------------------------------------------------------
  * Rejection sampling with ragged draft lengths  [EFR] (acceptance-aware draft

@@ -19,7 +19,7 @@ __all__ = ["SpecError", "library", "verify_attn", "verify_attn_workspace_size", 
            "reject_sample_workspace_size", "commit_lengths", "verify_step", "verify_attn_ragged",
            "reject_sample_ragged", "verify_attn_tree", "reject_sample_tree", "reject_sample_tree_workspace_size",
            "commit_tree", "rope_append", "lm_head", "reject_error_flag", "reject_workspace",
-           "reject_sample_noalloc",
+           "reject_sample_noalloc", "reject_sample_plan", "REJECT_PLANS",
            "LIB_PATH", "SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -48,6 +48,7 @@ SYMBOLS = {
     "spec_rope_append": (_c_int32, [_vp] * 8 + [_c_int32] * 8 + [ctypes.c_double, _vp]),
     "spec_lm_head": (_c_int32, [_vp] * 3 + [_c_int32] * 3 + [_vp]),
     "spec_reject_error_flag": (_c_int32, [_vp, _vp, _vp]),
+    "spec_reject_sample_plan": (_c_int32, [_c_int32] * 3 + [ctypes.POINTER(_c_int32)]),
     "spec_reject_sample_noalloc": (_c_int32, [_vp] * 5 + [_c_int32] * 3 + [ctypes.c_float, ctypes.c_uint64]
                                    + [_vp] * 5),
 }
@@ -135,6 +136,17 @@ def reject_sample_workspace_size(B, k, V) -> int:
     n = _c_size(0)
     _check(library().spec_reject_sample_workspace_size(B, k, V, ctypes.byref(n)), "spec_reject_sample_workspace_size")
     return n.value
+
+
+REJECT_PLANS = {0: "chain, 512-thread workgroups", 1: "chain, 256-thread workgroups", 2: "every level at once"}
+
+
+def reject_sample_plan(B, k, V) -> int:
+    """spec_reject_sample_plan: 0 / 1 = the levels one after another (512- / 256-thread
+    workgroups), 2 = every level of every sequence at once (all 2k+1 rows read)."""
+    m = _c_int32(-1)
+    _check(library().spec_reject_sample_plan(B, k, V, ctypes.byref(m)), "spec_reject_sample_plan")
+    return m.value
 
 
 def verify_attn(q, k_cache, v_cache, block_table, seq_lens, out, max_seq_len: int, sm_scale: float | None = None,

@@ -269,6 +269,16 @@ spec_status spec_reject_error_flag(void* workspace, int32_t* flag_out, void* str
     return from_hip(launch_reject_error_flag(workspace, flag_out, static_cast<hipStream_t>(stream)));
 }
 
+spec_status spec_reject_sample_plan(int32_t B, int32_t k, int32_t V, int32_t* mode_out) {
+    if (!mode_out) return SPEC_ERR_NULL_POINTER;
+    if (B < 1 || B > 65535 || k < 0 || k > 15 || V < 2 || V > (1 << 20)) return SPEC_ERR_BAD_SHAPE;
+    const spec_status s = check_device();
+    if (s != SPEC_OK) return s;
+    const RejectPlan plan = reject_plan(B, k, V);
+    *mode_out = plan.levels ? 2 : (plan.W == 4 ? 1 : 0);
+    return SPEC_OK;
+}
+
 spec_status spec_commit_lengths(int32_t* seq_lens, const int32_t* num_accepted, int32_t B, int32_t k,
                                 int32_t capacity_tokens, int32_t* overflow_flags, void* stream) {
     if (!seq_lens || !num_accepted) return SPEC_ERR_NULL_POINTER;

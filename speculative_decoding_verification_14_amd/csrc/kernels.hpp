@@ -69,6 +69,13 @@ struct RejectLaunch {
 size_t reject_workspace_bytes(int B, int k, int V);
 int reject_max_vocab();   // largest V the reject kernel accepts
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream);
+// How launch_reject runs a call of this shape on the current device: every level of every
+// sequence at once, or the chain with W-wavefront workgroups (W = 4 or 8).
+struct RejectPlan {
+    bool levels;
+    int W;
+};
+RejectPlan reject_plan(int B, int k, int V);
 // The library's own sampling workspace for callers that cannot allocate: its size, and the
 // current device's copy (looked up on the first call on each device; allocates nothing).
 size_t reject_noalloc_scratch_bytes();

@@ -1870,24 +1870,37 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
 // resident at once (the groups wait for each other's decisions). If the device
 // would not hold them all, the chain with the same workgroups runs instead (the
 // same bits).
+// Workgroups of the level kernel the current device holds at once (-1 if the device
+// cannot be queried).
 template <bool kVec4>
-hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
+int levels_capacity() {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    // Every group waits for the decisions of the levels before it, so all of them
-    // must be resident at once: the kernel's own occupancy decides.
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return -1;
+    }
     static DeviceMemo memo;
     int wgs = memo.get(dev);
     if (wgs <= 0) {
         int per_cu = 0, cus = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_levels_kernel<kVec4, 4>, 4 * kWave, 0);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_levels_kernel<kVec4, 4>, 4 * kWave, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return -1;
+        }
         wgs = per_cu * cus;
         memo.put(dev, wgs);
     }
+    return wgs;
+}
+
+template <bool kVec4>
+hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
+    // Every group waits for the decisions of the levels before it, so all of them
+    // must be resident at once: the kernel's own occupancy decides.
+    const int wgs = levels_capacity<kVec4>();
+    if (wgs < 0) return hipErrorInvalidDevice;
     if (static_cast<long long>(a.B) * (a.k + 1) * a.Q > wgs) return launch_variant<kVec4, false, 4>(a, stream);
     a.groups = a.B * (a.k + 1);
     hipLaunchKernelGGL((reject_levels_kernel<kVec4, 4>), dim3(a.groups * a.Q), dim3(4 * kWave), 0, stream, a);
@@ -1987,6 +2000,22 @@ hipError_t launch_reject_error_flag(void* workspace, int32_t* flag_out, hipStrea
     return hipGetLastError();
 }
 
+RejectPlan reject_plan(int B, int k, int V) {
+    const int cus = device_cus();
+    const long long q4 = groups_of(V, 4), q8 = groups_of(V, 8);
+    const long long level_cap = static_cast<long long>(cus) * (k <= 3 ? 2 : 1);
+    RejectPlan r;
+    r.levels = k >= 1 && cus > 0 && static_cast<long long>(B) * (k + 1) * q4 <= level_cap;
+    const bool one_round8 = static_cast<long long>(B) * q8 <= cus;
+    const bool own_cu4 = static_cast<long long>(B) * q4 <= cus;
+    r.W = (r.levels || own_cu4 || !one_round8) ? 4 : 8;
+    if (r.levels) {   // the level kernel's own residency decides in the end (launch_levels)
+        const int wgs = (V % 4) == 0 ? levels_capacity<true>() : levels_capacity<false>();
+        if (wgs <= 0 || static_cast<long long>(B) * (k + 1) * groups_of(V, 4) > wgs) r.levels = false;
+    }
+    return r;
+}
+
 hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
     // The levels of each sequence at once when all of them fit one workgroup per CU,
@@ -2001,13 +2030,9 @@ hipError_t launch_reject(const RejectLaunch& p, hipStream_t stream) {
     // different sequences share each CU (152K vocabulary, B = 256, inside the full
     // step: 210 us instead of 215 us; at B = 64 the same time). The outputs do not
     // depend on it.
-    const int cus = device_cus();
-    const long long q4 = groups_of(p.V, 4), q8 = groups_of(p.V, 8);
-    const long long level_cap = static_cast<long long>(cus) * (p.k <= 3 ? 2 : 1);
-    const bool levels = p.k >= 1 && cus > 0 && static_cast<long long>(p.B) * (p.k + 1) * q4 <= level_cap;
-    const bool one_round8 = static_cast<long long>(p.B) * q8 <= cus;
-    const bool own_cu4 = static_cast<long long>(p.B) * q4 <= cus;
-    const int W = (levels || own_cu4 || !one_round8) ? 4 : 8;
+    const RejectPlan plan = reject_plan(p.B, p.k, p.V);
+    const bool levels = plan.levels;
+    const int W = plan.W;
     const int Q = groups_of(p.V, W);
     if (Q > kMaxQ) return hipErrorInvalidValue;
     const RejectLayout lay = reject_layout(p.B, p.k, U);

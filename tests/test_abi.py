@@ -169,6 +169,16 @@ def test_error_flag_validation(lib):
     assert lib.spec_reject_error_flag(FAKE, NULL, NULL) == 1
 
 
+def test_reject_plan_validation(lib):
+    m = ctypes.c_int32(-1)
+    assert lib.spec_reject_sample_plan(64, 3, 128256, None) == 1
+    for B, k, V in [(0, 3, 1000), (65536, 3, 1000), (4, 16, 1000), (4, -1, 1000), (4, 3, 1), (4, 3, (1 << 20) + 1)]:
+        assert lib.spec_reject_sample_plan(B, k, V, ctypes.byref(m)) == 2
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.spec_reject_sample_plan(64, 3, 128256, ctypes.byref(m)) == 5
+
+
 def test_concurrent_host_threads(lib):
     """Eight host threads call every entry point at once, with invalid and valid host arguments
     (valid ones end at the device check on a host without a GPU). The library's only shared state
