@@ -597,6 +597,7 @@ struct SampRes {
     int owner;         // wavefront holding the crossing unit, -1 if in another workgroup
     unsigned flags;    // kSampUseP, kSampExact, kSampError
     double run, t, Z1, Z2;
+    double W;          // a residual round: the residual's mass sum max(0, p - q)
 };
 template <int W>
 struct SharedT {
@@ -756,17 +757,16 @@ __device__ __forceinline__ void emit_chain(const RejectArgs& a, const SeqCtx& s,
     a.num_accepted[s.b] = row;
 }
 
-// Draw from the weights of this unit (residual of row `row`; p_row when `use_p` or
-// for the bonus row), given the running sum `run` before this unit and the
-// target t. Only the wavefront owning the crossing unit calls this; the lane
-// holding the drawn token writes it, its probability and the padding of the
-// sequence's outputs.
-template <bool kVec4>
-__device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, int row, bool two_rows,
+// Draw from the weights of this unit (the residual of rows prow, qrow; p when `use_p`
+// or for the bonus row), given the running sum `run` before this unit and the
+// target t. Only the wavefront owning the crossing unit calls this; emit(y, p(y))
+// runs on the lane holding the drawn token.
+template <bool kVec4, typename E>
+__device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s, bool two_rows,
                                            const float* prow, const float* qrow, const SampleCtx& c,
                                            const LoadSums& ls, bool use_p, bool exact, double run, double t,
                                            double invZp, double invZq, double Zp_true, double wscale,
-                                           double M_ref) {
+                                           double M_ref, E&& emit) {
     // wscale maps this unit's weights onto the scale of run and t (1, except for
     // the bonus row, whose unit weights are relative to the unit's own maximum);
     // M_ref is the row maximum the emitted probability is taken against.
@@ -800,7 +800,7 @@ __device__ __forceinline__ void final_scan(const RejectArgs& a, const SeqCtx& s,
     int y;
     float zy;
     if (!scan_unit<kVec4>(a, s, prow, qrow, two_rows, exact, run, t, lv, wf, y, zy)) return;
-    emit_chain(a, s, row, y, exp_nonpos_f64((static_cast<double>(zy) - M_ref) * c.invT64) / Zp_true);
+    emit(y, exp_nonpos_f64((static_cast<double>(zy) - M_ref) * c.invT64) / Zp_true);
 }
 
 // Reads wave 0's sampling decision and runs the final scan in the owning
@@ -824,16 +824,9 @@ __device__ __forceinline__ bool read_samp(const RejectArgs& a, const SeqCtx& s, 
     return true;
 }
 
-// Sampling from the residual of row `row` after its draft was rejected; `st`
-// holds the chain statistics of that row. Each wavefront turns its unit (still in
-// registers) into weights; wave 0 sums the workgroup's units by quads, one
-// exchange gives it every quad's sums, it finds the crossing quad and, if that is
-// its workgroup's, the crossing unit, whose wavefront then scans it for the token.
-template <bool kVec4, typename SH>
-__device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s, int row, const f4 (&xp)[kVecs],
-                                           const f4 (&xq)[kVecs], const RowStats& st, SH& sh) {
-    const float* prow = s.prow_base + size_t(row) * a.V;
-    const float* qrow = s.qrow_base + size_t(row) * a.V;
+// SampleCtx of a row pair from its chain statistics: the normalisers the residual
+// support and the heavy thresholds are judged with.
+__device__ __forceinline__ SampleCtx residual_ctx(const RejectArgs& a, const RowStats& st) {
     SampleCtx c;
     c.Mp = st.Mp;
     c.Mq = st.Mq;
@@ -844,10 +837,27 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
     c.tp = heavy_threshold(st.Mp, st.Zp, a.T);
     c.tq = heavy_threshold(st.Mq, st.Zq, a.T);
     c.dn = ln_approx(st.Zp) - ln_approx(st.Zq);
+    return c;
+}
 
+// The residual round of a rejected candidate's rows p = prow, q = qrow (still in
+// registers). Each wavefront turns its unit into the sums A, B of a and b over the
+// support {p > q} (judged with the chain statistics in c) and the totals P, Q; wave 0
+// sums the workgroup's units by quads, and one exchange gives every workgroup all
+// quads' sums, hence the exact normalisers Z_p = sum P, Z_q = sum Q and the residual's
+// mass W = sum over quads of max(0, A/Z_p - B/Z_q). With `draw` the draw follows: u_smp
+// at position L + 1 + pos, from the residual, or from p when it sums to zero; the
+// workgroup holding the crossing quad finds the crossing unit, whose wavefront scans it,
+// and emit(y, p(y)) runs on the lane holding the token. Returns false if a wait gave up
+// (the error is flagged); Zp, Zq and W come back in every wavefront.
+template <bool kVec4, typename SH, typename E>
+__device__ __forceinline__ bool residual_round(const RejectArgs& a, const SeqCtx& s, const float* prow,
+                                               const float* qrow, int pos, unsigned long long* slots,
+                                               const f4 (&xp)[kVecs], const f4 (&xq)[kVecs], const SampleCtx& c,
+                                               SH& sh, bool draw, E&& emit, double& Zp_out, double& Zq_out,
+                                               double& W_out) {
     const int lane = lane_id();
     const UnitSums us = unit_sums<kVec4, true>(xp, xq, c, prow, qrow, a.V, s.u * kUnit + lane * 4, sh.ls[s.wave]);
-    unsigned long long* slots = a.samp_slots + size_t(s.b) * a.U * kSampSlots;
     if (lane == 0) sh.usum[s.wave] = make_double4(us.A, us.B, us.P, us.Q);
     __syncthreads();
     if (s.wave == 0) {
@@ -864,7 +874,7 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
             publish_quads(slots, pay, s.epoch, s.q * (SH::kW / kQuad), SH::kW, nq);
         }
         double u_acc, u_smp;
-        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + row, &u_acc, &u_smp);
+        verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[kSampSlots];
         const bool ok = gather<kSampSlots>(slots, nq, s.epoch, a.spin, v);
         // lane l < nq: quad l's sums (zero in the other lanes)
@@ -874,27 +884,30 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
         const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
         double Rg = fmax(0.0, Ag * invZp - Bg * invZq);
         double total = dpp_wave_sum(Rg);
+        const double W = total;
         bool use_p = false;
-        if (!(total > 0.0)) {      // zero residual: draw from p_j instead
+        if (!(total > 0.0)) {      // zero residual: draw from p instead
             use_p = true;
             Rg = Pg;
             total = Zp;
         }
         const double t = u_smp * total;
-        double run;
-        bool exact;
-        const int qstar = find_crossing(Rg, 0.0, t, run, exact);
+        double run = 0.0;
+        bool exact = false;
         int owner = -1;
-        if (qstar / (SH::kW / kQuad) == s.q) {   // the crossing quad is this workgroup's: find its unit
-            const int j = qstar % (SH::kW / kQuad);
-            double Ru = 0.0;
-            if (lane < kQuad) {
-                const double4 v4 = sh.usum[kQuad * j + lane];
-                Ru = use_p ? v4.z : fmax(0.0, v4.x * invZp - v4.y * invZq);
+        if (draw) {
+            const int qstar = find_crossing(Rg, 0.0, t, run, exact);
+            if (qstar / (SH::kW / kQuad) == s.q) {   // the crossing quad is this workgroup's: find its unit
+                const int j = qstar % (SH::kW / kQuad);
+                double Ru = 0.0;
+                if (lane < kQuad) {
+                    const double4 v4 = sh.usum[kQuad * j + lane];
+                    Ru = use_p ? v4.z : fmax(0.0, v4.x * invZp - v4.y * invZq);
+                }
+                bool exact_u;
+                owner = kQuad * j + find_crossing(Ru, run, t, run, exact_u);
+                exact = exact && exact_u;
             }
-            bool exact_u;
-            owner = kQuad * j + find_crossing(Ru, run, t, run, exact_u);
-            exact = exact && exact_u;
         }
         if (lane == 0) {
             sh.samp.owner = owner;
@@ -903,14 +916,35 @@ __device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s,
             sh.samp.t = t;
             sh.samp.Z1 = Zp;
             sh.samp.Z2 = Zq;
+            sh.samp.W = W;
         }
     }
     __syncthreads();
+    Zp_out = uniform(sh.samp.Z1);
+    Zq_out = uniform(sh.samp.Z2);
+    W_out = uniform(sh.samp.W);
     bool use_p, exact;
     double run, t, Zp, Zq;
-    if (!read_samp(a, s, sh, use_p, exact, run, t, Zp, Zq)) return;
-    final_scan<kVec4>(a, s, row, true, prow, qrow, c, sh.ls[s.wave], use_p, exact, run, t, 1.0 / Zp, 1.0 / Zq, Zp,
-                      1.0, c.Mp64);
+    if (!read_samp(a, s, sh, use_p, exact, run, t, Zp, Zq)) {
+        return !(static_cast<unsigned>(uniform(static_cast<int>(sh.samp.flags))) & kSampError);
+    }
+    if (draw)
+        final_scan<kVec4>(a, s, true, prow, qrow, c, sh.ls[s.wave], use_p, exact, run, t, 1.0 / Zp, 1.0 / Zq, Zp,
+                          1.0, c.Mp64, emit);
+    return true;
+}
+
+// Sampling from the residual of row `row` after its draft was rejected; `st` holds
+// the chain statistics of that row.
+template <bool kVec4, typename SH>
+__device__ __forceinline__ void sample_row(const RejectArgs& a, const SeqCtx& s, int row, const f4 (&xp)[kVecs],
+                                           const f4 (&xq)[kVecs], const RowStats& st, SH& sh) {
+    const float* prow = s.prow_base + size_t(row) * a.V;
+    const float* qrow = s.qrow_base + size_t(row) * a.V;
+    double Zp, Zq, W;
+    (void)residual_round<kVec4>(a, s, prow, qrow, row, a.samp_slots + size_t(s.b) * a.U * kSampSlots, xp, xq,
+                                residual_ctx(a, st), sh, true,
+                                [&](int y, double py) { emit_chain(a, s, row, y, py); }, Zp, Zq, W);
 }
 
 // One acceptance test: the rows it reads, the candidate, where its uniform comes
@@ -1220,36 +1254,20 @@ __device__ __forceinline__ void bonus_row(const RejectArgs& a, const SeqCtx& s, 
 // p_v. The first child is an ordinary level of the chain (same uniform, same
 // statistics); candidate i >= 2 takes word 0 of Philox stream i.
 
-// The rounds of one node after its first child was rejected, with the exact
-// normalisers of its two rows.
+// The residual of a node after its first child was rejected, in closed form. The
+// candidates of a node share the draft distribution q = q_v, so if r = max(0, p - c q) / W
+// (with W its sum), max(0, r - q) = max(0, p - (c + W) q) / W on every logit (where
+// p <= c q both sides are 0): after each rejection the residual is max(0, p - c q)
+// normalised, with c_1 = 1 and c_{j+1} = c_j + W_j, W_j = sum max(0, p - c_j q); a
+// residual that sums to zero leaves (c, W) as they were. c = 0, W = 1 is r = p.
 struct TreeRounds {
-    double iZp, iZq;
-    double iW[kMaxBranch];   // 1 / W_j, W_j the sum of round j's residual
-    unsigned keep;           // bit j: round j summed to zero and left r unchanged
-    int n;                   // rounds taken
+    double iZp, iZq;   // exact normalisers of the node's rows
+    double c, W, iW;   // r = max(0, p - c q) / W
 };
 
-// r after the rounds taken, for one logit with unnormalised weights a (p) and b (q).
+// r for one logit with unnormalised weights a (p) and b (q).
 __device__ __forceinline__ double tree_r(const TreeRounds& R, double a, double b) {
-    double r = a * R.iZp;
-    const double qb = b * R.iZq;
-#pragma unroll
-    for (int j = 0; j < kMaxBranch; ++j) {
-        if (j < R.n) {
-            const double u = fmax(0.0, r - qb);
-            r = ((R.keep >> j) & 1u) ? r : u * R.iW[j];
-        }
-    }
-    return r;
-}
-
-__device__ __forceinline__ void tree_push(TreeRounds& R, double W) {
-    const bool zero = !(W > 0.0);
-#pragma unroll
-    for (int j = 0; j < kMaxBranch; ++j)
-        if (j == R.n) R.iW[j] = zero ? 0.0 : 1.0 / W;
-    R.keep |= (zero ? 1u : 0u) << R.n;
-    ++R.n;
+    return fmax(0.0, a * R.iZp - R.c * (b * R.iZq)) * R.iW;
 }
 
 // One pass over the unit in registers (rows p_v, q_v): f(a, b) -> (w1, w2) for every
@@ -1442,21 +1460,6 @@ __device__ __forceinline__ void emit_tree(const RejectArgs& a, const SeqCtx& s, 
     a.num_accepted[s.b] = depth;
 }
 
-// SampleCtx of a node's rows from its chain statistics (as for the chain's residual).
-__device__ __forceinline__ SampleCtx residual_ctx(const RejectArgs& a, const RowStats& st) {
-    SampleCtx c;
-    c.Mp = st.Mp;
-    c.Mq = st.Mq;
-    c.invT = a.invT;
-    c.Mp64 = st.Mp;
-    c.Mq64 = st.Mq;
-    c.invT64 = a.invT64;
-    c.tp = heavy_threshold(st.Mp, st.Zp, a.T);
-    c.tq = heavy_threshold(st.Mq, st.Zq, a.T);
-    c.dn = ln_approx(st.Zp) - ln_approx(st.Zq);
-    return c;
-}
-
 // The walk of one sequence's tree (nodes 0 .. N, rows [N+1][V] of target and draft).
 template <bool kVec4>
 __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
@@ -1531,53 +1534,57 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
             ++depth;
             continue;
         }
-        // The first child was rejected. Phase 0 takes the exact normalisers; phase
-        // i = 1 .. m-1 the residual left by i rejections, then tests child i+1; phase
-        // m draws from the residual after all m rejections, phase m+1 (only if that
-        // residual sums to zero) from the residual before it. One pass per phase,
-        // at one call site, so the unit in registers is walked by a single copy of
-        // the pass.
+        // The first child was rejected. The chain's residual round gives the exact
+        // normalisers and W_1 = sum max(0, p - q) in one pass and one exchange; with a single
+        // child it also draws (as a rejected chain level does). Each later rejection costs one
+        // pass over the unit for the next residual's mass, and the draw after the last child
+        // one more (two if that residual sums to zero, which leaves r as it was).
         const SampleCtx c = residual_ctx(a, st);
+        double Zp, Zq, W1;
+        if (!residual_round<kVec4>(a, s, prow, qrow, depth, slot(ex++), xp, xq, c, sh, m == 1, emit, Zp, Zq, W1))
+            return;
+        if (m == 1) return;
         TreeRounds R;
-        R.iZp = 0.0;
-        R.iZq = 0.0;
-#pragma unroll
-        for (int j = 0; j < kMaxBranch; ++j) R.iW[j] = 0.0;
-        R.keep = 0u;
-        R.n = 0;
+        R.iZp = 1.0 / Zp;
+        R.iZq = 1.0 / Zq;
+        R.c = (W1 > 0.0) ? 1.0 : 0.0;
+        R.W = (W1 > 0.0) ? W1 : 1.0;
+        R.iW = 1.0 / R.W;
         bool moved = false;
-        for (int phase = 0;; ++phase) {
-            const bool draw = phase >= m;
-            const int fsel = phase == 0 ? 0 : (phase <= m ? 1 : 2);   // (a, b) | max(0, r - q) | r
-            auto f = [&](double av, double bv) {
-                const double r = tree_r(R, av, bv);
-                const double u = fmax(0.0, r - bv * R.iZq);
-                return make_double2(fsel == 0 ? av : (fsel == 1 ? u : r), fsel == 0 ? bv : 0.0);
-            };
+        for (int i = 2;; ++i) {   // candidate i, 1-based; i = m + 1 is the draw
+            if (i <= m) {
+                const int ci = static_cast<int>((chp >> (4 * (i - 1))) & 15u);
+                tested |= 1u << ci;
+                if (tree_candidate(a, s, c, R, prow, qrow, ci, i, depth, sh)) {
+                    v = ci;
+                    ++depth;
+                    moved = true;
+                    break;
+                }
+            }
+            const bool draw = i >= m;
+            const double cn = R.c + R.W;
+            auto f = [&](double av, double bv) { return make_double2(fmax(0.0, av * R.iZp - cn * (bv * R.iZq)), 0.0); };
             double T1, T2;
-            const int d = tree_round<kVec4>(a, s, xp, xq, c, R.iZp, prow, qrow, slot(ex++), depth, sh, draw, f,
-                                            emit, T1, T2);
-            if (d == kDrawError || (d == kDrawZero && phase > m)) {
+            int d = tree_round<kVec4>(a, s, xp, xq, c, R.iZp, prow, qrow, slot(ex++), depth, sh, draw, f, emit, T1,
+                                      T2);
+            if (d == kDrawZero) {   // the residual after the last rejection sums to zero: draw from r
+                auto g = [&](double av, double bv) {
+                    return make_double2(fmax(0.0, av * R.iZp - R.c * (bv * R.iZq)), 0.0);
+                };
+                d = tree_round<kVec4>(a, s, xp, xq, c, R.iZp, prow, qrow, slot(ex++), depth, sh, true, g, emit, T1,
+                                      T2);
+                if (d == kDrawZero) d = kDrawError;   // r has positive mass: cannot happen
+            }
+            if (d == kDrawError) {
                 flag_error(a, s);
                 return;
             }
-            if (draw) {
-                if (d == kDrawZero) continue;   // to phase m + 1
-                return;
-            }
-            if (phase == 0) {
-                R.iZp = 1.0 / T1;
-                R.iZq = 1.0 / T2;
-                continue;
-            }
-            tree_push(R, T1);
-            const int ci = static_cast<int>((chp >> (4 * phase)) & 15u);
-            tested |= 1u << ci;
-            if (tree_candidate(a, s, c, R, prow, qrow, ci, phase + 1, depth, sh)) {
-                v = ci;
-                ++depth;
-                moved = true;
-                break;
+            if (draw) return;
+            if (T1 > 0.0) {
+                R.c = cn;
+                R.W = T1;
+                R.iW = 1.0 / T1;
             }
         }
         if (moved) continue;
@@ -1866,10 +1873,6 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The level-parallel kernel: B (k + 1) groups of Q four-wavefront workgroups, all
-// resident at once (the groups wait for each other's decisions). If the device
-// would not hold them all, the chain with the same workgroups runs instead (the
-// same bits).
 // Workgroups of the level kernel the current device holds at once (-1 if the device
 // cannot be queried).
 template <bool kVec4>
@@ -1895,6 +1898,10 @@ int levels_capacity() {
     return wgs;
 }
 
+// The level-parallel kernel: B (k + 1) groups of Q four-wavefront workgroups, all
+// resident at once (the groups wait for each other's decisions). If the device
+// would not hold them all, the chain with the same workgroups runs instead (the
+// same bits).
 template <bool kVec4>
 hipError_t launch_levels(RejectArgs& a, hipStream_t stream) {
     // Every group waits for the decisions of the levels before it, so all of them
