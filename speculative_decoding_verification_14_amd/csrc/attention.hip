@@ -399,13 +399,18 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                         psum += p[i];
                     }
                     l_run[n] = l_run[n] * alpha + psum;
+                    const bool moved = __any(m_new != m_run[n]);
                     m_run[n] = m_new;
                     const bf16x8 pop = pack_bf16x8(p);
+                    // alpha is exactly 1 in every row whose maximum did not move: once the
+                    // running maxima settle, most blocks skip the rescale (a wave-uniform branch)
+                    if (moved) {
 #pragma unroll
-                    for (int j = 0; j < DJ; ++j) {
-                        o[n][j] *= alpha;
-                        o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[j]), pop, o[n][j], 0, 0, 0);
+                        for (int j = 0; j < DJ; ++j) o[n][j] *= alpha;
                     }
+#pragma unroll
+                    for (int j = 0; j < DJ; ++j)
+                        o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[j]), pop, o[n][j], 0, 0, 0);
                 }
             }
         }
