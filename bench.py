@@ -331,7 +331,7 @@ def _counter_means(path: str, counter: str) -> dict:
 
 
 def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, write_cmd: str,
-                   kind: str = "attn") -> None:
+                   kind: str = "attn", title: str = "") -> None:
     """Per-call HBM bytes of the verify attention (and, for reference, the reject
     kernel), or with kind "lm" of the LM head, from FETCH_SIZE / WRITE_SIZE runs, each
     scaled by what the same counter reads for the calibration kernel of known traffic."""
@@ -359,7 +359,8 @@ def write_counters(fetch_dir: str, write_dir: str, out: str, fetch_cmd: str, wri
     else:
         attn = sorted(k for k in set(fetch) | set(write) if k.startswith("attn_"))
         rej = sorted(k for k in set(fetch) | set(write) if k.startswith("reject_"))
-        lines = ["# rocprofv3 hardware counters, 8b workload (B=64, k=3, V=128256), one call of each kernel per step",
+        lines = [f"# rocprofv3 hardware counters, {title or '8b workload (B=64, k=3, V=128256)'}, "
+                 "one call of each kernel per step",
                  f"# fetch command: {fetch_cmd}", f"# write command: {write_cmd}", *head,
                  f"kernel_source_sha256_16: {kernel_source_hash()}",
                  f"reject_source_sha256_16: {kernel_source_hash(REJECT_KERNEL_SOURCES)}",
@@ -1120,6 +1121,7 @@ def main():
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--fetch-command", default="")
+    ap.add_argument("--counters-title", default="", help="workload named in a counter summary's first line")
     ap.add_argument("--write-command", default="")
     args = ap.parse_args()
 
@@ -1130,7 +1132,7 @@ def main():
     if args.write_counters:
         write_counters(args.fetch_dir, args.write_dir,
                        args.out or (LM_COUNTERS_FILE if args.counters_kind == "lm" else COUNTERS_FILE),
-                       args.fetch_command, args.write_command, args.counters_kind)
+                       args.fetch_command, args.write_command, args.counters_kind, args.counters_title)
         return
 
     if args.summarize_rocprof:
