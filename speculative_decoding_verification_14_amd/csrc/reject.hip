@@ -1318,31 +1318,33 @@ enum : int { kDrawn = 0, kDrawZero = 1, kDrawError = 2 };
 // One pass and one exchange: the group's totals (T1, T2) of f's two weights, in
 // every wavefront; with `draw`, also the draw from the w1 weights with u_smp at
 // position L + 1 + pos (emit(y, p_v(y)) runs on the lane holding the token), or
-// kDrawZero, without drawing, if they sum to zero.
-template <bool kVec4, typename F, typename E>
+// kDrawZero, without drawing, if they sum to zero. The exchange goes through quads
+// of units, as the chain's does, so the result is the same for any workgroup size.
+template <bool kVec4, typename SH, typename F, typename E>
 __device__ __forceinline__ int tree_round(const RejectArgs& a, const SeqCtx& s, const f4 (&xp)[kVecs],
                                           const f4 (&xq)[kVecs], const SampleCtx& c, double iZp, const float* prow,
-                                          const float* qrow, unsigned long long* slots, int pos, Shared& sh,
+                                          const float* qrow, unsigned long long* slots, int pos, SH& sh,
                                           bool draw, F&& f, E&& emit, double& T1, double& T2) {
     const int lane = lane_id();
     const double2 ws = tree_unit_pass<kVec4>(xp, xq, c, prow, qrow, a.V, s.u * kUnit + lane * 4, sh.ls[s.wave], f);
     if (lane == 0) sh.usum[s.wave] = make_double4(ws.x, ws.y, 0.0, 0.0);
     __syncthreads();
     if (s.wave == 0) {
+        const int nq = quads_of(a.U);
         double u1 = 0.0, u2 = 0.0;
-        if (lane < kUnitWaves) {
+        if (lane < SH::kW) {
             const double4 v = sh.usum[lane];
             u1 = v.x;
             u2 = v.y;
         }
-        const double w1 = dpp_wave_sum(u1), w2 = dpp_wave_sum(u2);
+        const double w1 = dpp_quad_sum(u1), w2 = dpp_quad_sum(u2);
         const unsigned pay[4] = {hi32(w1), lo32(w1), hi32(w2), lo32(w2)};
-        publish(slots + s.q, pay, s.epoch, a.Q);
+        publish_quads(slots, pay, s.epoch, s.q * (SH::kW / kQuad), SH::kW, nq);
         double u_acc, u_smp;
         verify_uniforms(a.seed, s.sid, int64_t(s.L) + 1 + pos, &u_acc, &u_smp);
         unsigned v[4];
-        const bool ok = gather<4>(slots, a.Q, s.epoch, a.spin, v);
-        const double Wg = join64(v[0], v[1]);      // lane l < Q: workgroup l's sums (zero in the others)
+        const bool ok = gather<4>(slots, nq, s.epoch, a.spin, v);
+        const double Wg = join64(v[0], v[1]);      // lane l < nq: quad l's sums (zero in the others)
         const double t1 = dpp_wave_sum(Wg), t2 = dpp_wave_sum(join64(v[2], v[3]));
         const double t = u_smp * t1;
         double run = 0.0;
@@ -1354,9 +1356,11 @@ __device__ __forceinline__ int tree_round(const RejectArgs& a, const SeqCtx& s, 
                 flags |= kSampUseP;                   // nothing to draw from
             } else {
                 const int qstar = find_crossing(Wg, 0.0, t, run, exact);
-                if (qstar == s.q) {
+                if (qstar / (SH::kW / kQuad) == s.q) {   // the crossing quad is this workgroup's: find its unit
+                    const int j = qstar % (SH::kW / kQuad);
+                    const double Ru = (lane < kQuad) ? sh.usum[kQuad * j + lane].x : 0.0;
                     bool exact_u;
-                    owner = find_crossing(u1, run, t, run, exact_u);
+                    owner = kQuad * j + find_crossing(Ru, run, t, run, exact_u);
                     exact = exact && exact_u;
                 }
             }
@@ -1407,9 +1411,10 @@ __device__ __forceinline__ int tree_round(const RejectArgs& a, const SeqCtx& s, 
 // The test of a node's i-th child (i >= 2) against the residual the rounds leave:
 // accept iff u < r(x) / q(x), u = word 0 of stream i. Every workgroup takes it from
 // the same bits; workgroup 0 writes its outputs. Returns the decision.
+template <typename SH>
 __device__ __forceinline__ bool tree_candidate(const RejectArgs& a, const SeqCtx& s, const SampleCtx& c,
                                                const TreeRounds& R, const float* prow, const float* qrow, int node,
-                                               int i, int depth, Shared& sh) {
+                                               int i, int depth, SH& sh) {
     if (s.wave == 0) {
         const int N = a.k;
         const size_t nb = size_t(s.b) * N;
@@ -1461,9 +1466,9 @@ __device__ __forceinline__ void emit_tree(const RejectArgs& a, const SeqCtx& s, 
 }
 
 // The walk of one sequence's tree (nodes 0 .. N, rows [N+1][V] of target and draft).
-template <bool kVec4>
+template <bool kVec4, typename SH>
 __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&xp)[kVecs], f4 (&xq)[kVecs],
-                                          Shared& sh, bool& counted) {
+                                          SH& sh, bool& counted) {
     const int N = a.k;
     const size_t b = s.b;
     const float* tbase = a.target + b * (N + 1) * a.V;
@@ -1592,8 +1597,8 @@ __device__ __forceinline__ void tree_walk(const RejectArgs& a, SeqCtx& s, f4 (&x
     }
 }
 
-template <bool kVec4>
-__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_tree_kernel(RejectArgs a) {
+template <bool kVec4, int W>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void reject_tree_kernel(RejectArgs a) {
     const int w = blockIdx.x;
     int group, q;
     if (a.groups % 8 == 0) {
@@ -1607,13 +1612,13 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     SeqCtx s;
     s.q = q;
     s.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    s.u = q * kUnitWaves + s.wave;
+    s.u = q * W + s.wave;
     {
         const unsigned last = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s.epoch = (last + 1u == 0u) ? 1u : last + 1u;
     }
     bool counted = q != 0;
-    __shared__ Shared sh;
+    __shared__ SharedT<W> sh;
     f4 xp[kVecs], xq[kVecs];
     for (int b = group; b < a.B; b += a.groups) {
         s.b = b;
@@ -1836,7 +1841,7 @@ hipError_t co_resident(int dev, int* wgs, int* cus_out) {
     }
     int per_cu = 0, cus = 0;
     hipError_t e = kTree
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_tree_kernel<kVec4>, kRT, 0)
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_tree_kernel<kVec4, W>, W * kWave, 0)
         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reject_kernel<kVec4, W>, W * kWave, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1868,7 +1873,7 @@ hipError_t launch_variant(RejectArgs& a, hipStream_t stream) {
     // cooperative launch would guarantee it, at ~13 us of extra launch latency
     // per call on this stack; should residency ever be partial, the waits are
     // bounded and the affected sequences report an error instead of hanging.)
-    if (kTree) hipLaunchKernelGGL((reject_tree_kernel<kVec4>), dim3(groups * a.Q), dim3(kRT), 0, stream, a);
+    if (kTree) hipLaunchKernelGGL((reject_tree_kernel<kVec4, W>), dim3(groups * a.Q), dim3(W * kWave), 0, stream, a);
     else hipLaunchKernelGGL((reject_kernel<kVec4, W>), dim3(groups * a.Q), dim3(W * kWave), 0, stream, a);
     return hipGetLastError();
 }
@@ -2087,7 +2092,12 @@ int reject_tree_max_branch() { return kMaxBranch; }
 
 hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
     const int U = (p.V + kUnit - 1) / kUnit;
-    const int Q = (U + kUnitWaves - 1) / kUnitWaves;
+    // Four-wave workgroups when each can have a CU of its own (a tree's serial walk then
+    // spreads over twice the CUs, as the chain's does at such batches), eight otherwise.
+    // The exchanges go through quads, so the outputs do not depend on it.
+    const int cus = device_cus();
+    const int W = (cus > 0 && static_cast<long long>(p.B) * groups_of(p.V, 4) <= cus) ? 4 : kUnitWaves;
+    const int Q = groups_of(p.V, W);
     if (Q > kMaxQ) return hipErrorInvalidValue;
     char* ws = static_cast<char*>(p.workspace);
     RejectArgs a;
@@ -2117,6 +2127,8 @@ hipError_t launch_reject_tree(const RejectLaunch& p, hipStream_t stream) {
     a.T = p.temperature;
     a.seed = p.seed;
     a.spin = reject_spin_limit();
+    if (W == 4)
+        return (p.V % 4) == 0 ? launch_variant<true, true, 4>(a, stream) : launch_variant<false, true, 4>(a, stream);
     return (p.V % 4) == 0 ? launch_variant<true, true, kUnitWaves>(a, stream)
                           : launch_variant<false, true, kUnitWaves>(a, stream);
 }
