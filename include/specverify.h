@@ -349,6 +349,11 @@ spec_status spec_reject_sample_ragged(const float* target_logits, const float* d
  * are a device-side precondition (a node with more than 4 children, or a parent
  * index out of range, ends that sequence with num_accepted = -1). Workspace:
  * spec_reject_sample_tree_workspace_size(B, N, V).
+ * Runs as spec_reject_sample's chain does: the walk of a sequence reads only the
+ * rows of the nodes it visits, its workgroups (of 512 threads, or of 256 when each
+ * can have a CU of its own) exchange partial sums while running, with the same
+ * residency requirement, bounded waits and error word; the outputs do not depend on
+ * the workgroup size.
  * ---------------------------------------------------------------------- */
 spec_status spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* parents,
