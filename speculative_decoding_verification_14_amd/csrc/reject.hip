@@ -62,7 +62,7 @@ constexpr int kUnit = kWave * kVecs * 4;   // 4096 logits: one wavefront's share
 constexpr int kStep = 4;                   // loads per online-softmax step (16 logits per lane)
 constexpr int kStatSlots = 6;              // M_p, M_q, Z_p (hi, lo), Z_q (hi, lo)
 constexpr int kSampSlots = 8;              // A, B, P, Q (hi, lo each); bonus row: weight sum, max
-constexpr int kUnitWaves = 8;              // unit wavefronts per workgroup (the tree walk; the chain: 8 or 4)
+constexpr int kUnitWaves = 8;              // unit wavefronts per workgroup at most (4 where the batch is small)
 constexpr int kRT = kUnitWaves * kWave;    // 512 threads
 constexpr int kMaxQ = 64;                  // workgroups per sequence: U <= 256 (V <= 2^20), four units each
 constexpr int kMaxBranch = 4;              // tree: children per node

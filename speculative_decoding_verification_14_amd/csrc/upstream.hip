@@ -139,7 +139,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeArgs a) {
 //
 // The hidden rows reach LDS by buffer-to-LDS loads (no register staging) into two
 // slots. A chunk row is 128 bytes; its eight 16-byte pieces are stored XOR-swizzled by
-// (row / 2) % 8, so the 16 rows of a fragment read land in 16 distinct bank groups.
+// sw(row) = (row % 8) ^ ((row / 8) % 2). A 16-byte LDS read is served eight lanes at a
+// time, and the eight rows 8i .. 8i + 7 of a fragment read then fetch eight different
+// pieces, i.e. eight distinct 16-byte bank groups of the 128-byte bank row; the 16 rows
+// of the fragment also fall in 16 distinct (row parity, piece) pairs, so a 256-byte
+// bank row would serve them without conflict too. (Swizzling by (row / 2) % 8 gave
+// pairs of rows the same piece: half of the LDS busy cycles were bank conflicts.)
 // The slots are two separate LDS arrays, each named by a compile-time index: the
 // compiler can then tell a read of one slot from a load into the other, and waits only
 // for the latter's own loads instead of draining every load in flight before each read
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lm_head_kernel(GemmArgs a) {
 
     // hidden rows m0 .. m0 + MB - 1 through a buffer resource: rows >= R read as zero (their
     // outputs are never stored). Load i of this wave fills LDS slots (wave kDma + i) 64 + lane:
-    // row r = slot / 8, physical piece slot % 8, holding logical piece (slot % 8) ^ ((r / 2) % 8).
+    // row r = slot / 8, physical piece slot % 8, holding logical piece (slot % 8) ^ sw(r).
     const int rows_here = min(MB, a.R - m0);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.A + size_t(m0) * a.H), static_cast<short>(0), rows_here * a.H * 2, 0x00020000);
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lm_head_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
         const int r = (wave * kDma + i) * 8 + (lane >> 3);
-        voff[i] = r * a.H * 2 + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+        voff[i] = r * a.H * 2 + (((lane & 7) ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
     }
     auto dma = [&](int chunk, unsigned char* buf) {
         const int kc = rot(min(chunk, chunks - 1));   // past the last chunk: a copy nobody reads
@@ -266,8 +271,9 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lm_head_kernel(GemmArgs a) {
     load_w(wr[0], 0);
     load_w(wr[1], min(1, chunks - 1));
 
-    // fragment reads: row 16 mt + l16, logical pieces 2 lg and 2 lg + 1
-    const int sw = (l16 >> 1) & 7;
+    // fragment reads: row 16 mt + l16, logical pieces 2 lg and 2 lg + 1 (sw depends on the row
+    // modulo 16 only, so it is the same for every row tile)
+    const int sw = (l16 & 7) ^ (l16 >> 3);
     const int rd0 = l16 * 128 + (((2 * lg) ^ sw) << 4);
     const int rd1 = l16 * 128 + (((2 * lg + 1) ^ sw) << 4);
 
