@@ -502,20 +502,15 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
 
 // One row (dims d0 .. d0 + D/16) of a split segment: M = max over the pieces w0 .. w1,
 // then their sums and outputs weighted by 2^(m - M), folded in workgroup order.
-// The loads of KB pieces are issued together (addresses clamped to the last piece,
-// weights past it 0, so the sums are the same bits as piece by piece). Returns 1 / sum.
+// The loads of KB pieces (max, sum and output row) are issued together, in one round
+// trip: addresses clamped to the last piece, weights past it 0. The running maximum
+// moves only between batches, so with at most KB pieces the weights are 2^(m_j - M) for
+// the pieces' own maximum M, the same bits as a separate pass for M would give; with
+// more, the sums so far are rescaled when a batch raises it. Returns 1 / sum.
 template <int D, int KB, typename PR>
 __device__ __forceinline__ float merge_row(const AttnArgs& a, PR&& prow_of, int w0, int w1, int n, int r, int d0,
                                            float (&acc)[D / 16]) {
-    float M = -INFINITY;
-    for (int wb = w0; wb <= w1; wb += KB) {
-        float mv[KB];
-#pragma unroll
-        for (int j = 0; j < KB; ++j) mv[j] = a.part_ml[prow_of(min(wb + j, w1), n, r) * 2];
-#pragma unroll
-        for (int j = 0; j < KB; ++j) M = fmaxf(M, (wb + j <= w1) ? mv[j] : -INFINITY);
-    }
-    float lsum = 0.0f;
+    float M = -INFINITY, lsum = 0.0f;
 #pragma unroll
     for (int dd = 0; dd < D / 16; ++dd) acc[dd] = 0.0f;
     for (int wb = w0; wb <= w1; wb += KB) {
@@ -528,6 +523,16 @@ __device__ __forceinline__ float merge_row(const AttnArgs& a, PR&& prow_of, int 
 #pragma unroll
             for (int dd = 0; dd < D / 16; ++dd) po[j][dd] = a.part_o[prow * D + d0 + dd];
         }
+        float bm = M;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) bm = fmaxf(bm, (wb + j <= w1) ? ms[j] : -INFINITY);
+        // scale of the sums so far: 0 before the first finite maximum (they are 0), else
+        // 2^(M - bm), exactly 1 when the batch does not raise M
+        const float sc = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - bm);
+        lsum *= sc;
+#pragma unroll
+        for (int dd = 0; dd < D / 16; ++dd) acc[dd] *= sc;
+        M = bm;
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
             // branch-free, so that all of the batch's loads stay in flight together
