@@ -61,6 +61,13 @@ EVENT_STEPS = 30    # at least this many steps with per-call events for the aver
 METRIC = "verified tokens/s + HBM GB/s (% of peak) for spec verify, 8B shape, k=3"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "verify_attn_8b_counters.txt")
 LM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "lm_head_8b_counters.txt")
+# counter runs of the uniform step per workload, each taken at that workload's own batch and k
+WORKLOAD_COUNTERS = {
+    "8b": COUNTERS_FILE,
+    "7b": os.path.join(ROOT, "profiles", "verify_7b_b256_counters.txt"),
+    "longtail": os.path.join(ROOT, "profiles", "verify_longtail_counters.txt"),
+    "262k": os.path.join(ROOT, "profiles", "verify_262k_counters.txt"),
+}
 KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/attention.hip",
                   "speculative_decoding_verification_14_amd/csrc/common.hpp"]
 LM_KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/upstream.hip",
@@ -127,6 +134,12 @@ def dense_reject_figure(preset, seconds: float) -> dict:
     dense = preset.B * (2 * preset.k + 1) * preset.V * 4
     gbs = dense / seconds / 1e9
     return dict(bytes=dense, gbs=gbs, frac_of_peak=gbs / HBM_PEAK_GBS)
+
+
+def workload_counters(workload: str, variant: str = "uniform"):
+    """The counter summary that measured this bench line's launches, or None: only the uniform
+    step of a workload at its own shape has one (plain decoding, k = 0, launches other kernels)."""
+    return WORKLOAD_COUNTERS.get(workload) if variant == "uniform" else None
 
 
 def stored_traffic(path=None, sources=None, key="hbm_bytes_per_call"):
@@ -949,7 +962,8 @@ def gpu_bench(args) -> dict:
     step_s = wall / args.steps
     attn_gbs = a_bytes / attn_avg_s / 1e9
     rej_gbs = r_bytes / rej_avg_s / 1e9
-    traffic = stored_traffic()
+    cfile = workload_counters(args.workload, args.variant)
+    traffic = stored_traffic(cfile) if cfile else None
     result = dict(
         metric=METRIC, value=tokens / step_s, unit="verified tokens/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=step_s * 1e3, higher_is_better=True, scaling="weak",
@@ -963,7 +977,8 @@ def gpu_bench(args) -> dict:
                       kernel="spec_verify_attn (attn_streamk_kernel + attn_merge_kernel)",
                       algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_avg_s * 1e6, calls_timed=len(evs)),
         roofline_reject=dict(bound="hbm", achieved=rej_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=rej_gbs / HBM_PEAK_GBS, traffic=stored_traffic(key="reject_hbm_bytes_per_call"),
+                             frac=rej_gbs / HBM_PEAK_GBS,
+                             traffic=stored_traffic(cfile, key="reject_hbm_bytes_per_call") if cfile else None,
                              kernel="spec_reject_sample", algorithmic_bytes_per_call=r_bytes,
                              avg_call_us=rej_avg_s * 1e6, calls_timed=len(evs)),
         verified_tokens_per_step=tokens,

@@ -57,3 +57,20 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "exactly one GPU" in res.stderr
+
+
+def test_each_workload_line_takes_traffic_from_its_own_counter_run():
+    # the counter summary a bench line cites must come from a run of that same line: its
+    # recorded fetch command names the workload (none for the default, 8b) and no variant
+    for workload in ("8b", "7b", "longtail", "262k"):
+        path = bench.workload_counters(workload)
+        with open(path) as f:
+            cmd = next(line for line in f if line.startswith("# fetch command:"))
+        args = cmd.split(" -- ", 1)[1].split()
+        named = args[args.index("--workload") + 1] if "--workload" in args else "8b"
+        assert named == workload, (workload, cmd)
+        assert "--variant" not in args and "--sweep" not in args, cmd
+    # other launches (plain decoding, ragged, trees, the fused pass) and other workloads have none
+    for variant in ("plain", "ragged", "tree", "fused"):
+        assert bench.workload_counters("8b", variant) is None
+    assert bench.workload_counters("tiny") is None
