@@ -24,6 +24,11 @@ MARGIN = 1e-6
 MISMATCH_BUDGET = 1e-4
 
 
+def seed_count(n: int) -> int:
+    """Seeds of a large-shape parity case: n, times SPECVERIFY_PARITY_SCALE for a longer run."""
+    return n * max(1, int(os.environ.get("SPECVERIFY_PARITY_SCALE", "1")))
+
+
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

@@ -16,7 +16,7 @@ import pytest
 from oracle import attention as oatt
 from oracle import commit as ocommit
 from oracle import reject as orej
-from tests.parity import ATTN_TOL, MARGIN, MISMATCH_BUDGET, PROB_TOL, Tally, bf16_dev, dev, run_attention, say
+from tests.parity import ATTN_TOL, MARGIN, MISMATCH_BUDGET, PROB_TOL, Tally, bf16_dev, dev, run_attention, say, seed_count
 from workloads import PRESETS, make_ragged_attention_inputs, make_ragged_reject_inputs, make_reject_inputs
 from workloads import pack_reject_inputs
 
@@ -183,7 +183,7 @@ def _check_ragged(inp, device, seeds, label):
 
 def test_reject_ragged_8b(device):
     inp = make_ragged_reject_inputs(PRESETS["8b"], 7)
-    _check_ragged(inp, device, [inp["seed"] + 13 * i for i in range(120)], "8b k_max 7")
+    _check_ragged(inp, device, [inp["seed"] + 13 * i for i in range(seed_count(120))], "8b k_max 7")
 
 
 def test_reject_ragged_tiny_k15(device):

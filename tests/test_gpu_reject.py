@@ -9,14 +9,13 @@ batch invariance.
 """
 
 import dataclasses
-import os
 
 import numpy as np
 import pytest
 
 from oracle import commit as ocommit
 from oracle import reject as orej
-from tests.parity import RejectDevice, Tally, compare_reject, say
+from tests.parity import RejectDevice, Tally, compare_reject, say, seed_count
 from workloads import PRESETS, draft_from_logits, make_reject_inputs
 
 pytestmark = pytest.mark.gpu
@@ -53,18 +52,16 @@ def test_tiny(device):
 
 
 def test_8b_full_batch_many_seeds(device):
-    """8B-shaped rows (B=64, V=128256, k=3) over enough seeds for >= 1e5 decisions
-    (SPECVERIFY_PARITY_SEEDS raises the seed count for a longer run; default 540)."""
+    """8B-shaped rows (B=64, V=128256, k=3) over enough seeds for >= 1e5 decisions."""
     inp = make_reject_inputs(PRESETS["8b"])
-    n = max(540, int(os.environ.get("SPECVERIFY_PARITY_SEEDS", "540")))
-    t = _check(inp, device, [inp["seed"] + 7919 * i for i in range(n)], label="8b")
+    t = _check(inp, device, [inp["seed"] + 7919 * i for i in range(seed_count(540))], label="8b")
     assert t.decisions >= 100_000
 
 
 @pytest.mark.parametrize("name,B", [("7b", 256), ("7b", 16), ("longtail", 8), ("262k", 2)])
 def test_other_workloads(device, name, B):
     inp = make_reject_inputs(PRESETS[name], B=B)
-    n_seeds = max(4, 4096 // B)
+    n_seeds = seed_count(max(4, 4096 // B))
     _check(inp, device, [inp["seed"] + 31 * i for i in range(n_seeds)], label=f"{name}/B{B}")
 
 

@@ -16,7 +16,7 @@ import pytest
 
 from oracle import commit as ocommit
 from oracle import tree as otree
-from tests.parity import ATTN_TOL, MARGIN, MISMATCH_BUDGET, PROB_TOL, Tally, bf16_dev, dev, run_attention, say
+from tests.parity import ATTN_TOL, MARGIN, MISMATCH_BUDGET, PROB_TOL, Tally, bf16_dev, dev, run_attention, say, seed_count
 from workloads import (PRESETS, make_tree_attention_inputs, make_tree_reject_inputs, random_parents, random_paths,
                        tree_parents)
 
@@ -155,11 +155,13 @@ def _compare_tree(g, o, tally):
 def _check_tree(inp, device, seeds, label):
     td = TreeDevice(inp, device)
     tally = Tally()
-    for s in seeds:
+    for i, s in enumerate(seeds):
         g = td.call(s)
         o = otree.verify_batch_tree(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["parents"],
                                     inp["seq_ids"], inp["seq_lens"], inp["temperature"], s)
         _compare_tree(g, o, tally)
+        if (i + 1) % 25 == 0:
+            say(f"[tree reject] {label}: {i + 1} of {len(seeds)} seeds")
     say(f"[tree reject] {label}: {tally.summary()}")
     tally.record(f"tree walk {label}")
     assert not tally.bad, tally.bad[:10]
@@ -183,7 +185,7 @@ def test_tree_reject_random_trees_per_sequence(device):
 @pytest.mark.parametrize("t,d", [(2, 2), (2, 3), (4, 1)])
 def test_tree_reject_8b(device, t, d):
     inp = make_tree_reject_inputs(PRESETS["8b"], tree_parents(t, d), B=64)
-    _check_tree(inp, device, [inp["seed"] + 11 * i for i in range(20)], f"8b t{t} d{d}")
+    _check_tree(inp, device, [inp["seed"] + 11 * i for i in range(seed_count(20))], f"8b t{t} d{d}")
 
 
 @pytest.mark.parametrize("t,d", [(2, 2), (4, 1)])
