@@ -144,7 +144,7 @@ def test_lm_head_shapes(device, R, H, V):
     assert np.all(np.isfinite(got)) and np.all(err <= bound) and np.all(err <= stat)
 
 
-def test_lm_head_8b_shape_sampled_columns(device):
+def test_lm_head_8b_shape(device):
     R, H, V = 256, 4096, 128256
     x = make_lm_head_inputs(R, H, V, seed=8)
     got = _lm_gpu(x, device)
@@ -159,6 +159,14 @@ def test_lm_head_8b_shape_sampled_columns(device):
     say(f"[lm head] 8b: {cols.size} columns, max err {err.max():.2e}, max err / bound {(err / bound).max():.3f}, "
         f"rows {rows.size}: max err / statistical bound {(err[rows] / stat).max():.3f}")
     assert np.all(err <= bound) and np.all(err[rows] <= stat)
+    # every column, on every eighth row, against the worst-case bound
+    r8 = np.arange(0, R, 8)
+    want8 = oup.lm_head(x["hidden"][r8], x["weight"])
+    bound8 = oup.lm_head_error_bound(x["hidden"][r8], x["weight"])
+    err8 = np.abs(got[r8] - want8)
+    say(f"[lm head] 8b: all {V} columns on {r8.size} rows, max err {err8.max():.2e}, "
+        f"max err / bound {(err8 / bound8).max():.3f}")
+    assert np.all(err8 <= bound8)
 
 
 def test_fused_pass_on_the_device(device):
