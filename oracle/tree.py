@@ -158,11 +158,14 @@ def walk(p_of, q_of, tokens, parents, L: int, uni) -> TreeResult:
 
 
 def verify_batch_tree(target_logits, draft_logits, draft_tokens, parents, seq_ids, seq_lens,
-                      temperature: float, seed: int):
+                      temperature: float, seed: int, rows_cache=None):
     """Batch driver; target_logits [B][N+1][V] (row n = node n), draft_logits [B][N+1][V] (row v =
     q at node v; rows of leaves unused), draft_tokens [B][N], parents [B][N]. Outputs padded like
     the C-ABI: out_tokens [B][N+1] (-1 after), accepted_nodes [B][N] (-1 after), out_probs
-    [B][N+1] (0 after), accept_probs [B][N] (-1 for untested nodes)."""
+    [B][N+1] (0 after), accept_probs [B][N] (-1 for untested nodes).
+
+    rows_cache: optional list of B empty dicts, kept by the caller across calls on the same logits
+    and temperature (many seeds): the softmax rows of each sequence are then computed once."""
     B, N1, _ = target_logits.shape
     N = N1 - 1
     out_tokens = np.full((B, N1), -1, dtype=np.int32)
@@ -172,7 +175,11 @@ def verify_batch_tree(target_logits, draft_logits, draft_tokens, parents, seq_id
     num_accepted = np.zeros(B, dtype=np.int32)
     results = []
     for b in range(B):
-        cache_p, cache_q = {}, {}
+        if rows_cache is None:
+            cache_p, cache_q = {}, {}
+        else:
+            cache_p = rows_cache[b].setdefault("p", {})
+            cache_q = rows_cache[b].setdefault("q", {})
 
         def p_of(v, b=b, cache=cache_p):
             if v not in cache:

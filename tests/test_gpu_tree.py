@@ -149,10 +149,11 @@ def _compare_tree(g, o, tally):
 def _check_tree(inp, device, seeds, label):
     td = TreeDevice(inp, device)
     tally = Tally()
+    rows = [{} for _ in range(inp["B"])]   # each sequence's softmax rows, computed once for all seeds
     for i, s in enumerate(seeds):
         g = td.call(s)
         o = otree.verify_batch_tree(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["parents"],
-                                    inp["seq_ids"], inp["seq_lens"], inp["temperature"], s)
+                                    inp["seq_ids"], inp["seq_lens"], inp["temperature"], s, rows_cache=rows)
         _compare_tree(g, o, tally)
         if (i + 1) % 25 == 0:
             say(f"[tree reject] {label}: {i + 1} of {len(seeds)} seeds")

@@ -270,3 +270,19 @@ def test_tree_commit_touches_only_the_new_prefix_and_refuses_overflow():
             dp, do = int(a["block_table"][b, (L[b] + j) // bs]), int((L[b] + j) % bs)
             np.testing.assert_array_equal(kc[dp, :, do, :], a["k_cache"][sp, :, so, :])
             np.testing.assert_array_equal(vc[dp, :, :, do], a["v_cache"][sp, :, :, so])
+
+
+def test_rows_cache_changes_nothing():
+    # the optional per-sequence row cache only memoises the softmax rows: every output over many
+    # seeds equals the uncached call's
+    from workloads import make_tree_reject_inputs
+    inp = make_tree_reject_inputs(PRESETS["tiny"], np.array([0, 0, 1, 1, 2], dtype=np.int32), seed=5, B=5)
+    args = (inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["parents"], inp["seq_ids"],
+            inp["seq_lens"], 1.0)
+    rows = [{} for _ in range(inp["target_logits"].shape[0])]
+    for seed in range(30):
+        plain = otree.verify_batch_tree(*args, seed)
+        cached = otree.verify_batch_tree(*args, seed, rows_cache=rows)
+        for key in ("out_tokens", "num_accepted", "accepted_nodes", "out_probs", "accept_probs"):
+            np.testing.assert_array_equal(plain[key], cached[key], err_msg=key)
+    assert all(r["p"] for r in rows)
