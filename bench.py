@@ -437,6 +437,61 @@ def write_mfma(pmc_dir: str, out: str, command: str) -> None:
     print("\n".join(lines))
 
 
+XCDS = 8   # GRBM counters are summed over the chip's accelerator dies
+
+
+def clock_table(pmc_csv_rows) -> dict:
+    """Average shader clock per kernel label from rows of a counter_collection.csv holding
+    GRBM_COUNT: the counter ticks once per engine clock in each of the 8 dies while the
+    dispatch runs, so GRBM_COUNT / 8 / (end - start) is the dispatch's mean clock.
+    Returns {label: (dispatches, median duration in us, median clock in GHz)}."""
+    per = {}
+    for row in pmc_csv_rows:
+        if row["Counter_Name"] != "GRBM_COUNT":
+            continue
+        ns = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+        if ns <= 0:
+            continue
+        per.setdefault(_kernel_label(row["Kernel_Name"]), []).append(
+            (ns * 1e-3, float(row["Counter_Value"]) / XCDS / ns))
+    med = lambda v: sorted(v)[len(v) // 2]
+    return {k: (len(v), med([x[0] for x in v]), med([x[1] for x in v])) for k, v in per.items()}
+
+
+def write_clock(pmc_dir: str, out: str, command: str, title: str) -> None:
+    """Shader clock per kernel from one rocprofv3 run with GRBM_GUI_ACTIVE and GRBM_COUNT."""
+    files = sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {pmc_dir}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows.extend(csv.DictReader(f))
+    max_mhz = ""
+    for fn in glob.glob(os.path.join(pmc_dir, "**", "*agent_info.csv"), recursive=True):
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Agent_Type") == "GPU":
+                    max_mhz = row.get("Max_Engine_Clk_Fcompute", "")
+    lines = [f"# rocprofv3 GRBM counters, {title}: mean shader clock per kernel",
+             f"# command: {command}",
+             f"# clock = GRBM_COUNT / {XCDS} dies / (End_Timestamp - Start_Timestamp) of the dispatch; "
+             "medians over the dispatches",
+             f"# maximum engine clock reported by the agent: {max_mhz} MHz",
+             "# the counters' window outlasts a dispatch by a few microseconds (a 7 us kernel reads ~4.7 GHz),",
+             "# so only dispatches over 100 us are listed; for those the clock reads at most ~2-3% high",
+             f"kernel_source_sha256_16: {kernel_source_hash()}",
+             f"lm_head_source_sha256_16: {kernel_source_hash(LM_KERNEL_SOURCES)}",
+             f"{'kernel':70s} {'dispatches':>10s} {'median_us':>10s} {'clock_GHz':>10s}"]
+    for k, (n, us, ghz) in sorted(clock_table(rows).items(), key=lambda kv: -kv[1][1]):
+        if us < 100.0:
+            continue   # the counters' window outlasts a dispatch by a few microseconds: short ones read high
+        lines.append(f"{k:70s} {n:10d} {us:10.1f} {ghz:10.3f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ----------------------------------------------------------------------------- GPU benchmark
 
 def copy_calibration(dev) -> dict:
@@ -1132,6 +1187,8 @@ def main():
     ap.add_argument("--write-counters", action="store_true")
     ap.add_argument("--write-mfma", metavar="PMC_DIR",
                     help="write the attention's MFMA counter summary from a rocprofv3 run in PMC_DIR")
+    ap.add_argument("--write-clock", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 run with GRBM_GUI_ACTIVE and GRBM_COUNT: shader clock per kernel")
     ap.add_argument("--counters-kind", choices=["attn", "lm"], default="attn")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
@@ -1142,6 +1199,10 @@ def main():
 
     if args.write_mfma:
         write_mfma(args.write_mfma, args.out or MFMA_FILE, args.command)
+        return
+
+    if args.write_clock:
+        write_clock(args.write_clock, args.out or "/dev/stdout", args.command, args.counters_title or args.workload)
         return
 
     if args.write_counters:

@@ -74,3 +74,18 @@ def test_each_workload_line_takes_traffic_from_its_own_counter_run():
     for variant in ("plain", "ragged", "tree", "fused"):
         assert bench.workload_counters("8b", variant) is None
     assert bench.workload_counters("tiny") is None
+
+
+def test_clock_table_divides_the_die_summed_count_by_the_duration():
+    # two dispatches of one kernel at 2.0 and 2.2 GHz (GRBM_COUNT summed over the 8 dies) and a
+    # row of another counter, which is ignored; the median of two values is the upper one
+    def row(name, counter, value, t0, t1):
+        return {"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": str(value),
+                "Start_Timestamp": str(t0), "End_Timestamp": str(t1)}
+    rows = [row("void k<1>(int)", "GRBM_COUNT", 8 * 2.0 * 1000, 0, 1000),
+            row("void k<1>(int)", "GRBM_GUI_ACTIVE", 1.0, 0, 1000),
+            row("void k<1>(int)", "GRBM_COUNT", 8 * 2.2 * 500, 5000, 5500)]
+    t = bench.clock_table(rows)
+    (label,) = t
+    n, us, ghz = t[label]
+    assert n == 2 and abs(us - 1.0) < 1e-9 and abs(ghz - 2.2) < 1e-9
