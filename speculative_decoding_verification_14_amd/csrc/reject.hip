@@ -384,11 +384,20 @@ struct SampleCtx {
     double Mp64, Mq64, invT64;
 };
 
-// Log-weight of a logit in nats, (z - M) / T, and the residual-support test. The
-// operations are written with the no-contraction intrinsics so that every call
-// site rounds identically (the support must be the same set wherever it is judged).
-__device__ __forceinline__ float log_weight(float z, float M, float invT) { return __fmul_rn(__fsub_rn(z, M), invT); }
-__device__ __forceinline__ bool in_support(float xp, float xq, float dn) { return __fsub_rn(xp, xq) > dn; }
+// Log-weight of a logit in nats, (z - M) / T, and the residual-support test. Each
+// operation rounds on its own: contraction is switched off here, because HIP's
+// __fmul_rn / __fsub_rn are plain operators that the compiler may fuse, and it
+// fused the support test's subtraction with one of the two products at one call
+// site but not necessarily at another. The support must be the same set wherever
+// it is judged (the unit sums, the heavy re-reads, the final scan).
+__device__ __forceinline__ float log_weight(float z, float M, float invT) {
+#pragma clang fp contract(off)
+    return (z - M) * invT;
+}
+__device__ __forceinline__ bool in_support(float xp, float xq, float dn) {
+#pragma clang fp contract(off)
+    return xp - xq > dn;
+}
 __device__ __forceinline__ bool is_heavy(bool residual, float zp, float zq, const SampleCtx& c) {
     return static_cast<int>(heavy_sign(residual, zp, zq, c.tp, c.tq)) < 0;
 }
