@@ -68,12 +68,15 @@ WORKLOAD_COUNTERS = {
     "longtail": os.path.join(ROOT, "profiles", "verify_longtail_counters.txt"),
     "262k": os.path.join(ROOT, "profiles", "verify_262k_counters.txt"),
 }
+# sources (and the build script, which holds per-file compiler flags) whose hash a counter
+# summary records: counters taken before a change to any of them are not used
+BUILD_SCRIPT = "speculative_decoding_verification_14_amd/build.py"
 KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/attention.hip",
-                  "speculative_decoding_verification_14_amd/csrc/common.hpp"]
+                  "speculative_decoding_verification_14_amd/csrc/common.hpp", BUILD_SCRIPT]
 LM_KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/upstream.hip",
-                     "speculative_decoding_verification_14_amd/csrc/common.hpp"]
+                     "speculative_decoding_verification_14_amd/csrc/common.hpp", BUILD_SCRIPT]
 REJECT_KERNEL_SOURCES = [f"speculative_decoding_verification_14_amd/csrc/{f}"
-                         for f in ("reject.hip", "common.hpp", "heavy.hpp", "fastexp.hpp", "philox.hpp")]
+                         for f in ("reject.hip", "common.hpp", "heavy.hpp", "fastexp.hpp", "philox.hpp")] + [BUILD_SCRIPT]
 
 
 def kernel_source_hash(sources=None) -> str:
