@@ -96,6 +96,23 @@ __device__ __forceinline__ SeqShape seq_shape(const int32_t* cu, int b, int k, i
     return s;
 }
 
+// The values of this lane and of lane l ^ 16 (pair16) or l ^ 32 (pair32), in either
+// order, through v_permlane16_swap / v_permlane32_swap: VALU instructions, where a
+// __shfl_xor compiles to an LDS permute and a wait for it. Given the same register
+// twice, the 16-lane swap exchanges odd rows of 16 lanes with even ones and the 32-lane
+// swap the upper half with the lower, so each lane ends up holding its own value and
+// its partner's. Sums and maxima of the pair are then the shuffle's, bit for bit.
+__device__ __forceinline__ void pair16(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     const __bf16 h = static_cast<__bf16>(x);
     return __builtin_bit_cast(uint16_t, h);
@@ -388,8 +405,13 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
                     float bmax = sv[0];
 #pragma unroll
                     for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sv[i]);
-                    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
-                    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
+                    {
+                        float x0, x1;
+                        pair16(bmax, x0, x1);
+                        bmax = fmaxf(x0, x1);
+                        pair32(bmax, x0, x1);
+                        bmax = fmaxf(x0, x1);
+                    }
                     const float m_new = fmaxf(m_run[n], bmax);
                     const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
                     const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_ref);
@@ -420,8 +442,11 @@ __global__ __launch_bounds__(kAT) void attn_streamk_kernel(AttnArgs a) {
         // ---- combine the four waves: per row, M = max over waves, weights 2^(m_w - M).
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            float lt = l_run[n] + __shfl_xor(l_run[n], 16, kWave);
-            lt += __shfl_xor(lt, 32, kWave);
+            float x0, x1;
+            pair16(l_run[n], x0, x1);
+            float lt = x0 + x1;
+            pair32(lt, x0, x1);
+            lt = x0 + x1;
             if (lg == 0) {
                 s_m[wave][n][l16] = m_run[n];
                 s_l[wave][n][l16] = lt;
