@@ -159,11 +159,13 @@ def _check_ragged(inp, device, seeds, label):
     rows = [orej.SequenceRows(inp["target_logits"][cu[b] + b: cu[b + 1] + b + 1],
                               inp["draft_logits"][cu[b]: cu[b + 1]], inp["temperature"]) for b in range(inp["B"])]
     tally = Tally()
-    for s in seeds:
+    for n, s in enumerate(seeds, 1):
         g = rd.call(s)
         o = orej.verify_batch_ragged(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], cu,
                                      inp["seq_ids"], inp["seq_lens"], inp["temperature"], s, rows_cache=rows)
         _compare_ragged(g, o, cu, tally)
+        if n % 500 == 0:
+            say(f"[ragged reject] {label}: {n} of {len(seeds)} seeds")
     say(f"[ragged reject] {label} lens {np.diff(cu).tolist()[:16]}: {tally.summary()}")
     tally.record(f"ragged reject {label}")
     assert not tally.bad, tally.bad[:10]

@@ -37,9 +37,11 @@ def _check(inp, device, seeds, temperature=None, label=""):
     rd = RejectDevice(inp, device)
     rows = _rows(inp, temperature)
     tally = Tally()
-    for s in seeds:
+    for n, s in enumerate(seeds, 1):
         gpu = rd.call(s, temperature)
         compare_reject(gpu, _oracle(inp, s, rows, temperature), tally, inp["k"])
+        if n % 1000 == 0:
+            say(f"[reject] {label}: {n} of {len(seeds)} seeds")
     say(f"[reject] {label}: {tally.summary()}")
     tally.record(f"reject {label} B={inp['B']} k={inp['k']} V={inp['V']}")
     assert tally.ok(), (tally.summary(), tally.bad[:10])
