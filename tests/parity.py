@@ -3,7 +3,7 @@ binding, and the decision-by-decision comparison with the oracle.
 
 Parity bar:
 * attention: |GPU - oracle| <= 1e-2 absolute (bf16 inputs, fp32 accumulation)
-* probabilities (out_probs, accept_probs): <= 1e-5 absolute
+* probabilities (out_probs, accept_probs): <= 1e-6 absolute (the decision margin: accept_probs is what the uniform is compared with)
 * accepted lengths and tokens: bit-exact, except at decisions whose oracle margin
   is below 1e-6; such mismatches are counted and must stay under 1e-4 of all
   decisions. Comparison of a sequence stops at its first mismatch.
@@ -19,7 +19,11 @@ import time
 import numpy as np
 
 ATTN_TOL = 1e-2
-PROB_TOL = 1e-5
+# out_probs and accept_probs: accept_probs = min(1, p/q) is the very number the acceptance
+# uniform is compared with, and a decision may differ from the oracle's only where the
+# uniform lies within MARGIN of it; an error in it above MARGIN would let larger-margin
+# disagreements through, so both probability outputs are held to MARGIN as well
+PROB_TOL = 1e-6
 MARGIN = 1e-6
 MISMATCH_BUDGET = 1e-4
 

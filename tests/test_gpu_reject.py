@@ -2,7 +2,7 @@
 
 Tokens and accepted lengths must match decision by decision, except where the
 oracle's margin is below 1e-6 (counted, under 1e-4 of decisions); probabilities
-within 1e-5. Every workload size, plus edge cases: q = p, one-hot rows, zero
+within 1e-6. Every workload size, plus edge cases: q = p, one-hot rows, zero
 draft probability, vocab sizes that are not multiples of 4 or of the slice,
 temperature != 1, k = 0 (plain decoding), k = 1 and k = 15, determinism and
 batch invariance.
