@@ -76,7 +76,7 @@ KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/attention.hip",
 LM_KERNEL_SOURCES = ["speculative_decoding_verification_14_amd/csrc/upstream.hip",
                      "speculative_decoding_verification_14_amd/csrc/common.hpp", BUILD_SCRIPT]
 REJECT_KERNEL_SOURCES = [f"speculative_decoding_verification_14_amd/csrc/{f}"
-                         for f in ("reject.hip", "common.hpp", "heavy.hpp", "fastexp.hpp", "philox.hpp")] + [BUILD_SCRIPT]
+                         for f in ("reject.hip", "common.hpp", "heavy.hpp", "softmax_step.hpp", "fastexp.hpp", "philox.hpp")] + [BUILD_SCRIPT]
 
 
 def kernel_source_hash(sources=None) -> str:

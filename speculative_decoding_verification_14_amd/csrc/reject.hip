@@ -51,6 +51,7 @@
 #include "common.hpp"
 #include "fastexp.hpp"
 #include "heavy.hpp"
+#include "softmax_step.hpp"
 #include "kernels.hpp"
 #include "philox.hpp"
 
@@ -334,18 +335,12 @@ __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t rp, __amdgpu_bu
 // running sum s of 2^{(x - m) c2}, c2 = log2(e)/T, the terms as hardware exp2 of
 // one fma each. The statistics feed the acceptance ratio u < p/q, whose decisions
 // the fp64 oracle reproduces except within a small margin of u, so the sum must
-// carry no error common to all its terms:
-//  * the step's offset -ref c2 is rounded to fp32 (nr), which scales every term of
-//    the step by the same 2^-eps, -ref c2 = nr + eps exactly (eps from one fma).
-//    With a maximum near 20 that is up to ~7e-7 of the sum. The step's sum is
-//    multiplied back by 2^eps = 1 + eps ln 2 (to within eps^2);
-//  * the sum so far moves from m to ref with the factor 2^{(m - ref) c2}, its
-//    exponent taken as fma(m, c2, nr) + eps. When the maximum did not move that is
-//    exactly 0 (the fma returns -eps exactly), where exp2(fma(m, c2, nr)) alone
-//    applied 2^-eps again at every step, compounding over the steps; after a move
-//    it is off by one rounding of a number the size of the move.
-// What remains is the rounding of each term's own argument and exp2, independent
-// from term to term. (fp64 for these two corrections measured 4% slower.)
+// carry no error common to all its terms (softmax_step.hpp): the rounding of the
+// step's offset -ref c2 is put back into the step's sum, and the sum so far moves
+// onto the new maximum with an exponent that is exactly 0 when the maximum did not
+// move. (Without this the error compounded over the steps to ~2e-6 of the sum; fp64
+// for the same corrections measured 4% slower.) What remains is the rounding of
+// each term's own argument and exp2, independent from term to term.
 __device__ __forceinline__ void online_step(const f4 (&x)[kVecs], int s, float c2, float& m, double& acc) {
     // maximum() rather than fmaxf(): the inputs are never NaN, and it takes loaded
     // values without a canonicalising instruction each (three-input form on gfx950)
@@ -356,23 +351,19 @@ __device__ __forceinline__ void online_step(const f4 (&x)[kVecs], int s, float c
                  __builtin_elementwise_maximum(x[i].x, x[i].y), __builtin_elementwise_maximum(x[i].z, x[i].w)));
     const float mn = __builtin_elementwise_maximum(m, gm);
     const float ref = (mn == -INFINITY) ? 0.0f : mn;   // all -inf so far: every term is 0
-    const float nr = -ref * c2;                        // exps as exp2(x * c2 + nr), one fma each
-    const float eps = fmaf(-ref, c2, -nr);             // -ref c2 - nr, exactly
-    // (m - ref) c2 = (m c2 + nr) + eps; m = ref gives fma(m, c2, nr) = -eps exactly, so
-    // the factor is exactly 1; m = -inf gives 0
-    const float rescale = __builtin_amdgcn_exp2f(fmaf(m, c2, nr) + eps);
+    const StepOffset off = step_offset(ref, c2);       // exps as exp2(x * c2 + off.nr), one fma each
+    const float rescale = __builtin_amdgcn_exp2f(rescale_exponent(m, c2, off));   // 1 if no move, 0 from -inf
     float part[kStep];
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
         const f4 v = x[kStep * s + i];
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(v.x, c2, nr));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(v.y, c2, nr));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(v.z, c2, nr));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(v.w, c2, nr));
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(v.x, c2, off.nr));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(v.y, c2, off.nr));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(v.z, c2, off.nr));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(v.w, c2, off.nr));
         part[i] = (e0 + e1) + (e2 + e3);
     }
-    const float sum0 = (part[0] + part[1]) + (part[2] + part[3]);
-    const float sum = fmaf(sum0, eps * 0.69314718f, sum0);   // times 2^eps = 1 + eps ln 2
+    const float sum = corrected_sum((part[0] + part[1]) + (part[2] + part[3]), off);
     acc = acc * static_cast<double>(rescale) + static_cast<double>(sum);
     m = mn;
 }
