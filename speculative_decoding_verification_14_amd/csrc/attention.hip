@@ -571,10 +571,13 @@ __device__ __forceinline__ float merge_row(const AttnArgs& a, PR&& prow_of, int 
 }
 
 // Combine the pieces of every (sequence, KV head, row group) segment that was
-// split between workgroups, in workgroup order.
+// split between workgroups, in workgroup order. One workgroup per 16-row tile of a
+// segment (blockIdx.z), so that the tiles of a row group merge side by side rather
+// than one after another: a merge is a chain of dependent round trips, one per
+// batch of pieces.
 template <int D>
 __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) {
-    const int u = blockIdx.x, b = blockIdx.y;
+    const int u = blockIdx.x, b = blockIdx.y, n = blockIdx.z;
     const int rgr = 16 * tiles;
     const SeqShape sh = seq_shape(a.cu, b, a.k, a.G, rgr);
     const int U_b = sh.row_groups * a.Hkv;
@@ -595,11 +598,11 @@ __global__ __launch_bounds__(kAT) void attn_merge_kernel(AttnArgs a, int tiles) 
     auto prow_of = [&](int ww, int n, int r) {
         return (size_t(ww) * 2 + (ww == w0 ? first_slot : 0)) * rgr + n * 16 + r;
     };
-    for (int n = 0; n < tiles; ++n) {
+    {
         const int r = tid / 16;
         const int d0 = (tid % 16) * (D / 16);
         const int row = rg * rgr + n * 16 + r;
-        if (row >= sh.rows) continue;
+        if (row >= sh.rows) return;
         float acc[D / 16];
         const float inv = (w1 - w0 < 2) ? merge_row<D, 2>(a, prow_of, w0, w1, n, r, d0, acc)
                                         : merge_row<D, kMergeBatch>(a, prow_of, w0, w1, n, r, d0, acc);
@@ -709,7 +712,7 @@ hipError_t launch_attn(const AttnLaunch& p, const AttnGeometry& geo, hipStream_t
 #undef SPEC_ATTN_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 mgrid(a.U, p.B);
+    const dim3 mgrid(a.U, p.B, geo.tiles);
     if (p.D == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, block, 0, stream, a, geo.tiles);
     else hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, block, 0, stream, a, geo.tiles);
     return hipGetLastError();
