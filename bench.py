@@ -68,6 +68,11 @@ WORKLOAD_COUNTERS = {
     "longtail": os.path.join(ROOT, "profiles", "verify_longtail_counters.txt"),
     "262k": os.path.join(ROOT, "profiles", "verify_262k_counters.txt"),
 }
+# counter runs of other launches at the 8B shape: (variant, tree shape or None) -> summary
+VARIANT_COUNTERS = {
+    ("ragged", None): os.path.join(ROOT, "profiles", "verify_ragged_8b_counters.txt"),
+    ("tree", "2,2"): os.path.join(ROOT, "profiles", "verify_tree_2x2_8b_counters.txt"),
+}
 # sources (and the build script, which holds per-file compiler flags) whose hash a counter
 # summary records: counters taken before a change to any of them are not used
 BUILD_SCRIPT = "speculative_decoding_verification_14_amd/build.py"
@@ -139,10 +144,15 @@ def dense_reject_figure(preset, seconds: float) -> dict:
     return dict(bytes=dense, gbs=gbs, frac_of_peak=gbs / HBM_PEAK_GBS)
 
 
-def workload_counters(workload: str, variant: str = "uniform"):
-    """The counter summary that measured this bench line's launches, or None: only the uniform
-    step of a workload at its own shape has one (plain decoding, k = 0, launches other kernels)."""
-    return WORKLOAD_COUNTERS.get(workload) if variant == "uniform" else None
+def workload_counters(workload: str, variant: str = "uniform", tree: str | None = None):
+    """The counter summary that measured this bench line's launches, or None: the uniform step
+    of each workload at its own shape, and at the 8B shape the ragged step and the 2x2 tree
+    (plain decoding, k = 0, launches other kernels, and the fused pass has its own LM-head file)."""
+    if variant == "uniform":
+        return WORKLOAD_COUNTERS.get(workload)
+    if workload != "8b":
+        return None
+    return VARIANT_COUNTERS.get((variant, tree if variant == "tree" else None))
 
 
 def stored_traffic(path=None, sources=None, key="hbm_bytes_per_call"):
@@ -612,7 +622,9 @@ def gpu_bench_ragged(args, p, dev) -> dict:
                               "one attention layer + rejection sampling + commit"),
                     global_batch=B, k="ragged", parallelism="none (1 GPU)"),
         roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
-                      traffic=None, kernel="spec_verify_attn_ragged (attn_streamk_kernel + attn_merge_kernel)",
+                      traffic=stored_traffic(workload_counters(args.workload, "ragged"))
+                      if workload_counters(args.workload, "ragged") else None,
+                      kernel="spec_verify_attn_ragged (attn_streamk_kernel + attn_merge_kernel)",
                       algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_s * 1e6),
         verified_tokens_per_step=tokens,
         kernels=dict(verify_attn=dict(avg_us=attn_s * 1e6, bytes=a_bytes, gbs=attn_gbs,
@@ -880,7 +892,9 @@ def gpu_bench_tree(args, p, dev) -> dict:
                               "one attention layer + tree walk + tree commit"),
                     global_batch=B, k=f"tree {t_br}x{depth}", parallelism="none (1 GPU)"),
         roofline=dict(bound="hbm", achieved=attn_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
-                      traffic=None, kernel="spec_verify_attn_tree (attn_streamk_kernel + attn_merge_kernel)",
+                      traffic=stored_traffic(workload_counters(args.workload, "tree", args.tree))
+                      if workload_counters(args.workload, "tree", args.tree) else None,
+                      kernel="spec_verify_attn_tree (attn_streamk_kernel + attn_merge_kernel)",
                       algorithmic_bytes_per_call=a_bytes, avg_call_us=attn_s * 1e6),
         verified_tokens_per_step=tokens,
         mean_emitted_per_sequence=tokens / B,
@@ -922,6 +936,8 @@ def gpu_bench(args) -> dict:
     p = PRESETS[args.workload]
     if args.variant == "plain":
         p = dataclasses.replace(p, k=0)
+    if args.variant in ("ragged", "tree") and args.copy_calibration:
+        copy_calibration(dev)   # the counter runs' calibration kernel (the other paths run it themselves)
     if args.variant == "ragged":
         return gpu_bench_ragged(args, p, dev)
     if args.variant == "tree":

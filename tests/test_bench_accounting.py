@@ -70,9 +70,19 @@ def test_each_workload_line_takes_traffic_from_its_own_counter_run():
         named = args[args.index("--workload") + 1] if "--workload" in args else "8b"
         assert named == workload, (workload, cmd)
         assert "--variant" not in args and "--sweep" not in args, cmd
-    # other launches (plain decoding, ragged, trees, the fused pass) and other workloads have none
-    for variant in ("plain", "ragged", "tree", "fused"):
-        assert bench.workload_counters("8b", variant) is None
+    # the ragged step and the 2x2 tree at the 8B shape have runs of their own, naming that variant
+    for variant, tree in (("ragged", None), ("tree", "2,2")):
+        path = bench.workload_counters("8b", variant, tree)
+        with open(path) as f:
+            cmd = next(line for line in f if line.startswith("# fetch command:"))
+        args = cmd.split(" -- ", 1)[1].split()
+        assert args[args.index("--variant") + 1] == variant, cmd
+        assert (args[args.index("--tree") + 1] if "--tree" in args else None) == tree, cmd
+        assert "--workload" not in args, cmd
+    # other launches (plain decoding, other trees, the fused pass) and other workloads have none
+    for variant, tree in (("plain", None), ("tree", "2,3"), ("fused", None)):
+        assert bench.workload_counters("8b", variant, tree) is None
+    assert bench.workload_counters("7b", "ragged") is None
     assert bench.workload_counters("tiny") is None
 
 
