@@ -70,8 +70,10 @@ WORKLOAD_COUNTERS = {
 }
 # counter runs of other launches at the 8B shape: (variant, tree shape or None) -> summary
 VARIANT_COUNTERS = {
+    ("plain", None): os.path.join(ROOT, "profiles", "verify_plain_8b_counters.txt"),
     ("ragged", None): os.path.join(ROOT, "profiles", "verify_ragged_8b_counters.txt"),
     ("tree", "2,2"): os.path.join(ROOT, "profiles", "verify_tree_2x2_8b_counters.txt"),
+    ("tree", "2,3"): os.path.join(ROOT, "profiles", "verify_tree_2x3_8b_counters.txt"),
 }
 # sources (and the build script, which holds per-file compiler flags) whose hash a counter
 # summary records: counters taken before a change to any of them are not used
@@ -146,8 +148,8 @@ def dense_reject_figure(preset, seconds: float) -> dict:
 
 def workload_counters(workload: str, variant: str = "uniform", tree: str | None = None):
     """The counter summary that measured this bench line's launches, or None: the uniform step
-    of each workload at its own shape, and at the 8B shape the ragged step and the 2x2 tree
-    (plain decoding, k = 0, launches other kernels, and the fused pass has its own LM-head file)."""
+    of each workload at its own shape, and at the 8B shape plain decoding (k = 0), the ragged
+    step and the 2x2 and 2x3 trees (the fused pass has its own LM-head file)."""
     if variant == "uniform":
         return WORKLOAD_COUNTERS.get(workload)
     if workload != "8b":

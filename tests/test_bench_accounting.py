@@ -70,8 +70,9 @@ def test_each_workload_line_takes_traffic_from_its_own_counter_run():
         named = args[args.index("--workload") + 1] if "--workload" in args else "8b"
         assert named == workload, (workload, cmd)
         assert "--variant" not in args and "--sweep" not in args, cmd
-    # the ragged step and the 2x2 tree at the 8B shape have runs of their own, naming that variant
-    for variant, tree in (("ragged", None), ("tree", "2,2")):
+    # plain decoding, the ragged step and the trees at the 8B shape have runs of their own,
+    # naming that variant
+    for variant, tree in (("plain", None), ("ragged", None), ("tree", "2,2"), ("tree", "2,3")):
         path = bench.workload_counters("8b", variant, tree)
         with open(path) as f:
             cmd = next(line for line in f if line.startswith("# fetch command:"))
@@ -79,8 +80,8 @@ def test_each_workload_line_takes_traffic_from_its_own_counter_run():
         assert args[args.index("--variant") + 1] == variant, cmd
         assert (args[args.index("--tree") + 1] if "--tree" in args else None) == tree, cmd
         assert "--workload" not in args, cmd
-    # other launches (plain decoding, other trees, the fused pass) and other workloads have none
-    for variant, tree in (("plain", None), ("tree", "2,3"), ("fused", None)):
+    # other launches (other trees, the fused pass) and other workloads have none
+    for variant, tree in (("tree", "3,2"), ("fused", None)):
         assert bench.workload_counters("8b", variant, tree) is None
     assert bench.workload_counters("7b", "ragged") is None
     assert bench.workload_counters("tiny") is None
